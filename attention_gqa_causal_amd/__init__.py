@@ -1,0 +1,273 @@
+"""Python binding of the MI355X attention library (``libgqa_attn.so``).
+
+Argument marshalling only: every step of the computation runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current stream.  There is
+no fallback: if the library is not built, every call raises.
+
+Functions (names follow the C ABI in ``include/gqa_attn.h``):
+
+* ``attn_prefill(q, k, v, sinks, window=0, scale=None)``
+* ``attn_decode(q, kv_cache, seqlens, sinks, window=0, scale=None)``
+* ``attn_varlen_paged(q, kv_cache, block_table, cu_seqlens_q, seqlens_k, sinks, ...)``
+
+The computation is causal grouped-query attention with a learned per-head sink
+logit and an optional sliding window (0 = dense), as described on the pages
+«GPT-OSS vs Qwen3» (sections "Introduction de Grouped Query Attention",
+"Utilisation de Sliding Window Attention", "Attention Bias et Sinks") and
+«GPT-OSS-20B : Architecture MoE & Résumé du Model Card» (§3.3).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "attn_prefill",
+    "attn_decode",
+    "attn_varlen_paged",
+    "decode_workspace_size",
+    "varlen_workspace_size",
+    "lib",
+    "lib_path",
+    "GQA_BF16",
+    "GQA_FP32",
+    "GqaError",
+]
+
+GQA_BF16 = 0
+GQA_FP32 = 1
+GQA_OK = 0
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libgqa_attn.so"
+_lib = None
+
+
+class GqaError(RuntimeError):
+    """A nonzero status returned by the C library."""
+
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name} ({status}): {detail}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return os.environ.get("GQA_ATTN_LIB") or os.path.join(_PKG, _LIB_NAME)
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "gqa_attn_version": (_I, []),
+    "gqa_attn_status_string": (ctypes.c_char_p, [_I]),
+    "gqa_attn_last_error": (ctypes.c_char_p, []),
+    "gqa_attn_prefill": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "gqa_attn_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "gqa_attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "gqa_attn_varlen_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "gqa_attn_varlen_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _P, _P, _P,
+                                   _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load the C library (after torch, so that one HIP runtime serves both)."""
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is not built; run `python -m attention_gqa_causal_amd.build` (no CPU fallback exists)")
+        L = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != GQA_OK:
+        L = lib()
+        raise GqaError(status, L.gqa_attn_status_string(status).decode(), L.gqa_attn_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GQA_BF16
+    if t.dtype == torch.float32:
+        return GQA_FP32
+    raise ValueError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensor(t, name, dtype, device, ndim):
+    _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _need(t.is_cuda, f"{name} must be a GPU tensor")
+    _need(t.device == device, f"{name} must be on {device}")
+    _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _need(t.dim() == ndim, f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _sinks_arg(sinks, hq, device):
+    if sinks is None:
+        return None
+    _check_tensor(sinks, "sinks", torch.float32, device, 1)
+    _need(sinks.shape[0] == hq, f"sinks must have Hq={hq} entries")
+    return sinks
+
+
+def _scale(scale) -> float:
+    return 0.0 if scale is None else float(scale)
+
+
+def _split_cache(kv_cache):
+    if isinstance(kv_cache, (tuple, list)):
+        _need(len(kv_cache) == 2, "kv_cache must be (k_cache, v_cache)")
+        return kv_cache[0], kv_cache[1]
+    _need(kv_cache.shape[0] == 2, "a single kv_cache tensor must stack K and V on dim 0")
+    return kv_cache[0], kv_cache[1]
+
+
+def attn_prefill(q, k, v, sinks=None, window: int = 0, scale=None, return_lse: bool = False, out=None):
+    """Causal self-attention over whole sequences.
+
+    q [B, S, Hq, 64], k/v [B, S, Hkv, 64] (bf16 or fp32, same dtype, on the GPU);
+    sinks [Hq] fp32 or None.  Returns out [B, S, Hq, 64] (and lse [B, Hq, S] fp32).
+    """
+    dev = q.device
+    _check_tensor(q, "q", q.dtype, dev, 4)
+    dt = _dtype_code(q)
+    B, S, Hq, D = q.shape
+    _check_tensor(k, "k", q.dtype, dev, 4)
+    _check_tensor(v, "v", q.dtype, dev, 4)
+    _need(k.shape[:2] == (B, S) and k.shape[3] == D and v.shape == k.shape, "k/v must be [B, S, Hkv, D] matching q")
+    Hkv = k.shape[2]
+    sinks = _sinks_arg(sinks, Hq, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor(out, "out", q.dtype, dev, 4)
+        _need(out.shape == q.shape, "out must match q")
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev) if return_lse else None
+    _check(lib().gqa_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(out), _ptr(lse),
+                                  B, S, Hq, Hkv, D, int(window), _scale(scale), dt, _stream(dev)))
+    return (out, lse) if return_lse else out
+
+
+def decode_workspace_size(B, Lmax, Hq, Hkv, D=64, window=0, dtype=GQA_BF16) -> int:
+    return int(lib().gqa_attn_decode_workspace_size(B, Lmax, Hq, Hkv, D, int(window), dtype))
+
+
+def attn_decode(q, kv_cache, seqlens, sinks=None, window: int = 0, scale=None, return_lse: bool = False,
+                workspace=None):
+    """One new query token per sequence against a contiguous KV cache.
+
+    q [B, Hq, 64]; kv_cache = (k_cache, v_cache) each [B, Lmax, Hkv, 64], or one
+    [2, B, Lmax, Hkv, 64] tensor; seqlens [B] int32 on the GPU (cached positions
+    including the new token).  Returns out [B, Hq, 64] (and lse [B, Hq]).
+    """
+    dev = q.device
+    _check_tensor(q, "q", q.dtype, dev, 3)
+    dt = _dtype_code(q)
+    B, Hq, D = q.shape
+    kc, vc = _split_cache(kv_cache)
+    _check_tensor(kc, "k_cache", q.dtype, dev, 4)
+    _check_tensor(vc, "v_cache", q.dtype, dev, 4)
+    _need(kc.shape[0] == B and kc.shape[3] == D and vc.shape == kc.shape, "caches must be [B, Lmax, Hkv, D]")
+    Lmax, Hkv = kc.shape[1], kc.shape[2]
+    _check_tensor(seqlens, "seqlens", torch.int32, dev, 1)
+    _need(seqlens.shape[0] == B, "seqlens must have B entries")
+    sinks = _sinks_arg(sinks, Hq, dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None
+    ws_bytes = int(lib().gqa_attn_decode_workspace_size(B, Lmax, Hq, Hkv, D, int(window), dt))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().gqa_attn_decode(_ptr(q), _ptr(kc), _ptr(vc), _ptr(seqlens), _ptr(sinks), _ptr(out), _ptr(lse),
+                                 B, Lmax, Hq, Hkv, D, int(window), _scale(scale), dt,
+                                 _ptr(workspace), ws_have, _stream(dev)))
+    return (out, lse) if return_lse else out
+
+
+def varlen_workspace_size(B, max_q_len, max_kv_len, Hq, Hkv, D=64, window=0, dtype=GQA_BF16) -> int:
+    return int(lib().gqa_attn_varlen_workspace_size(B, max_q_len, max_kv_len, Hq, Hkv, D, int(window), dtype))
+
+
+def attn_varlen_paged(q, kv_cache, block_table, cu_seqlens_q, seqlens_k, sinks=None, window: int = 0, scale=None,
+                      max_q_len: int | None = None, max_kv_len: int | None = None, cu_seqlens_k=None,
+                      return_lse: bool = False, workspace=None):
+    """Packed variable-length queries over a paged KV cache (mixed prefill chunks and decode steps).
+
+    q [Tq, Hq, 64]; kv_cache = (k_cache, v_cache) each [num_blocks, block_size, Hkv, 64]
+    with block_table [B, max_blocks] int32, or, with block_table None, packed
+    [num_rows, Hkv, 64] caches addressed by cu_seqlens_k [B+1].  cu_seqlens_q [B+1]
+    and seqlens_k [B] are int32 on the GPU.  max_q_len / max_kv_len are host-side
+    bounds; when omitted they are read back from the GPU (a synchronising copy).
+    Returns out [Tq, Hq, 64] (and lse [Hq, Tq]).
+    """
+    dev = q.device
+    _check_tensor(q, "q", q.dtype, dev, 3)
+    dt = _dtype_code(q)
+    Tq, Hq, D = q.shape
+    kc, vc = _split_cache(kv_cache)
+    _check_tensor(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev, 1)
+    _check_tensor(seqlens_k, "seqlens_k", torch.int32, dev, 1)
+    B = seqlens_k.shape[0]
+    _need(cu_seqlens_q.shape[0] == B + 1, "cu_seqlens_q must have B+1 entries")
+    if block_table is not None:
+        _check_tensor(kc, "k_cache", q.dtype, dev, 4)
+        _check_tensor(vc, "v_cache", q.dtype, dev, 4)
+        _need(vc.shape == kc.shape and kc.shape[3] == D, "paged caches must be [num_blocks, block_size, Hkv, D]")
+        _check_tensor(block_table, "block_table", torch.int32, dev, 2)
+        _need(block_table.shape[0] == B, "block_table must have B rows")
+        num_blocks, block_size, Hkv = kc.shape[0], kc.shape[1], kc.shape[2]
+        max_blocks = block_table.shape[1]
+        cap = max_blocks * block_size
+    else:
+        _check_tensor(kc, "k_cache", q.dtype, dev, 3)
+        _check_tensor(vc, "v_cache", q.dtype, dev, 3)
+        _need(vc.shape == kc.shape and kc.shape[2] == D, "packed caches must be [num_rows, Hkv, D]")
+        _need(cu_seqlens_k is not None, "cu_seqlens_k is required without a block table")
+        _check_tensor(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev, 1)
+        _need(cu_seqlens_k.shape[0] == B + 1, "cu_seqlens_k must have B+1 entries")
+        num_blocks, block_size, Hkv = kc.shape[0], 1, kc.shape[1]
+        max_blocks = 0
+        cap = None
+    if max_q_len is None:
+        max_q_len = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if B else 0
+    if max_kv_len is None:
+        max_kv_len = cap if cap is not None else (int(seqlens_k.max().item()) if B else 0)
+    sinks = _sinks_arg(sinks, Hq, dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev) if return_lse else None
+    ws_bytes = int(lib().gqa_attn_varlen_workspace_size(B, max_q_len, max_kv_len, Hq, Hkv, D, int(window), dt))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().gqa_attn_varlen_paged(_ptr(q), _ptr(kc), _ptr(vc), _ptr(cu_seqlens_q), _ptr(seqlens_k),
+                                       _ptr(block_table), max_blocks, block_size, _ptr(cu_seqlens_k), num_blocks,
+                                       _ptr(sinks), _ptr(out), _ptr(lse), B, Tq, int(max_q_len), int(max_kv_len),
+                                       Hq, Hkv, D, int(window), _scale(scale), dt,
+                                       _ptr(workspace), ws_have, _stream(dev)))
+    return (out, lse) if return_lse else out

@@ -1,0 +1,323 @@
+// C ABI of the attention library: argument validation, launch planning (grid
+// sizes, split-K count, workspace layout) and dispatch to the gfx950 kernels.
+// Every entry point validates first and launches nothing on error; no C++
+// exception leaves this file.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "gqa_attn.h"
+#include "kernels.h"
+
+using namespace gqa;
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return GQA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(GQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// number of compute units of the current device (cached per device; 256 when
+// no device can be queried, e.g. during host-only argument checks)
+int num_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  if (!s || !*s) return dflt;
+  return atoi(s);
+}
+
+int check_common(int Hq, int Hkv, int D, int window, float scale, int dtype) {
+  if (dtype != GQA_BF16 && dtype != GQA_FP32) return fail(GQA_ERR_UNSUPPORTED, "dtype %d is not GQA_BF16 or GQA_FP32", dtype);
+  if (Hq <= 0 || Hkv <= 0) return fail(GQA_ERR_INVALID_ARG, "head counts must be positive (Hq=%d, Hkv=%d)", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(GQA_ERR_UNSUPPORTED, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (D != kHeadDim) return fail(GQA_ERR_UNSUPPORTED, "head_dim %d is not supported (only 64)", D);
+  if (window < 0) return fail(GQA_ERR_INVALID_ARG, "window %d is negative (0 = dense)", window);
+  if (std::isnan(scale) || scale < 0.f) return fail(GQA_ERR_INVALID_ARG, "scale must be >= 0 (0 = 1/sqrt(D))");
+  return GQA_OK;
+}
+
+float scale_log2_of(float scale, int D) {
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
+  return sc * kLog2e;
+}
+
+struct SplitPlan {
+  int n_splits;
+  int split_len;
+};
+
+// Split of the decode key range so that the grid covers the chip about twice;
+// each split keeps at least 4 tiles (one per wave) of 64 keys.
+SplitPlan plan_splits(int B, int Hkv, int G, int Lmax, int window) {
+  const int eff = window > 0 ? (window < Lmax ? window : Lmax) : Lmax;
+  const int n_hc = (G + 15) / 16;
+  const long units = (long)B * Hkv * n_hc;
+  SplitPlan p{1, 64};
+  if (eff <= 0 || units <= 0) return p;
+  const long target = 2L * num_cus();
+  long want = (target + units - 1) / units;
+  const long max_by_len = (eff + 255) / 256;
+  if (want > max_by_len) want = max_by_len;
+  if (want < 1) want = 1;
+  if (want > 64) want = 64;
+  const int forced = env_int("GQA_DECODE_SPLITS", 0);
+  if (forced > 0) want = forced > 256 ? 256 : forced;
+  int len = (int)((eff + want - 1) / want);
+  len = (len + 63) & ~63;
+  p.split_len = len;
+  p.n_splits = (eff + len - 1) / len;
+  return p;
+}
+
+size_t decode_ws_bytes(const SplitPlan& p, int B, int Hq) {
+  if (p.n_splits <= 1) return 0;
+  return (size_t)B * Hq * p.n_splits * (2 + kHeadDim) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_attn_version(void) { return 100; }
+
+const char* gqa_attn_status_string(int status) {
+  switch (status) {
+    case GQA_OK: return "GQA_OK";
+    case GQA_ERR_INVALID_ARG: return "GQA_ERR_INVALID_ARG";
+    case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED";
+    case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE";
+    case GQA_ERR_HIP: return "GQA_ERR_HIP";
+    default: return "GQA_ERR_UNKNOWN";
+  }
+}
+
+const char* gqa_attn_last_error(void) { return g_err; }
+
+int gqa_attn_prefill(const void* q, const void* k, const void* v, const float* sinks, void* out, float* lse,
+                     int B, int S, int Hq, int Hkv, int D, int window, float scale, int dtype, void* stream) {
+  int rc = check_common(Hq, Hkv, D, window, scale, dtype);
+  if (rc) return rc;
+  if (B < 0 || S < 0) return fail(GQA_ERR_INVALID_ARG, "negative size (B=%d, S=%d)", B, S);
+  if (B == 0 || S == 0) return ok();
+  if (!q || !k || !v || !out) return fail(GQA_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
+  const int G = Hq / Hkv;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+  SeqArgs seq{};
+  seq.q_len_fixed = S;
+  seq.kv_len_fixed = S;
+  seq.lmax = S;
+  const float sl2 = scale_log2_of(scale, D);
+
+  if (dtype == GQA_FP32) {
+    if ((long long)B * S * Hq > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "problem too large for the fp32 path");
+    Fp32Args a{};
+    a.q = (const float*)q; a.k = (const float*)k; a.v = (const float*)v; a.sinks = sinks;
+    a.out = (float*)out; a.lse = lse; a.seq = seq;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = window; a.scale_log2 = sl2;
+    a.max_q_len = S; a.varlen_q = 0;
+    a.lse_sb = (int64_t)Hq * S; a.lse_sh = S; a.lse_row0 = 0;
+    hipError_t e = launch_fp32(a, KV_BATCHED, st);
+    return e == hipSuccess ? ok() : hip_fail(e, "prefill fp32 launch");
+  }
+
+  PrefillArgs a{};
+  a.q = (const __bf16*)q; a.k = (const __bf16*)k; a.v = (const __bf16*)v; a.sinks = sinks;
+  a.out = (__bf16*)out; a.lse = lse; a.seq = seq;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = window; a.scale_log2 = sl2;
+  const long ntiles = (long)((S + 31) / 32) * G;
+  a.wg_per_seq = (int)((ntiles + 7) / 8);
+  a.skip_single = 0;
+  a.lse_sb = (int64_t)Hq * S; a.lse_sh = S; a.lse_row0 = 0;
+  if ((long long)B * Hkv * a.wg_per_seq > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
+  hipError_t e = launch_prefill_bf16(a, KV_BATCHED, false, st);
+  return e == hipSuccess ? ok() : hip_fail(e, "prefill bf16 launch");
+}
+
+size_t gqa_attn_decode_workspace_size(int B, int Lmax, int Hq, int Hkv, int D, int window, int dtype) {
+  if (dtype != GQA_BF16 || B <= 0 || Lmax <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D != kHeadDim || window < 0) return 0;
+  const SplitPlan p = plan_splits(B, Hkv, Hq / Hkv, Lmax, window);
+  return decode_ws_bytes(p, B, Hq);
+}
+
+int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
+                    const float* sinks, void* out, float* lse, int B, int Lmax, int Hq, int Hkv, int D,
+                    int window, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(Hq, Hkv, D, window, scale, dtype);
+  if (rc) return rc;
+  if (B < 0 || Lmax < 0) return fail(GQA_ERR_INVALID_ARG, "negative size (B=%d, Lmax=%d)", B, Lmax);
+  if (B == 0) return ok();
+  if (Lmax == 0) return fail(GQA_ERR_INVALID_ARG, "Lmax must be >= 1 (the cache holds the new token)");
+  if (!q || !k_cache || !v_cache || !out || !seqlens)
+    return fail(GQA_ERR_INVALID_ARG, "q, k_cache, v_cache, seqlens and out must be non-NULL");
+  const int G = Hq / Hkv;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  SeqArgs seq{};
+  seq.seqlens_k = seqlens;
+  seq.q_len_fixed = 1;
+  seq.kv_len_fixed = Lmax;
+  seq.lmax = Lmax;
+  const float sl2 = scale_log2_of(scale, D);
+
+  if (dtype == GQA_FP32) {
+    Fp32Args a{};
+    a.q = (const float*)q; a.k = (const float*)k_cache; a.v = (const float*)v_cache; a.sinks = sinks;
+    a.out = (float*)out; a.lse = lse; a.seq = seq;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = window; a.scale_log2 = sl2;
+    a.max_q_len = 1; a.varlen_q = 0;
+    a.lse_sb = Hq; a.lse_sh = 1; a.lse_row0 = 0;
+    hipError_t e = launch_fp32(a, KV_BATCHED, st);
+    return e == hipSuccess ? ok() : hip_fail(e, "decode fp32 launch");
+  }
+
+  const SplitPlan p = plan_splits(B, Hkv, G, Lmax, window);
+  const size_t need = decode_ws_bytes(p, B, Hq);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(GQA_ERR_WORKSPACE, "decode needs a workspace of %zu bytes (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
+  DecodeArgs a{};
+  a.q = (const __bf16*)q; a.k = (const __bf16*)k_cache; a.v = (const __bf16*)v_cache; a.sinks = sinks;
+  a.out = (__bf16*)out; a.lse = lse; a.seq = seq;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.n_hc = (G + 15) / 16;
+  a.window = window; a.scale_log2 = sl2;
+  a.n_splits = p.n_splits; a.split_len = p.split_len;
+  a.ws_ml = (float*)workspace;
+  a.ws_acc = need ? (float*)workspace + (size_t)B * Hq * p.n_splits * 2 : nullptr;
+  a.varlen_q = 0;
+  a.lse_sb = Hq; a.lse_sh = 1; a.lse_row0 = 0;
+  if ((long long)B * Hkv * a.n_hc * a.n_splits > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
+  hipError_t e = launch_decode_bf16(a, KV_BATCHED, st);
+  return e == hipSuccess ? ok() : hip_fail(e, "decode bf16 launch");
+}
+
+size_t gqa_attn_varlen_workspace_size(int B, int max_q_len, int max_kv_len, int Hq, int Hkv, int D, int window,
+                                      int dtype) {
+  if (dtype != GQA_BF16 || B <= 0 || max_q_len <= 0 || max_kv_len <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv ||
+      D != kHeadDim || window < 0)
+    return 0;
+  const SplitPlan p = plan_splits(B, Hkv, Hq / Hkv, max_kv_len, window);
+  return decode_ws_bytes(p, B, Hq);
+}
+
+int gqa_attn_varlen_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* cu_seqlens_q,
+                          const int32_t* seqlens_k, const int32_t* block_table, int max_blocks, int block_size,
+                          const int32_t* cu_seqlens_k, int num_blocks, const float* sinks, void* out, float* lse,
+                          int B, int Tq, int max_q_len, int max_kv_len, int Hq, int Hkv, int D, int window,
+                          float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(Hq, Hkv, D, window, scale, dtype);
+  if (rc) return rc;
+  if (B < 0 || Tq < 0 || max_q_len < 0 || max_kv_len < 0)
+    return fail(GQA_ERR_INVALID_ARG, "negative size (B=%d, Tq=%d, max_q_len=%d, max_kv_len=%d)", B, Tq, max_q_len, max_kv_len);
+  if (B == 0 || Tq == 0 || max_q_len == 0) return ok();
+  if (!q || !k_cache || !v_cache || !out || !cu_seqlens_q || !seqlens_k)
+    return fail(GQA_ERR_INVALID_ARG, "q, k_cache, v_cache, cu_seqlens_q, seqlens_k and out must be non-NULL");
+  if (num_blocks <= 0) return fail(GQA_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  int mode, log2b = 0;
+  if (block_table) {
+    if (block_size < 1 || block_size > 1024 || (block_size & (block_size - 1)))
+      return fail(GQA_ERR_UNSUPPORTED, "block_size %d is not a power of two in [1, 1024]", block_size);
+    if (max_blocks <= 0) return fail(GQA_ERR_INVALID_ARG, "max_blocks must be >= 1");
+    while ((1 << log2b) < block_size) ++log2b;
+    if ((long long)max_blocks * block_size < max_kv_len)
+      return fail(GQA_ERR_INVALID_ARG, "max_kv_len %d exceeds the block table capacity %lld", max_kv_len,
+                  (long long)max_blocks * block_size);
+    mode = KV_PAGED;
+  } else {
+    if (!cu_seqlens_k) return fail(GQA_ERR_INVALID_ARG, "cu_seqlens_k is required when block_table is NULL");
+    mode = KV_PACKED;
+  }
+  if (max_q_len > max_kv_len) return fail(GQA_ERR_INVALID_ARG, "max_q_len %d exceeds max_kv_len %d", max_q_len, max_kv_len);
+  const int G = Hq / Hkv;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  SeqArgs seq{};
+  seq.cu_seqlens_q = cu_seqlens_q;
+  seq.seqlens_k = seqlens_k;
+  seq.block_table = block_table;
+  seq.cu_seqlens_k = cu_seqlens_k;
+  seq.max_blocks = max_blocks;
+  seq.log2_block = log2b;
+  seq.num_blocks = num_blocks;
+  seq.lmax = max_kv_len;
+  const float sl2 = scale_log2_of(scale, D);
+
+  if (dtype == GQA_FP32) {
+    if ((long long)B * max_q_len * Hq > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "problem too large for the fp32 path");
+    Fp32Args a{};
+    a.q = (const float*)q; a.k = (const float*)k_cache; a.v = (const float*)v_cache; a.sinks = sinks;
+    a.out = (float*)out; a.lse = lse; a.seq = seq;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = window; a.scale_log2 = sl2;
+    a.max_q_len = max_q_len; a.varlen_q = 1;
+    a.lse_sb = 0; a.lse_sh = Tq; a.lse_row0 = 1;
+    hipError_t e = launch_fp32(a, mode, st);
+    return e == hipSuccess ? ok() : hip_fail(e, "varlen fp32 launch");
+  }
+
+  const SplitPlan p = plan_splits(B, Hkv, G, max_kv_len, window);
+  const size_t need = decode_ws_bytes(p, B, Hq);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(GQA_ERR_WORKSPACE, "varlen needs a workspace of %zu bytes (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
+
+  if (max_q_len > 1) {
+    PrefillArgs a{};
+    a.q = (const __bf16*)q; a.k = (const __bf16*)k_cache; a.v = (const __bf16*)v_cache; a.sinks = sinks;
+    a.out = (__bf16*)out; a.lse = lse; a.seq = seq;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = window; a.scale_log2 = sl2;
+    const long ntiles = (long)((max_q_len + 31) / 32) * G;
+    a.wg_per_seq = (int)((ntiles + 7) / 8);
+    a.skip_single = 1;
+    a.lse_sb = 0; a.lse_sh = Tq; a.lse_row0 = 1;
+    if ((long long)B * Hkv * a.wg_per_seq > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
+    hipError_t e = launch_prefill_bf16(a, mode, true, st);
+    if (e != hipSuccess) return hip_fail(e, "varlen prefill launch");
+  }
+  DecodeArgs a{};
+  a.q = (const __bf16*)q; a.k = (const __bf16*)k_cache; a.v = (const __bf16*)v_cache; a.sinks = sinks;
+  a.out = (__bf16*)out; a.lse = lse; a.seq = seq;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.n_hc = (G + 15) / 16;
+  a.window = window; a.scale_log2 = sl2;
+  a.n_splits = p.n_splits; a.split_len = p.split_len;
+  a.ws_ml = (float*)workspace;
+  a.ws_acc = need ? (float*)workspace + (size_t)B * Hq * p.n_splits * 2 : nullptr;
+  a.varlen_q = 1;
+  a.lse_sb = 0; a.lse_sh = Tq; a.lse_row0 = 1;
+  if ((long long)B * Hkv * a.n_hc * a.n_splits > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
+  hipError_t e = launch_decode_bf16(a, mode, st);
+  return e == hipSuccess ? ok() : hip_fail(e, "varlen decode launch");
+}
+
+}  // extern "C"

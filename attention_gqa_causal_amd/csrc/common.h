@@ -1,0 +1,139 @@
+// Shared device-side definitions of the gfx950 attention kernels: vector types,
+// bf16 packing, wave-level helpers and the KV / query addressing modes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegBig = -3.0e38f;  // finite floor for running maxima (avoids inf - inf)
+
+constexpr int kHeadDim = 64;
+
+// ---------------------------------------------------------------------------
+// addressing of sequences
+//
+// A "sequence view" tells a workgroup where its queries and keys live:
+//   q_row0     first packed query row of the sequence (row = index over [*, Hq, D])
+//   q_len      number of query tokens
+//   kv_len     number of KV positions (queries are the newest q_len of them)
+// and, per KV position j, the packed KV row (index over [*, Hkv, D]).
+
+enum KvMode : int {
+  KV_BATCHED = 0,  // k [B, Lmax, Hkv, D]: row = b * Lmax + j
+  KV_PAGED = 1,    // k [Nblk, bs, Hkv, D]: row = table[b][j >> log2bs] * bs + (j & (bs - 1))
+  KV_PACKED = 2    // k [Nrows, Hkv, D]: row = cu_seqlens_k[b] + j
+};
+
+struct SeqArgs {
+  // query side
+  const int32_t* cu_seqlens_q;  // varlen only (NULL for batched)
+  const int32_t* seqlens_k;     // varlen/decode (NULL for batched prefill)
+  int q_len_fixed;              // batched: S (prefill) or 1 (decode)
+  int kv_len_fixed;             // batched prefill: S; decode: Lmax (clamp bound)
+  // KV side
+  const int32_t* block_table;
+  const int32_t* cu_seqlens_k;
+  int max_blocks;
+  int log2_block;
+  int num_blocks;  // paged: number of physical blocks; packed: number of rows
+  int lmax;        // batched: Lmax (row stride per sequence)
+};
+
+struct SeqView {
+  int64_t q_row0;
+  int q_len;
+  int kv_len;
+  int b;
+};
+
+template <int MODE>
+__device__ __forceinline__ SeqView seq_view(const SeqArgs& a, int b, bool varlen_q) {
+  SeqView s;
+  s.b = b;
+  if (varlen_q) {
+    int r0 = a.cu_seqlens_q[b];
+    int r1 = a.cu_seqlens_q[b + 1];
+    s.q_row0 = r0;
+    s.q_len = max(r1 - r0, 0);
+  } else {
+    s.q_row0 = (int64_t)b * a.q_len_fixed;
+    s.q_len = a.q_len_fixed;
+  }
+  if (a.seqlens_k) {
+    int L = a.seqlens_k[b];
+    if (MODE == KV_BATCHED) L = min(L, a.lmax);
+    if (MODE == KV_PAGED) L = min(L, a.max_blocks << a.log2_block);
+    s.kv_len = max(L, 0);
+  } else {
+    s.kv_len = a.kv_len_fixed;
+  }
+  // queries are the newest positions; never more queries than positions
+  if (s.q_len > s.kv_len) s.q_len = s.kv_len;
+  return s;
+}
+
+template <int MODE>
+__device__ __forceinline__ int64_t kv_row(const SeqArgs& a, const SeqView& s, int j) {
+  if (MODE == KV_BATCHED) {
+    return (int64_t)s.b * a.lmax + j;
+  } else if (MODE == KV_PAGED) {
+    int blk = a.block_table[(int64_t)s.b * a.max_blocks + (j >> a.log2_block)];
+    blk = min(max(blk, 0), a.num_blocks - 1);
+    return ((int64_t)blk << a.log2_block) + (j & ((1 << a.log2_block) - 1));
+  } else {
+    int64_t r = (int64_t)a.cu_seqlens_k[s.b] + j;
+    r = r < 0 ? 0 : r;
+    return r < a.num_blocks ? r : (int64_t)a.num_blocks - 1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// small helpers
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// two fp32 -> packed bf16x2 (round to nearest even; v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Make this wave's LDS writes visible to its other lanes (and order later
+// writes after earlier reads): a wavefront-scope release/acquire pair around a
+// wave barrier.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace gqa

@@ -1,0 +1,74 @@
+// Argument blocks and launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include "common.h"
+
+namespace gqa {
+
+// Prefill-style attention: many query rows per sequence, one workgroup per
+// (sequence, KV head, group of 8 tiles of 32 (position, head) query rows).
+struct PrefillArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const float* sinks;
+  __bf16* out;
+  float* lse;
+  SeqArgs seq;
+  int B, Hq, Hkv, G;
+  int window;
+  float scale_log2;  // softmax scale times log2(e)
+  int wg_per_seq;    // workgroups per (sequence, KV head)
+  int skip_single;   // sequences with q_len == 1 are left to the decode kernel
+  int64_t lse_sb;    // lse index = b*lse_sb + h*lse_sh + t (+ q_row0 when lse_row0)
+  int64_t lse_sh;
+  int lse_row0;
+};
+
+// Decode-style attention: one query token per sequence, KV split over
+// n_splits workgroups per (sequence, KV head, chunk of 16 query heads).
+struct DecodeArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const float* sinks;
+  __bf16* out;
+  float* lse;
+  SeqArgs seq;
+  int B, Hq, Hkv, G, n_hc;
+  int window;
+  float scale_log2;
+  int n_splits;
+  int split_len;     // keys per split, a multiple of 64
+  float* ws_ml;      // [B*Hq, n_splits, 2]  running max (log2 units) and sum
+  float* ws_acc;     // [B*Hq, n_splits, 64] unnormalised output
+  int varlen_q;      // queries packed by cu_seqlens_q; sequences with q_len != 1 are skipped
+  int64_t lse_sb;    // lse index = b*lse_sb + h*lse_sh (+ q_row0 when lse_row0)
+  int64_t lse_sh;
+  int lse_row0;
+};
+
+// fp32 I/O path: one wave per (query row, query head).
+struct Fp32Args {
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* sinks;
+  float* out;
+  float* lse;
+  SeqArgs seq;
+  int B, Hq, Hkv, G;
+  int window;
+  float scale_log2;
+  int max_q_len;
+  int varlen_q;
+  int64_t lse_sb;
+  int64_t lse_sh;
+  int lse_row0;
+};
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int kv_mode, bool varlen_q, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, int kv_mode, hipStream_t s);
+hipError_t launch_fp32(const Fp32Args& a, int kv_mode, hipStream_t s);
+
+}  // namespace gqa

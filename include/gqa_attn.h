@@ -1,0 +1,159 @@
+/*
+ * gqa_attn.h -- C ABI of the MI355X (gfx950) attention library.
+ *
+ * Forward pass of causal grouped-query attention with a learned per-head sink
+ * logit and an optional sliding window, over Q/K that already carry their
+ * rotary position encoding.
+ *
+ * What is computed (for query head h at sequence position p):
+ *   G = Hq / Hkv, g = h / G            -- query heads share KV heads in
+ *                                         contiguous groups.  «GPT-OSS-20B :
+ *                                         Architecture MoE & Résumé du Model
+ *                                         Card», §3.3 (64 query heads over 8
+ *                                         KV heads, 8 per KV head).
+ *   J = { j : j <= p, and j > p - W when W > 0 }
+ *                                      -- causal (decoder-only, autoregressive:
+ *                                         «OpenAI lance gpt-oss-20b, qui tient
+ *                                         sur 16 Go», opening section); a
+ *                                         window keeps the W most recent keys
+ *                                         counting the query's own position
+ *                                         («GPT-OSS vs Qwen3», section
+ *                                         "Utilisation de Sliding Window
+ *                                         Attention": the last 128 tokens).
+ *   x_j = scale * <q, k_j[g]>,  s = sinks[h]
+ *   o   = sum_{j in J} e^{x_j} v_j[g] / (e^{s} + sum_{j in J} e^{x_j})
+ *   lse = ln(e^{s} + sum_{j in J} e^{x_j})
+ *                                      -- the sink is a learned logit per head
+ *                                         that only adds to the softmax
+ *                                         denominator («GPT-OSS vs Qwen3»,
+ *                                         section "Attention Bias et Sinks";
+ *                                         off-by-one attention when s = 0).
+ *   Dense and windowed layers alternate («gpt-oss Deep Dive with Xiaoli Alex
+ *   Shen», Key Moments); the caller passes the layer's window on each call.
+ *   If J is empty and there is no sink, o = 0 and lse = -inf.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers, row-major, densely packed,
+ *     16-byte aligned.  The caller owns every buffer; the library never
+ *     allocates device memory, keeps no state between calls and is
+ *     thread-safe.  Split-K scratch comes in through `workspace`.
+ *   - dtype: GQA_BF16 (inputs/outputs bf16, fp32 accumulation) or GQA_FP32
+ *     (everything fp32).  q, k, v and out share the dtype.  sinks and lse are
+ *     always fp32.
+ *   - sinks: [Hq] fp32, or NULL for no sink (s = -inf: plain softmax).
+ *   - lse: optional fp32 output (NULL = not written), natural-log units.
+ *   - head_dim D must be 64; Hq must be a positive multiple of Hkv.
+ *   - window: 0 = dense causal; W > 0 = the W most recent keys; W < 0 is an
+ *     error.
+ *   - scale: scale > 0 is used as given; scale == 0 selects 1/sqrt(D); a
+ *     negative or NaN scale is an error.
+ *   - stream: a hipStream_t (NULL = the default stream).  Every launch is
+ *     asynchronous on it; the library never synchronises.
+ *   - Errors: arguments are validated synchronously, before any launch; on
+ *     error a negative status is returned, nothing is launched and `out` is
+ *     untouched.  A failed launch returns GQA_ERR_HIP.  No C++ exception
+ *     crosses this ABI.  gqa_attn_last_error() gives the detail (per thread).
+ *   - Values that live on the device (seqlens, cu_seqlens, block tables) are
+ *     not checked on the host.  The kernels clamp lengths to the stated
+ *     maxima and block ids to [0, num_blocks) so that no access leaves the
+ *     caller's buffers; results for out-of-range metadata are unspecified.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gqa_dtype { GQA_BF16 = 0, GQA_FP32 = 1 } gqa_dtype;
+
+enum {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARG = -1,   /* NULL pointer, negative size, bad window/scale */
+  GQA_ERR_UNSUPPORTED = -2,   /* dtype, head_dim != 64, Hq % Hkv != 0, block size */
+  GQA_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required */
+  GQA_ERR_HIP = -4            /* a HIP launch failed */
+};
+
+/* Library version, as 10000*major + 100*minor + patch. */
+int gqa_attn_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char* gqa_attn_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* gqa_attn_last_error(void);
+
+/*
+ * Prefill: causal self-attention over whole sequences of equal length.
+ *   q   [B, S, Hq, D]     k, v [B, S, Hkv, D]     out [B, S, Hq, D]
+ *   lse [B, Hq, S] fp32 (optional)
+ * Position of row t is t.  B == 0 or S == 0 is a no-op returning GQA_OK.
+ */
+int gqa_attn_prefill(const void* q, const void* k, const void* v, const float* sinks,
+                     void* out, float* lse,
+                     int B, int S, int Hq, int Hkv, int D,
+                     int window, float scale, int dtype, void* stream);
+
+/*
+ * Decode: one new query token per sequence against a contiguous KV cache.
+ *   q [B, Hq, D]    k_cache, v_cache [B, Lmax, Hkv, D]    out [B, Hq, D]
+ *   seqlens [B] int32 (device): cached positions of sequence b INCLUDING the
+ *     new token, in [1, Lmax]; the query sits at position seqlens[b] - 1.
+ *   lse [B, Hq] fp32 (optional)
+ * The sequence is split over up to `gqa_attn_decode_workspace_size`-sized
+ * partials; pass a workspace of at least that many bytes (may be NULL when
+ * that size is 0).  On windowed layers only the last W positions are read.
+ */
+size_t gqa_attn_decode_workspace_size(int B, int Lmax, int Hq, int Hkv, int D,
+                                      int window, int dtype);
+
+int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* seqlens, const float* sinks,
+                    void* out, float* lse,
+                    int B, int Lmax, int Hq, int Hkv, int D,
+                    int window, float scale, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Variable-length packed queries over a paged (or packed) KV cache; mixes
+ * prefill chunks and single-token decode steps in one call.
+ *   q [Tq, Hq, D], out [Tq, Hq, D]; sequence b owns query rows
+ *     cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (cu_seqlens_q [B+1] int32,
+ *     device, non-decreasing, cu_seqlens_q[B] == Tq).
+ *   seqlens_k [B] int32 (device): KV positions of sequence b, including its
+ *     q_len new tokens; the q_len queries are the newest positions, query t at
+ *     position seqlens_k[b] - q_len + t (q_len <= seqlens_k[b]).
+ *   Paged (block_table != NULL): k_cache, v_cache [num_blocks, block_size, Hkv, D];
+ *     position p of sequence b is slot p % block_size of physical block
+ *     block_table[b * max_blocks + p / block_size] (block_table [B, max_blocks]
+ *     int32, device).  block_size must be a power of two in [1, 1024].
+ *   Packed (block_table == NULL): k_cache, v_cache [num_rows, Hkv, D] and
+ *     sequence b's positions start at row cu_seqlens_k[b] (cu_seqlens_k [B+1]
+ *     int32, device); num_blocks is then the row count and block_size is ignored.
+ *   max_q_len (host): upper bound of any q_len; max_kv_len (host): upper
+ *     bound of any seqlens_k[b] (for paged caches at most
+ *     max_blocks * block_size).  Both size the grids.
+ *   lse [Hq, Tq] fp32 (optional).
+ */
+size_t gqa_attn_varlen_workspace_size(int B, int max_q_len, int max_kv_len, int Hq, int Hkv,
+                                      int D, int window, int dtype);
+
+int gqa_attn_varlen_paged(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                          const int32_t* block_table, int max_blocks, int block_size,
+                          const int32_t* cu_seqlens_k, int num_blocks,
+                          const float* sinks, void* out, float* lse,
+                          int B, int Tq, int max_q_len, int max_kv_len,
+                          int Hq, int Hkv, int D,
+                          int window, float scale, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

@@ -1,0 +1,156 @@
+"""The C-ABI library: it loads, exports every symbol its header declares, and
+rejects bad arguments with the documented status before launching anything.
+CPU only: no call here reaches a kernel."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import attention_gqa_causal_amd as gq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+
+P = ctypes.c_void_p
+DUMMY = P(256)  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_attn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return gq.lib()
+
+
+def test_library_loads(L):
+    assert L.gqa_attn_version() == 100
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert L.gqa_attn_status_string(0) == b"GQA_OK"
+    assert L.gqa_attn_status_string(-1) == b"GQA_ERR_INVALID_ARG"
+    assert L.gqa_attn_status_string(-2) == b"GQA_ERR_UNSUPPORTED"
+    assert L.gqa_attn_status_string(-3) == b"GQA_ERR_WORKSPACE"
+    assert L.gqa_attn_status_string(-4) == b"GQA_ERR_HIP"
+    assert L.gqa_attn_status_string(-99) == b"GQA_ERR_UNKNOWN"
+
+
+def prefill(L, q=DUMMY, k=DUMMY, v=DUMMY, out=DUMMY, B=1, S=16, Hq=64, Hkv=8, D=64, window=0, scale=0.0, dt=0):
+    return L.gqa_attn_prefill(q, k, v, None, out, None, B, S, Hq, Hkv, D, window, scale, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=32), -2),
+    (dict(D=128), -2),
+    (dict(Hq=12, Hkv=8), -2),
+    (dict(Hq=0), -1),
+    (dict(Hkv=-1), -1),
+    (dict(window=-1), -1),
+    (dict(scale=float("nan")), -1),
+    (dict(scale=-0.5), -1),
+    (dict(dt=7), -2),
+    (dict(B=-1), -1),
+    (dict(S=-3), -1),
+    (dict(q=None), -1),
+    (dict(k=None), -1),
+    (dict(out=None), -1),
+])
+def test_prefill_rejects(L, kw, code):
+    assert prefill(L, **kw) == code
+    assert len(L.gqa_attn_last_error()) > 0
+
+
+def test_prefill_empty_is_noop(L):
+    assert prefill(L, q=None, k=None, v=None, out=None, B=0) == 0
+    assert prefill(L, q=None, k=None, v=None, out=None, S=0) == 0
+    assert L.gqa_attn_last_error() == b""
+
+
+def decode(L, ws=None, ws_bytes=0, seqlens=DUMMY, B=64, Lmax=8192, Hq=64, Hkv=8, D=64, window=0, dt=0):
+    return L.gqa_attn_decode(DUMMY, DUMMY, DUMMY, seqlens, None, DUMMY, None, B, Lmax, Hq, Hkv, D, window, 0.0, dt,
+                             ws, ws_bytes, None)
+
+
+def test_decode_workspace_rules(L):
+    # a long single-batch decode is split, so it needs a workspace
+    need = L.gqa_attn_decode_workspace_size(8, 131072, 64, 8, 64, 0, 0)
+    assert need > 0 and need % 4 == 0
+    assert decode(L, B=8, Lmax=131072) == -3
+    assert decode(L, ws=DUMMY, ws_bytes=need - 4, B=8, Lmax=131072) == -3
+    # fp32 and invalid shapes need none
+    assert L.gqa_attn_decode_workspace_size(8, 131072, 64, 8, 64, 0, 1) == 0
+    assert L.gqa_attn_decode_workspace_size(8, 131072, 64, 8, 32, 0, 0) == 0
+    # a sliding window caps the work per sequence: never more partials than dense
+    assert L.gqa_attn_decode_workspace_size(8, 131072, 64, 8, 64, 128, 0) <= need
+
+
+def test_decode_rejects(L):
+    assert decode(L, seqlens=None) == -1
+    assert decode(L, D=80) == -2
+    assert decode(L, Lmax=0) == -1
+    assert decode(L, window=-5) == -1
+    assert decode(L, B=0) == 0
+
+
+def varlen(L, table=DUMMY, cu_k=None, bs=16, maxblk=512, nblk=100, B=16, Tq=100, mq=64, mk=8192, window=0,
+           cu_q=DUMMY, ws=None, ws_bytes=0, D=64):
+    return L.gqa_attn_varlen_paged(DUMMY, DUMMY, DUMMY, cu_q, DUMMY, table, maxblk, bs, cu_k, nblk, None, DUMMY, None,
+                                   B, Tq, mq, mk, 64, 8, D, window, 0.0, 0, ws, ws_bytes, None)
+
+
+def test_varlen_rejects(L):
+    need = L.gqa_attn_varlen_workspace_size(16, 64, 8192, 64, 8, 64, 0, 0)
+    assert varlen(L, bs=12, ws=DUMMY, ws_bytes=need) == -2          # block size not a power of two
+    assert varlen(L, bs=2048, ws=DUMMY, ws_bytes=need) == -2
+    assert varlen(L, table=None, cu_k=None) == -1                 # packed needs cu_seqlens_k
+    assert varlen(L, maxblk=4, bs=16, mk=8192) == -1               # table too small for max_kv_len
+    assert varlen(L, mq=9000, mk=8192) == -1                       # more queries than positions
+    assert varlen(L, cu_q=None) == -1
+    assert varlen(L, nblk=0) == -1
+    assert varlen(L, D=48) == -2
+    assert varlen(L, B=0) == 0 and varlen(L, Tq=0) == 0 and varlen(L, mq=0) == 0
+    if need:
+        assert varlen(L, ws=None) == -3
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        gq.attn_prefill(q, k, k.clone(), None)
+    with pytest.raises(ValueError):
+        gq.attn_decode(q[:, 0], (k, k), torch.ones(1, dtype=torch.int32), None)
+
+
+def test_header_documents_each_entry_point():
+    text = open(HEADER).read()
+    for n in ("gqa_attn_prefill", "gqa_attn_decode", "gqa_attn_varlen_paged"):
+        assert n in text
+    # every entry point states layouts, ownership and error behaviour
+    for word in ("[B, S, Hq, D]", "[B, Lmax, Hkv, D]", "block_table", "caller owns", "GQA_ERR_WORKSPACE"):
+        assert word in text
+
+
+def test_no_oracle_on_product_path():
+    """The package must not import, call or link the CPU oracle."""
+    pkg = os.path.join(ROOT, "attention_gqa_causal_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                src = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "import oracle" not in src and "from oracle" not in src, f
