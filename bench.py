@@ -1,0 +1,328 @@
+"""Benchmark of the attention hot path on one MI355X; prints ONE JSON line.
+
+A step is one pass over every stage of the path, on seeded synthetic inputs
+already resident in HBM:
+  1. layer-shaped prefill  B1 S4096, 64 query / 8 KV heads, D64, bf16 -- one
+     dense layer, then one 128-token sliding-window layer;
+  2. batched decode        B64, cache 8192, same heads -- dense, then window 128;
+  3. ragged + paged        16 sequences, lengths U{128..8192}, 512-token
+     prefill chunks and single-token decode steps, 16-token pages under a
+     permuted block table -- dense, then window 128.
+`value` is the prefill throughput of the layer pair (1), in algorithmic
+TFLOP/s (4*D*Hq per visible query-key pair), timed with HIP events on the
+stream the kernels run on; every stage's own time, TFLOP/s, GB/s and roofline
+fraction is reported under "parts".  "roofline" describes the dominant kernel
+(dense prefill, MFMA-bound); "roofline_decode" the HBM-bound dense decode.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+METRIC = "prefill attn TFLOP/s + decode KV GB/s, % of MI355X roofline, dense vs SWA-128"
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "attention_gqa_causal_amd", "csrc")
+
+
+# ----------------------------------------------------------------------------- algorithmic work
+
+def visible_pairs(q_pos_last, n_q, window):
+    """Number of (query, key) pairs visible for n_q queries at positions q_pos_last-n_q+1 .. q_pos_last."""
+    tot = 0
+    p0 = q_pos_last - n_q + 1
+    # sum over p of min(p + 1, W) (or p + 1 when dense)
+    if window <= 0:
+        return (p0 + 1 + q_pos_last + 1) * n_q // 2
+    for p in range(p0, q_pos_last + 1):
+        tot += min(p + 1, window)
+    return tot
+
+
+def prefill_work(B, S, Hq, Hkv, D, window, elt=2):
+    pairs = B * visible_pairs(S - 1, S, window)
+    flop = 4 * D * Hq * pairs
+    byts = elt * (2 * B * S * Hq * D + 2 * B * S * Hkv * D)
+    return flop, byts
+
+
+def decode_work(seqlens, Hq, Hkv, D, window, elt=2):
+    n_read = [min(L, window) if window > 0 else L for L in seqlens]
+    flop = 4 * D * Hq * sum(n_read)
+    byts = elt * (2 * sum(n_read) * Hkv * D + 2 * len(seqlens) * Hq * D)
+    return flop, byts
+
+
+def varlen_work(kv_lens, q_lens, Hq, Hkv, D, window, elt=2):
+    pairs = 0
+    rows = 0
+    for L, n in zip(kv_lens, q_lens):
+        L, n = int(L), int(n)
+        if n == 0:
+            continue
+        pairs += visible_pairs(L - 1, n, window)
+        first = L - n
+        lo = max(0, first - window + 1) if window > 0 else 0
+        rows += L - lo
+    flop = 4 * D * Hq * pairs
+    byts = elt * (2 * sum(int(n) for n in q_lens) * Hq * D + 2 * rows * Hkv * D)
+    return flop, byts
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "prefill": ["prefill_bf16.hip", "common.h", "kernels.h"],
+    "decode": ["decode_bf16.hip", "common.h", "kernels.h"],
+}
+
+
+def load_traffic(kind, launches_per_call=1):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the kernel source as it is now; None otherwise."""
+    path = os.path.join(PROFILES, f"traffic_{kind}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kind]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- CPU oracle baseline
+
+def cpu_baseline(seconds: float):
+    """Time the fp64 oracle on a bounded row sample of the dense layer-shaped prefill."""
+    import numpy as np
+
+    import gqa_inputs as gi
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    p = gi.c2_layer()
+    q, k, v = p.q.f64, p.k.f64, p.v.f64
+    S, Hq, D = 4096, 64, 64
+    rng = np.random.default_rng(0)
+    done_rows = 0
+    flop = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        rows = np.sort(rng.choice(S, size=16, replace=False))
+        oracle.prefill_rows_ref(q, k, v, p.sinks, 0, p.scale, rows=rows)
+        done_rows += len(rows)
+        flop += 4 * D * Hq * int((rows + 1).sum())
+    dt = time.perf_counter() - t0
+    return {
+        "value": flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"dense layer-shaped prefill (B1 S4096 64/8 heads), {done_rows} query rows drawn uniformly, "
+                  f"all 64 heads, fp64 NumPy oracle, {dt:.1f} s",
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return None
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--parts", default="all", help="comma list of stages to run (profiling aid)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              f"(the attention path is not sharded across GPUs in this library)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import attention_gqa_causal_amd as gq
+    import gqa_inputs as gi
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    gq.lib()
+
+    def up(t):
+        return gi.to_torch(t, dev)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    stages = {}
+    want = None if args.parts == "all" else set(args.parts.split(","))
+
+    # 1. layer-shaped prefill
+    p = gi.c2_layer()
+    B, S, Hq, Hkv, D = p.dims
+    pq, pk, pv, ps = up(p.q), up(p.k), up(p.v), f32(p.sinks)
+    pout = torch.empty_like(pq)
+    for name, W in (("prefill_dense", 0), ("prefill_swa128", 128)):
+        fl, by = prefill_work(B, S, Hq, Hkv, D, W)
+        stages[name] = dict(fn=(lambda W=W: gq.attn_prefill(pq, pk, pv, ps, window=W, out=pout)), flop=fl, bytes=by,
+                            bound="mfma" if W == 0 else "hbm")
+
+    # 2. batched decode
+    d = gi.c3_decode()
+    dq, dk, dv, dsl, ds = up(d.q), up(d.k), up(d.v), i32(d.seqlens), f32(d.sinks)
+    Bd, Ld = d.k.shape[0], d.k.shape[1]
+    for name, W in (("decode_dense", 0), ("decode_swa128", 128)):
+        fl, by = decode_work([int(x) for x in d.seqlens], Hq, Hkv, D, W)
+        nbytes = gq.decode_workspace_size(Bd, Ld, Hq, Hkv, D, W)
+        ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+        stages[name] = dict(fn=(lambda W=W, ws=ws: gq.attn_decode(dq, (dk, dv), dsl, ds, window=W, workspace=ws)),
+                            flop=fl, bytes=by, bound="hbm")
+
+    # 3. ragged + paged
+    r = gi.c5_ragged()
+    rq, rk, rv, rs = up(r.q), up(r.k), up(r.v), f32(r.sinks)
+    rbt, rcu, rsl = i32(r.block_table), i32(r.cu_seqlens_q), i32(r.seqlens_k)
+    for name, W in (("varlen_dense", 0), ("varlen_swa128", 128)):
+        fl, by = varlen_work(r.seqlens_k, r.q_lens, Hq, Hkv, D, W)
+        nbytes = gq.varlen_workspace_size(16, r.max_q_len, r.max_kv_len, Hq, Hkv, D, W)
+        ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+        stages[name] = dict(fn=(lambda W=W, ws=ws: gq.attn_varlen_paged(
+            rq, (rk, rv), rbt, rcu, rsl, rs, window=W, max_q_len=r.max_q_len, max_kv_len=r.max_kv_len,
+            workspace=ws)), flop=fl, bytes=by, bound="mfma" if W == 0 else "hbm")
+
+    if want is not None:
+        stages = {k: v for k, v in stages.items() if k in want}
+    names = list(stages)
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        for n in names:
+            stages[n]["fn"]()
+    torch.cuda.synchronize()
+
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+          for n in names}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for n in names:
+            a, b = ev[n][i]
+            a.record()
+            stages[n]["fn"]()
+            b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    parts = {}
+    for n in names:
+        ms = sorted(a.elapsed_time(b) for a, b in ev[n])
+        avg = sum(ms) / len(ms)
+        st = stages[n]
+        t = avg / 1e3
+        t_roof = max(st["flop"] / (PEAK_BF16_TFLOPS * 1e12), st["bytes"] / (PEAK_HBM_GBPS * 1e9))
+        parts[n] = {
+            "ms": round(avg, 5),
+            "ms_median": round(ms[len(ms) // 2], 5),
+            "tflops": round(st["flop"] / t / 1e12, 3),
+            "gbps": round(st["bytes"] / t / 1e9, 2),
+            "bound": st["bound"],
+            "roofline_frac": round(t_roof / t, 4),
+            "alg_flop": st["flop"],
+            "alg_bytes": st["bytes"],
+        }
+
+    out = {
+        "metric": METRIC,
+        "value": None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "layer-shaped prefill B1 S4096 Hq64 Hkv8 D64 bf16, dense layer then 128-token sliding-window "
+                        "layer (value); each step also runs batched decode B64 cache 8192 (dense, window 128) and "
+                        "ragged+paged 16 sequences (dense, window 128)",
+            "global_batch": 1,
+            "seq_len": 4096,
+            "parallelism": "single GPU",
+        },
+        "parts": parts,
+    }
+    if "prefill_dense" in parts and "prefill_swa128" in parts:
+        tot_f = stages["prefill_dense"]["flop"] + stages["prefill_swa128"]["flop"]
+        tot_t = (parts["prefill_dense"]["ms"] + parts["prefill_swa128"]["ms"]) / 1e3
+        out["value"] = round(tot_f / tot_t / 1e12, 3)
+    if "prefill_dense" in parts:
+        pd = parts["prefill_dense"]
+        out["roofline"] = {
+            "bound": "mfma",
+            "achieved": pd["tflops"],
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(pd["tflops"] / PEAK_BF16_TFLOPS, 4),
+            "traffic": load_traffic("prefill"),
+            "kernel": "prefill_bf16_kernel<KV_BATCHED> (dense, S4096)",
+        }
+    if "decode_dense" in parts:
+        dd = parts["decode_dense"]
+        out["roofline_decode"] = {
+            "bound": "hbm",
+            "achieved": dd["gbps"],
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(dd["gbps"] / PEAK_HBM_GBPS, 4),
+            "traffic": load_traffic("decode"),
+            "kernel": "decode_split_kernel<KV_BATCHED> (dense, B64 x 8192)",
+        }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
