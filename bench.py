@@ -155,6 +155,50 @@ def _cpu_model():
     return None
 
 
+# ----------------------------------------------------------------------------- stages
+
+def add_prefill(stages, gq, p, up, f32, dev):
+    import torch
+
+    B, S, Hq, Hkv, D = p.dims
+    pq, pk, pv, ps = up(p.q), up(p.k), up(p.v), f32(p.sinks)
+    pout = torch.empty_like(pq)
+    for name, W in (("prefill_dense", 0), ("prefill_swa128", 128)):
+        fl, by = prefill_work(B, S, Hq, Hkv, D, W)
+        stages[name] = dict(fn=(lambda W=W: gq.attn_prefill(pq, pk, pv, ps, window=W, out=pout)), flop=fl, bytes=by,
+                            bound="mfma" if W == 0 else "hbm")
+
+
+def add_decode(stages, gq, d, up, i32, f32, dev):
+    import torch
+
+    Hq, Hkv, D = d.q.shape[1], d.k.shape[2], d.q.shape[2]
+    dq, dk, dv, dsl, ds = up(d.q), up(d.k), up(d.v), i32(d.seqlens), f32(d.sinks)
+    Bd, Ld = d.k.shape[0], d.k.shape[1]
+    for name, W in (("decode_dense", 0), ("decode_swa128", 128)):
+        fl, by = decode_work([int(x) for x in d.seqlens], Hq, Hkv, D, W)
+        nbytes = gq.decode_workspace_size(Bd, Ld, Hq, Hkv, D, W)
+        ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+        stages[name] = dict(fn=(lambda W=W, ws=ws: gq.attn_decode(dq, (dk, dv), dsl, ds, window=W, workspace=ws)),
+                            flop=fl, bytes=by, bound="hbm")
+
+
+def add_varlen(stages, gq, r, up, i32, f32, dev):
+    import torch
+
+    Hq, Hkv, D = r.q.shape[1], r.k.shape[2], r.q.shape[2]
+    rq, rk, rv, rs = up(r.q), up(r.k), up(r.v), f32(r.sinks)
+    rbt, rcu, rsl = i32(r.block_table), i32(r.cu_seqlens_q), i32(r.seqlens_k)
+    nseq = len(r.seqlens_k)
+    for name, W in (("varlen_dense", 0), ("varlen_swa128", 128)):
+        fl, by = varlen_work(r.seqlens_k, r.q_lens, Hq, Hkv, D, W)
+        nbytes = gq.varlen_workspace_size(nseq, r.max_q_len, r.max_kv_len, Hq, Hkv, D, W)
+        ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+        stages[name] = dict(fn=(lambda W=W, ws=ws: gq.attn_varlen_paged(
+            rq, (rk, rv), rbt, rcu, rsl, rs, window=W, max_q_len=r.max_q_len, max_kv_len=r.max_kv_len,
+            workspace=ws)), flop=fl, bytes=by, bound="mfma" if W == 0 else "hbm")
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -196,39 +240,18 @@ def main():
     stages = {}
     want = None if args.parts == "all" else set(args.parts.split(","))
 
+    def wanted(prefix):
+        return want is None or any(w.startswith(prefix) for w in want)
+
     # 1. layer-shaped prefill
-    p = gi.c2_layer()
-    B, S, Hq, Hkv, D = p.dims
-    pq, pk, pv, ps = up(p.q), up(p.k), up(p.v), f32(p.sinks)
-    pout = torch.empty_like(pq)
-    for name, W in (("prefill_dense", 0), ("prefill_swa128", 128)):
-        fl, by = prefill_work(B, S, Hq, Hkv, D, W)
-        stages[name] = dict(fn=(lambda W=W: gq.attn_prefill(pq, pk, pv, ps, window=W, out=pout)), flop=fl, bytes=by,
-                            bound="mfma" if W == 0 else "hbm")
-
+    if wanted("prefill"):
+        add_prefill(stages, gq, gi.c2_layer(), up, f32, dev)
     # 2. batched decode
-    d = gi.c3_decode()
-    dq, dk, dv, dsl, ds = up(d.q), up(d.k), up(d.v), i32(d.seqlens), f32(d.sinks)
-    Bd, Ld = d.k.shape[0], d.k.shape[1]
-    for name, W in (("decode_dense", 0), ("decode_swa128", 128)):
-        fl, by = decode_work([int(x) for x in d.seqlens], Hq, Hkv, D, W)
-        nbytes = gq.decode_workspace_size(Bd, Ld, Hq, Hkv, D, W)
-        ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
-        stages[name] = dict(fn=(lambda W=W, ws=ws: gq.attn_decode(dq, (dk, dv), dsl, ds, window=W, workspace=ws)),
-                            flop=fl, bytes=by, bound="hbm")
-
+    if wanted("decode"):
+        add_decode(stages, gq, gi.c3_decode(), up, i32, f32, dev)
     # 3. ragged + paged
-    r = gi.c5_ragged()
-    rq, rk, rv, rs = up(r.q), up(r.k), up(r.v), f32(r.sinks)
-    rbt, rcu, rsl = i32(r.block_table), i32(r.cu_seqlens_q), i32(r.seqlens_k)
-    for name, W in (("varlen_dense", 0), ("varlen_swa128", 128)):
-        fl, by = varlen_work(r.seqlens_k, r.q_lens, Hq, Hkv, D, W)
-        nbytes = gq.varlen_workspace_size(16, r.max_q_len, r.max_kv_len, Hq, Hkv, D, W)
-        ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
-        stages[name] = dict(fn=(lambda W=W, ws=ws: gq.attn_varlen_paged(
-            rq, (rk, rv), rbt, rcu, rsl, rs, window=W, max_q_len=r.max_q_len, max_kv_len=r.max_kv_len,
-            workspace=ws)), flop=fl, bytes=by, bound="mfma" if W == 0 else "hbm")
-
+    if wanted("varlen"):
+        add_varlen(stages, gq, gi.c5_ragged(), up, i32, f32, dev)
     if want is not None:
         stages = {k: v for k, v in stages.items() if k in want}
     names = list(stages)
