@@ -162,7 +162,7 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, const float* s
   a.out = (__bf16*)out; a.lse = lse; a.seq = seq;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = window; a.scale_log2 = sl2;
   const long ntiles = (long)((S + 31) / 32) * G;
-  a.wg_per_seq = (int)((ntiles + 7) / 8);
+  a.wg_per_seq = (int)((ntiles + prefill_ntiles_per_wg() - 1) / prefill_ntiles_per_wg());
   a.skip_single = 0;
   a.lse_sb = (int64_t)Hq * S; a.lse_sh = S; a.lse_row0 = 0;
   if ((long long)B * Hkv * a.wg_per_seq > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
@@ -298,7 +298,7 @@ int gqa_attn_varlen_paged(const void* q, const void* k_cache, const void* v_cach
     a.out = (__bf16*)out; a.lse = lse; a.seq = seq;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = window; a.scale_log2 = sl2;
     const long ntiles = (long)((max_q_len + 31) / 32) * G;
-    a.wg_per_seq = (int)((ntiles + 7) / 8);
+    a.wg_per_seq = (int)((ntiles + prefill_ntiles_per_wg() - 1) / prefill_ntiles_per_wg());
     a.skip_single = 1;
     a.lse_sb = 0; a.lse_sh = Tq; a.lse_row0 = 1;
     if ((long long)B * Hkv * a.wg_per_seq > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");

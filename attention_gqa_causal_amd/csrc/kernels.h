@@ -67,6 +67,7 @@ struct Fp32Args {
   int lse_row0;
 };
 
+int prefill_ntiles_per_wg();  // N-tiles (32 rows of one head) per prefill workgroup
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int kv_mode, bool varlen_q, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int kv_mode, hipStream_t s);
 hipError_t launch_fp32(const Fp32Args& a, int kv_mode, hipStream_t s);

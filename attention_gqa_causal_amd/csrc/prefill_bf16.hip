@@ -11,33 +11,164 @@
 // "N-tiles"; an N-tile is 32 query positions of one query head of g's group.
 // For the 64/8 head layout that is all 8 heads of the group at 32 positions, so
 // every K/V tile staged in LDS is used by the whole group.  Each of the 4 waves
-// owns two N-tiles (64 query rows).
+// owns two N-tiles (64 query rows); two workgroups share a CU.
 //
 // The scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-//   A = K tile rows (keys) read straight from LDS, B = Q^T held in registers.
-// In the MFMA result a lane holds 16 keys of ONE query row, so the row max and
-// the rescale of the output are per lane (one exchange with lane ^ 32 for the
-// max).  The output is also accumulated transposed, O^T += V^T P^T, with P^T
-// taken from the score registers as they are (the contraction order over keys
-// is free) and V^T read from a transposed LDS copy of the V tile.
+// A = rows of the K tile (keys) from LDS, B = Q^T held in registers.  In the
+// result a lane holds 16 keys of ONE query row, so the row max and the output
+// rescale are per lane (one lane^32 exchange for the max).  The output is also
+// accumulated transposed, O^T += V^T P^T: P^T comes from the score registers as
+// they are (the contraction order over keys is free), and V^T from the V tile,
+// stored in LDS in its natural [key][d] layout and read with the transposing
+// LDS load ds_read_b64_tr_b16.
+//
+// Per 64-key tile a wave computes the scores of both its N-tiles (each K
+// operand read from LDS feeds two MFMAs), runs the two softmax steps, then
+// accumulates P V for both (each V operand feeds two MFMAs).  The two
+// workgroups sharing a CU overlap each other's MFMA and VALU phases.  K/V
+// tiles are staged one tile ahead in double-buffered LDS, with one workgroup
+// barrier per tile.  The running max moves lazily (only when a tile max
+// exceeds it by more than 2^8), so the output is almost never rescaled.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace gqa {
 namespace {
 
 constexpr int BK = 64;          // keys per tile
-constexpr int NTHREADS = 256;   // 4 waves
-constexpr int KS = 72;          // LDS row stride (elements) of K [key][d]
-constexpr int VS = 68;          // LDS row stride (elements) of V^T [d][key]
+constexpr int NWAVES = 4;
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int NT_WG = 2 * NWAVES;  // N-tiles per workgroup
+constexpr int KS = 72;          // LDS row stride (elements) of K [key][d]: conflict-free 16-byte row reads
+constexpr int VS = 96;          // LDS row stride (elements) of V [key][d]: conflict-free transposing reads
+constexpr float kLazy = 8.f;    // log2 headroom before the reference max is moved
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+// S^T for both N-tiles: keys 32*mt + (MFMA row) of the tile x 32 query rows
+__device__ __forceinline__ void qk_tile(f32x16 (&s0)[2], f32x16 (&s1)[2], const __bf16* ks, const bf16x8 (&qb)[2][4],
+                                        int lr, int lg) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + (32 * mt + lr) * KS + 16 * k + 8 * lg);
+      s0[mt] = mfma32(ka, qb[0][k], k == 0 ? zero16() : s0[mt]);
+      s1[mt] = mfma32(ka, qb[1][k], k == 0 ? zero16() : s1[mt]);
+    }
+  }
+}
+
+// O^T += V^T P^T for one N-tile.  In 16-lane group c of the wave, lane j reads 4
+// consecutive d of key row (j/4); the transposing load hands lane i of the
+// group the 4 keys at d = dbase + i.  The key order of k-step u matches the
+// score registers: 16u + {4lg..4lg+3, 8+4lg..8+4lg+3}.
+__device__ __forceinline__ void pv_tile(f32x16 (&o)[2][2], const __bf16* vs, const bf16x8 (&p0)[4],
+                                        const bf16x8 (&p1)[4], int vofs) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      const __bf16* base = vs + vofs + 16 * u * VS + 32 * dt;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * VS));
+      const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const bf16x8 va = __builtin_bit_cast(bf16x8, w);
+      o[0][dt] = mfma32(va, p0[u], o[0][dt]);
+      o[1][dt] = mfma32(va, p1[u], o[1][dt]);
+    }
+  }
+}
+
+// Online-softmax step of one N-tile on one 64-key tile: optional mask, running
+// max with lazy update, exponentials, partial row sum of the bf16 weights,
+// bf16 packing into the P^T operand.  Lane holds keys
+// j0 + 32*mt + 8*(r/4) + 4*lg + r%4 of query row lr.  Returns alpha (1 when the
+// reference max did not move) and sets *up when it moved.
+template <bool MASKED>
+__device__ __forceinline__ float softmax_ntile(f32x16 (&s)[2], bf16x8 (&pb)[4], float& m, float& l, bool& up,
+                                               int j0, int p, int W, float c, int lg) {
+  if (MASKED) {
+    // visible iff (key - j0 - 4lg) is in (dl, dh]: compare against per-lane bounds so
+    // the per-register key offsets stay compile-time constants
+    const int dh = p - j0 - 4 * lg;
+    const int dl = W > 0 ? dh - W : -0x40000000;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 32 * mt + 8 * (r >> 2) + (r & 3);
+        if (off > dh || off <= dl) s[mt][r] = -INFINITY;
+      }
+  }
+  // tree max over the 32 scores of this lane, then across the lane pair (l, l^32)
+  float t[11];
+#pragma unroll
+  for (int q = 0; q < 10; ++q) {
+    const int a = 3 * q, b = a + 1, cc = a + 2;
+    t[q] = fmaxf(fmaxf(s[a >> 4][a & 15], s[b >> 4][b & 15]), s[cc >> 4][cc & 15]);
+  }
+  t[10] = fmaxf(s[1][14], s[1][15]);
+  const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]);
+  const float u1 = fmaxf(fmaxf(t[3], t[4]), t[5]);
+  const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]);
+  const float u3 = fmaxf(t[9], t[10]);
+  float mx = fmaxf(fmaxf(u0, u1), fmaxf(u2, u3));
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
+  const float mt_ = mx * c;
+  up = mt_ > m + kLazy;
+  const float m_new = up ? mt_ : m;
+  const float alpha = up ? fast_exp2(m - m_new) : 1.f;
+  m = m_new;
+  float rs = 0.f;
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    bf16x8 tt;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      bf16x2 pk;
+      pk[0] = (__bf16)fast_exp2(__builtin_fmaf(s[u >> 1][8 * (u & 1) + e], c, -m_new));
+      pk[1] = (__bf16)fast_exp2(__builtin_fmaf(s[u >> 1][8 * (u & 1) + e + 1], c, -m_new));
+      tt[e] = pk[0];
+      tt[e + 1] = pk[1];
+      rs = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, rs, false);
+    }
+    pb[u] = tt;
+  }
+  l = l * alpha + rs;
+  return alpha;
+}
+
+__device__ __forceinline__ void rescale(f32x16 (&o)[2], float alpha, bool up) {
+  if (__builtin_amdgcn_ballot_w64(up)) {
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) o[dt] *= alpha;
+  }
+}
+
 template <int MODE, bool VARLEN>
 __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[BK * KS];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[kHeadDim * VS];
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BK * KS];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BK * VS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -68,33 +199,38 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   const SeqView sv = seq_view<MODE>(a.seq, b, VARLEN);
   const int G = a.G;
   const int n_ntiles = ((sv.q_len + 31) >> 5) * G;
-  if (tg < 0 || tg * 8 >= n_ntiles) return;  // uniform over the workgroup
+  if (tg < 0 || tg * NT_WG >= n_ntiles) return;  // uniform over the workgroup
   if (a.skip_single && sv.q_len == 1) return;
   const int pos_off = sv.kv_len - sv.q_len;
   const int W = a.window;
+  const float c = a.scale_log2;
 
   // ---- this wave's two N-tiles
-  int nt_t0[2], nt_hq[2];
+  int nt_t0[2], nt_hq[2], pos0[2], phi[2];
   bool nt_valid[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int n = tg * 8 + wave * 2 + i;
+    const int n = tg * NT_WG + wave * 2 + i;
     nt_valid[i] = n < n_ntiles;
     const int pb = n / G;
     nt_t0[i] = pb * 32;
     nt_hq[i] = g * G + (n - pb * G);
+    pos0[i] = pos_off + nt_t0[i];
+    phi[i] = pos_off + min(nt_t0[i] + 31, sv.q_len - 1);
   }
 
   // ---- key range of the whole workgroup
-  const int n_last = min(tg * 8 + 7, n_ntiles - 1);
-  const int t_min = ((tg * 8) / G) * 32;
+  const int n_last = min(tg * NT_WG + NT_WG - 1, n_ntiles - 1);
+  const int t_min = ((tg * NT_WG) / G) * 32;
   const int t_max = min((n_last / G) * 32 + 31, sv.q_len - 1);
   const int p_min = pos_off + t_min;
   const int p_max = pos_off + t_max;
   const int lo = W > 0 ? max(0, p_min - W + 1) : 0;
   const int hi = min(p_max, sv.kv_len - 1);  // inclusive
+  const int j_begin = lo & ~(BK - 1);
+  const int n_tiles = hi >= j_begin ? (hi - j_begin) / BK + 1 : 0;
 
-  // ---- Q^T operands (B of S^T = K Q^T): lane holds row lr, d = 16*ks + 8*lg .. +7
+  // ---- Q^T operands (B of S^T = K Q^T): lane holds row lr, d = 16*k + 8*lg .. +7
   bf16x8 qb[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -102,15 +238,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
     const bool ok = nt_valid[i] && t < sv.q_len;
     const __bf16* qp = a.q + ((sv.q_row0 + t) * a.Hq + nt_hq[i]) * (int64_t)kHeadDim + 8 * lg;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (ok) w = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
-      qb[i][ks] = __builtin_bit_cast(bf16x8, w);
+    for (int k = 0; k < 4; ++k) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ok) v = *reinterpret_cast<const u32x4*>(qp + 16 * k);
+      qb[i][k] = __builtin_bit_cast(bf16x8, v);
     }
   }
-
-  // ---- running softmax state per (N-tile, lane): max in log2 units and partial sum
   float m_run[2], l_run[2];
+  f32x16 o[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const float s2 = a.sinks ? a.sinks[nt_hq[i]] * kLog2e : -INFINITY;
@@ -118,150 +253,83 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
     m_run[i] = none ? kNegBig : s2;
     // the sink's own term e^{s-m} = 1 at m = s; only one lane of the pair carries it
     l_run[i] = (none || lg) ? 0.f : 1.f;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) o[i][dt] = zero16();
   }
-  f32x16 o[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][dt][r] = 0.f;
 
-  // ---- tile loader: 512 16-byte chunks of K and of V per tile, 2 of each per thread
+  // ---- global -> register -> LDS staging: 512 16-byte chunks per K or V tile, 2 of each per thread
   const int64_t kv_stride = (int64_t)a.Hkv * kHeadDim;
-  u32x4 kreg[2], vreg[2];
-  auto load_tile = [&](int j0) {
+  const __bf16* kbase = a.k + g * kHeadDim;
+  const __bf16* vbase = a.v + g * kHeadDim;
+  auto load_rows = [&](const __bf16* base, int t, u32x4 (&reg)[2]) {
+    const int j0 = j_begin + BK * t;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int chunk = tid + c * NTHREADS;
-      const int key = chunk >> 3;
-      const int col = (chunk & 7) * 8;
-      const int j = j0 + key;
-      u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-      if (j <= hi) {
-        const int64_t off = kv_row<MODE>(a.seq, sv, j) * kv_stride + g * kHeadDim + col;
-        kw = *reinterpret_cast<const u32x4*>(a.k + off);
-        vw = *reinterpret_cast<const u32x4*>(a.v + off);
-      }
-      kreg[c] = kw;
-      vreg[c] = vw;
+    for (int cc = 0; cc < 2; ++cc) {
+      const int chunk = tid + cc * NTHREADS;
+      const int j = j0 + (chunk >> 3);
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (j <= hi) v = *reinterpret_cast<const u32x4*>(base + kv_row<MODE>(a.seq, sv, j) * kv_stride + (chunk & 7) * 8);
+      reg[cc] = v;
     }
   };
-  auto store_tile = [&]() {
+  auto store_rows = [&](__bf16* dst, int stride, const u32x4 (&reg)[2]) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int chunk = tid + c * NTHREADS;
-      const int key = chunk >> 3;
-      const int col = (chunk & 7) * 8;
-      *reinterpret_cast<u32x4*>(&Ks[key * KS + col]) = kreg[c];
-      const uint16_t* hv = reinterpret_cast<const uint16_t*>(&vreg[c]);
-      uint16_t* vt = reinterpret_cast<uint16_t*>(Vt);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vt[(col + e) * VS + key] = hv[e];
+    for (int cc = 0; cc < 2; ++cc) {
+      const int chunk = tid + cc * NTHREADS;
+      *reinterpret_cast<u32x4*>(dst + (chunk >> 3) * stride + (chunk & 7) * 8) = reg[cc];
     }
   };
+  auto tile_masked = [&](int t) {
+    const int j0 = j_begin + BK * t;
+    bool m = false;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) m |= !((j0 + BK - 1 <= pos0[i]) && (W <= 0 || j0 > phi[i] - W));
+    return m;
+  };
+  // lane's address offset for the transposing V reads (see pv_ntile)
+  const int vofs = (4 * (lane >> 5) + ((lane & 15) >> 2)) * VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  const int j_begin = lo & ~(BK - 1);
-  if (j_begin <= hi) load_tile(j_begin);
-
-  for (int j0 = j_begin; j0 <= hi; j0 += BK) {
-    __syncthreads();  // everyone is done reading the previous tile
-    store_tile();
+  // one 64-key tile; K/V of tile t are in buffer t % 2, tile t+1 is staged into the other
+  auto body = [&](auto mask_tag, int t) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int buf = t & 1;
+    const int j0 = j_begin + BK * t;
+    const bool next = t + 1 < n_tiles;
+    u32x4 kreg[2], vreg[2];
+    if (next) {
+      load_rows(kbase, t + 1, kreg);
+      load_rows(vbase, t + 1, vreg);
+    }
+    f32x16 s0[2], s1[2];
+    bf16x8 p0[4], p1[4];
+    bool up0, up1;
+    qk_tile(s0, s1, Ks[buf], qb, lr, lg);
+    const float al0 = softmax_ntile<MASK>(s0, p0, m_run[0], l_run[0], up0, j0, pos0[0] + lr, W, c, lg);
+    const float al1 = softmax_ntile<MASK>(s1, p1, m_run[1], l_run[1], up1, j0, pos0[1] + lr, W, c, lg);
+    rescale(o[0], al0, up0);
+    rescale(o[1], al1, up1);
+    pv_tile(o, Vs[buf], p0, p1, vofs);
+    if (next) {
+      store_rows(Ks[buf ^ 1], KS, kreg);
+      store_rows(Vs[buf ^ 1], VS, vreg);
+    }
     __syncthreads();
-    if (j0 + BK <= hi) load_tile(j0 + BK);  // in flight during this tile's math
+  };
 
-    // classify this key tile for each N-tile: skip / unmasked / masked
-    bool active[2], masked[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int plo = pos_off + nt_t0[i];
-      const int phi = pos_off + min(nt_t0[i] + 31, sv.q_len - 1);
-      const bool none = !nt_valid[i] || j0 > phi || (W > 0 && j0 + BK - 1 <= plo - W);
-      const bool full = (j0 + BK - 1 <= plo) && (W <= 0 || j0 > phi - W);
-      active[i] = !none;
-      masked[i] = !full;
+  if (n_tiles > 0) {
+    {
+      u32x4 r[2];
+      load_rows(kbase, 0, r);
+      store_rows(Ks[0], KS, r);
+      load_rows(vbase, 0, r);
+      store_rows(Vs[0], VS, r);
     }
-    if (!active[0] && !active[1]) continue;
-
-    // S^T tile: keys 32*mt + (row of the MFMA output) x query rows
-    f32x16 s[2][2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[mt][i][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[(32 * mt + lr) * KS + 16 * ks + 8 * lg]);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) s[mt][i] = mfma32(ka, qb[i][ks], s[mt][i]);
-      }
-    }
-
-    // online softmax (exp2 domain); lane holds keys 32*mt + 8*(r/4) + 4*lg + r%4 of row lr
-    bf16x8 pb[2][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      if (masked[i]) {
-        const int p = pos_off + nt_t0[i] + lr;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + 32 * mt + 8 * (r >> 2) + 4 * lg + (r & 3);
-            const bool vis = key <= p && (W <= 0 || key > p - W);
-            if (!vis) s[mt][i][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][i][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[i], mx * a.scale_log2);
-      const float alpha = fast_exp2(m_run[i] - m_new);
-      m_run[i] = m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(s[mt][i][r], a.scale_log2, -m_new));
-          s[mt][i][r] = p;
-          rs += p;
-        }
-      l_run[i] = l_run[i] * alpha + rs;
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[i][dt][r] *= alpha;
-      // P^T operands: MFMA k-step u takes registers 8*(u%2) .. +7 of score tile u/2
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        bf16x8 t;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) t[e] = (__bf16)s[u >> 1][i][8 * (u & 1) + e];
-        pb[i][u] = t;
-      }
-    }
-
-    // O^T += V^T P^T; the key order of k-step u is 16u + {4lg..4lg+3, 8+4lg..8+4lg+3}
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const __bf16* vp = &Vt[(32 * dt + lr) * VS + 16 * u + 4 * lg];
-        const u32x2 v0 = *reinterpret_cast<const u32x2*>(vp);
-        const u32x2 v1 = *reinterpret_cast<const u32x2*>(vp + 8);
-        const u32x4 vw = {v0[0], v0[1], v1[0], v1[1]};
-        const bf16x8 va = __builtin_bit_cast(bf16x8, vw);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) o[i][dt] = mfma32(va, pb[i][u], o[i][dt]);
-      }
+    __syncthreads();
+    std::true_type MSK;
+    std::false_type PLN;
+    for (int t = 0; t < n_tiles; ++t) {
+      if (tile_masked(t)) body(MSK, t);
+      else body(PLN, t);
     }
   }
 
@@ -269,7 +337,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     if (!nt_valid[i]) continue;
-    const float lt = l_run[i] + __shfl_xor(l_run[i], 32, 64);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[i]), __float_as_uint(l_run[i]), false, false);
+    const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     const int t = nt_t0[i] + lr;
     if (t >= sv.q_len) continue;
     const float inv = lt > 0.f ? 1.f / lt : (lt == 0.f ? 0.f : lt);
@@ -277,12 +346,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int d0 = 32 * dt + 8 * c + 4 * lg;
-        u32x2 w;
-        w[0] = pack_bf16x2(o[i][dt][4 * c + 0] * inv, o[i][dt][4 * c + 1] * inv);
-        w[1] = pack_bf16x2(o[i][dt][4 * c + 2] * inv, o[i][dt][4 * c + 3] * inv);
-        *reinterpret_cast<u32x2*>(op + d0) = w;
+      for (int cq = 0; cq < 4; ++cq) {
+        const int d0 = 32 * dt + 8 * cq + 4 * lg;
+        u32x2 v;
+        v[0] = pack_bf16x2(o[i][dt][4 * cq + 0] * inv, o[i][dt][4 * cq + 1] * inv);
+        v[1] = pack_bf16x2(o[i][dt][4 * cq + 2] * inv, o[i][dt][4 * cq + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + d0) = v;
       }
     if (a.lse && lg == 0) {
       const float v = (lt == 0.f) ? -INFINITY : (m_run[i] + __log2f(lt)) * kLn2;
@@ -293,6 +362,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
 }
 
 }  // namespace
+
+int prefill_ntiles_per_wg() { return NT_WG; }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int kv_mode, bool varlen_q, hipStream_t s) {
   const int grid = a.B * a.Hkv * a.wg_per_seq;

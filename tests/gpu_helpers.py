@@ -10,9 +10,9 @@ import gqa_inputs as gi
 # bf16 I/O: max |err| <= 2e-2 and mean |err| <= 2e-3; fp32 I/O: max |err| <= 1e-4
 BF16_MAX, BF16_MEAN = 2e-2, 2e-3
 FP32_MAX = 1e-4
-# log-sum-exp is fp32 in both paths; bf16 inputs are exact in fp32, so only fp32
-# rounding of the sums (and the bf16 rounding of P in the sum's companion) remain
-LSE_TOL = 2e-3
+# the log-sum-exp output is held to the same bar as the attention output of its
+# path: the bf16 kernels form the normaliser from the bf16-rounded weights they
+# feed to the matrix cores (relative error up to 2^-9 per weight)
 
 
 def say(msg: str):
@@ -56,10 +56,13 @@ def assert_fp32_close(got, ref, what=""):
     return mx, mean
 
 
-def assert_lse_close(got, ref, what=""):
+def assert_lse_close(got, ref, what="", fp32=False):
     fin = np.isfinite(ref)
     assert np.array_equal(np.isfinite(got), fin), f"{what}: lse finiteness differs"
     assert (got[~fin] == ref[~fin]).all(), f"{what}: infinite lse differs"
     if fin.any():
-        mx = float(np.abs(got[fin] - ref[fin]).max())
-        assert mx <= LSE_TOL, f"{what}: lse max err {mx:.3e}"
+        e = np.abs(got[fin] - ref[fin])
+        if fp32:
+            assert e.max() <= FP32_MAX, f"{what}: lse max err {e.max():.3e}"
+        else:
+            assert e.max() <= BF16_MAX and e.mean() <= BF16_MEAN, f"{what}: lse max {e.max():.3e} mean {e.mean():.3e}"
