@@ -82,17 +82,18 @@ struct SplitPlan {
   int split_len;
 };
 
-// Split of the decode key range so that the grid covers the chip about twice;
-// each split keeps at least 4 tiles (one per wave) of 64 keys.
+// Split of the decode key range: enough workgroups to keep about 16 per CU in
+// the queue (the streaming loads then overlap the merge of finished ones),
+// while every split keeps at least 1024 keys (4 tiles of 64 per wave).
 SplitPlan plan_splits(int B, int Hkv, int G, int Lmax, int window) {
   const int eff = window > 0 ? (window < Lmax ? window : Lmax) : Lmax;
   const int n_hc = (G + 15) / 16;
   const long units = (long)B * Hkv * n_hc;
   SplitPlan p{1, 64};
   if (eff <= 0 || units <= 0) return p;
-  const long target = 2L * num_cus();
+  const long target = 16L * num_cus();
   long want = (target + units - 1) / units;
-  const long max_by_len = (eff + 255) / 256;
+  const long max_by_len = eff / 1024;
   if (want > max_by_len) want = max_by_len;
   if (want < 1) want = 1;
   if (want > 64) want = 64;

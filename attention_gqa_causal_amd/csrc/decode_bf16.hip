@@ -14,9 +14,11 @@
 // writes a partial (max, sum, unnormalised output) and a combine kernel merges
 // the splits.
 //
-// Per tile the scores are S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K straight
-// from global memory in the A layout, Q^T in registers, 16 head columns), and
-// the output is O^T += V^T P^T with V^T read from a per-wave transposed LDS copy.
+// Each wave streams whole 128-byte K and V rows of its key tiles with
+// non-temporal loads (the access pattern that reaches the highest HBM rate),
+// stages them in its own LDS slice, and computes S^T = K Q^T on
+// v_mfma_f32_16x16x32_bf16 (K rows from LDS, Q^T in registers, 16 head
+// columns) and O^T += V^T P^T with V^T read by the transposing LDS load.
 #include "kernels.h"
 
 namespace gqa {
@@ -24,18 +26,28 @@ namespace {
 
 constexpr int DT = 64;         // keys per wave tile
 constexpr int DTHREADS = 256;  // 4 waves
-constexpr int VSD = 68;        // LDS row stride (elements) of the per-wave V^T [d][key]
+constexpr int KSD = 72;        // LDS row stride (elements) of a wave's K tile [key][d]
+constexpr int VSD = 80;        // LDS row stride (elements) of a wave's V tile [key][d]
+constexpr int WAVE_LDS = DT * KSD + DT * VSD;  // elements per wave
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// streamed once: non-temporal loads keep the KV cache from evicting reusable lines
+__device__ __forceinline__ u32x4 load_stream(const __bf16* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 template <int MODE>
 __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[4][kHeadDim * VSD];
-  __shared__ float red_m[4][16];
-  __shared__ float red_l[4][16];
-  __shared__ __attribute__((aligned(16))) float red_o[4][16][kHeadDim + 4];
+  // per wave: K tile then V tile; after the key loop the same memory holds the
+  // 4-wave merge buffers
+  __shared__ __attribute__((aligned(16))) __bf16 lds[4 * WAVE_LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -80,63 +92,53 @@ __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a)
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int64_t kv_stride = (int64_t)a.Hkv * kHeadDim;
-  const __bf16* kbase = a.k + g * kHeadDim;
-  const __bf16* vbase = a.v + g * kHeadDim;
-  uint16_t* vt = reinterpret_cast<uint16_t*>(Vt[wave]);
+  const __bf16* kbase = a.k + g * kHeadDim + 8 * (lane & 7);
+  const __bf16* vbase = a.v + g * kHeadDim + 8 * (lane & 7);
+  __bf16* Kw = lds + wave * WAVE_LDS;
+  __bf16* Vw = Kw + DT * KSD;
 
-  // K chunk (kb, ks): key 16*kb + lc, d 32*ks + 8*lq (the MFMA A layout)
-  // V chunk i: key 8*i + lane/8, d 8*(lane%8) (whole 128-byte rows per 8 lanes)
+  // whole 128-byte rows: load i brings keys 8*i + lane/8, 16 bytes at d = 8*(lane%8);
+  // rows past the split repeat its last row (masked below, always in bounds)
   u32x4 kreg[8], vreg[8];
   auto load = [&](int j0) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int j = j0 + 16 * kb + lc;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (j < s_hi) w = *reinterpret_cast<const u32x4*>(kbase + kv_row<MODE>(a.seq, sv, j) * kv_stride + 32 * ks + 8 * lq);
-        kreg[kb * 2 + ks] = w;
-      }
-    }
-#pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int j = j0 + 8 * i + (lane >> 3);
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (j < s_hi) w = *reinterpret_cast<const u32x4*>(vbase + kv_row<MODE>(a.seq, sv, j) * kv_stride + 8 * (lane & 7));
-      vreg[i] = w;
+      const int j = min(j0 + 8 * i + (lane >> 3), s_hi - 1);
+      const int64_t row = kv_row<MODE>(a.seq, sv, j) * kv_stride;
+      kreg[i] = load_stream(kbase + row);
+      vreg[i] = load_stream(vbase + row);
     }
   };
+  // transposing V reads (see below): lane's row/column offset within the V tile
+  const int vofs = (4 * lq + ((lane & 15) >> 2)) * VSD + 4 * (lane & 3);
 
   int j0 = s_lo + wave * DT;
   if (j0 < s_hi) load(j0);
   for (; j0 < s_hi; j0 += 4 * DT) {
-    // transposed copy of this tile's V into the wave's LDS slice
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int key = 8 * i + (lane >> 3);
-      const int d0 = 8 * (lane & 7);
-      const uint16_t* hv = reinterpret_cast<const uint16_t*>(&vreg[i]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vt[(d0 + e) * VSD + key] = hv[e];
+      *reinterpret_cast<u32x4*>(Kw + key * KSD + 8 * (lane & 7)) = kreg[i];
+      *reinterpret_cast<u32x4*>(Vw + key * VSD + 8 * (lane & 7)) = vreg[i];
     }
-    u32x4 kcur[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) kcur[i] = kreg[i];
+    wave_lds_sync();  // the tile is visible to every lane of the wave
     const int jn = j0 + 4 * DT;
     if (jn < s_hi) load(jn);  // next tile in flight during this one's math
 
-    // S^T: 4 blocks of 16 keys x 16 heads
+    // S^T: 4 blocks of 16 keys x 16 heads; A operand = K rows 16*kb + lc, d 32*ks + 8*lq
     f32x4 s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) acc = mfma16(__builtin_bit_cast(bf16x8, kcur[kb * 2 + ks]), qb[ks], acc);
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kw + (16 * kb + lc) * KSD + 32 * ks + 8 * lq);
+        acc = mfma16(ka, qb[ks], acc);
+      }
       s[kb] = acc;
     }
     // lane holds keys j0 + 16*kb + 4*lq + r of head lc
-    const bool full = (j0 + DT <= s_hi);
-    if (!full) {
+    if (j0 + DT > s_hi) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -166,9 +168,9 @@ __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a)
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
 
-    wave_lds_sync();  // the V^T stores above are visible to every lane
-
-    // O^T += V^T P^T over 2 k-steps of 32 keys: keys 32u + {4lq..4lq+3, 16+4lq..16+4lq+3}
+    // O^T += V^T P^T over 2 k-steps of 32 keys: keys 32u + {4lq..4lq+3, 16+4lq..16+4lq+3}.
+    // V^T via the transposing LDS load: in lane group lq, lane j reads 4 d of key
+    // row 32u + 4lq + j/4; the hardware hands lane i the 4 keys at d = 16*dt + i.
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       bf16x8 pbv;
@@ -179,52 +181,56 @@ __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a)
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const uint16_t* vp = &vt[(16 * dt + lc) * VSD + 32 * u + 4 * lq];
-        const u32x2 v0 = *reinterpret_cast<const u32x2*>(vp);
-        const u32x2 v1 = *reinterpret_cast<const u32x2*>(vp + 16);
-        const u32x4 vw = {v0[0], v0[1], v1[0], v1[1]};
-        o[dt] = mfma16(__builtin_bit_cast(bf16x8, vw), pbv, o[dt]);
+        const __bf16* base = Vw + vofs + 32 * u * VSD + 16 * dt;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * VSD));
+        const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[dt] = mfma16(__builtin_bit_cast(bf16x8, w), pbv, o[dt]);
       }
     }
-    wave_lds_sync();  // all lanes done reading V^T before the next overwrite
+    wave_lds_sync();  // all lanes done reading the tile before the next overwrite
   }
 
   // ---- merge the 4 waves: per head max m, sum l, output acc[d]
+  __syncthreads();  // every wave is out of its key loop: the tile memory becomes the merge buffers
+  float* red_m = reinterpret_cast<float*>(lds);  // [4][16]
+  float* red_l = red_m + 64;                    // [4][16]
+  float* red_o = red_l + 64;                    // [4][16][68]
   {
     float lt = l_run + __shfl_xor(l_run, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
     if (lq == 0) {
-      red_m[wave][lc] = m_run;
-      red_l[wave][lc] = lt;
+      red_m[wave * 16 + lc] = m_run;
+      red_l[wave * 16 + lc] = lt;
     }
     // lane holds O^T[d = 16*dt + 4*lq + r][head lc]
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red_o[wave][lc][16 * dt + 4 * lq + r] = o[dt][r];
+      for (int r = 0; r < 4; ++r) red_o[(wave * 16 + lc) * 68 + 16 * dt + 4 * lq + r] = o[dt][r];
   }
   __syncthreads();
   {
     const int hh = tid >> 4;         // head within the chunk
     const int d0 = (tid & 15) * 4;   // 4 output columns
     if (hh < n_heads) {
-      float M = red_m[0][hh];
+      float M = red_m[hh];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) M = fmaxf(M, red_m[w][hh]);
+      for (int w = 1; w < 4; ++w) M = fmaxf(M, red_m[w * 16 + hh]);
       float wsc[4];
       float lsum = 0.f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        wsc[w] = fast_exp2(red_m[w][hh] - M);
-        lsum += red_l[w][hh] * wsc[w];
+        wsc[w] = fast_exp2(red_m[w * 16 + hh] - M);
+        lsum += red_l[w * 16 + hh] * wsc[w];
       }
       float acc[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int cq = 0; cq < 4; ++cq) {
         float t = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) t += red_o[w][hh][d0 + c] * wsc[w];
-        acc[c] = t;
+        for (int w = 0; w < 4; ++w) t += red_o[(w * 16 + hh) * 68 + d0 + cq] * wsc[w];
+        acc[cq] = t;
       }
       const int hq = h_base + hh;
       if (a.n_splits == 1) {
