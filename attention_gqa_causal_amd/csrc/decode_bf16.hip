@@ -99,12 +99,32 @@ __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a)
 
   // whole 128-byte rows: load i brings keys 8*i + lane/8, 16 bytes at d = 8*(lane%8);
   // rows past the split repeat its last row (masked below, always in bounds)
+  // With a paged cache the block ids of a tile's rows are fetched one tile
+  // ahead, so no K/V load waits on the block table.
   u32x4 kreg[8], vreg[8];
+  int blk[8];
+  auto fetch_blk = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      blk[i] = 0;
+      if (MODE == KV_PAGED) {
+        const int j = min(j0 + 8 * i + (lane >> 3), s_hi - 1);
+        blk[i] = a.seq.block_table[(int64_t)b * a.seq.max_blocks + (j >> a.seq.log2_block)];
+      }
+    }
+  };
   auto load = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int j = min(j0 + 8 * i + (lane >> 3), s_hi - 1);
-      const int64_t row = kv_row<MODE>(a.seq, sv, j) * kv_stride;
+      int64_t row;
+      if (MODE == KV_PAGED) {
+        const int bb = min(max(blk[i], 0), a.seq.num_blocks - 1);
+        row = ((int64_t)bb << a.seq.log2_block) + (j & ((1 << a.seq.log2_block) - 1));
+      } else {
+        row = kv_row<MODE>(a.seq, sv, j);
+      }
+      row *= kv_stride;
       kreg[i] = load_stream(kbase + row);
       vreg[i] = load_stream(vbase + row);
     }
@@ -113,7 +133,11 @@ __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a)
   const int vofs = (4 * lq + ((lane & 15) >> 2)) * VSD + 4 * (lane & 3);
 
   int j0 = s_lo + wave * DT;
-  if (j0 < s_hi) load(j0);
+  if (j0 < s_hi) {
+    fetch_blk(j0);
+    load(j0);
+    fetch_blk(j0 + 4 * DT);
+  }
   for (; j0 < s_hi; j0 += 4 * DT) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -123,7 +147,10 @@ __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a)
     }
     wave_lds_sync();  // the tile is visible to every lane of the wave
     const int jn = j0 + 4 * DT;
-    if (jn < s_hi) load(jn);  // next tile in flight during this one's math
+    if (jn < s_hi) {
+      load(jn);  // next tile in flight during this one's math
+      fetch_blk(jn + 4 * DT);
+    }
 
     // S^T: 4 blocks of 16 keys x 16 heads; A operand = K rows 16*kb + lc, d 32*ks + 8*lq
     f32x4 s[4];

@@ -261,15 +261,35 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   const int64_t kv_stride = (int64_t)a.Hkv * kHeadDim;
   const __bf16* kbase = a.k + g * kHeadDim;
   const __bf16* vbase = a.v + g * kHeadDim;
-  auto load_rows = [&](const __bf16* base, int t, u32x4 (&reg)[2]) {
-    const int j0 = j_begin + BK * t;
+  // This thread moves rows r0 and r0 + 32 of every tile (16 bytes at d = 8*(tid%8)).
+  // With a paged cache their block ids are fetched one tile ahead, so no K/V
+  // load waits on the block table.  Rows past the key range repeat row hi (they
+  // are masked, and the loads stay in bounds).
+  const int r0 = tid >> 3;
+  auto fetch_blk = [&](int t, int (&blk)[2]) {
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
-      const int chunk = tid + cc * NTHREADS;
-      const int j = j0 + (chunk >> 3);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (j <= hi) v = *reinterpret_cast<const u32x4*>(base + kv_row<MODE>(a.seq, sv, j) * kv_stride + (chunk & 7) * 8);
-      reg[cc] = v;
+      blk[cc] = 0;
+      if (MODE == KV_PAGED) {
+        const int j = min(j_begin + BK * t + r0 + 32 * cc, hi);
+        blk[cc] = a.seq.block_table[(int64_t)b * a.seq.max_blocks + (j >> a.seq.log2_block)];
+      }
+    }
+  };
+  auto load_kv = [&](int t, const int (&blk)[2], u32x4 (&kreg)[2], u32x4 (&vreg)[2]) {
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const int j = min(j_begin + BK * t + r0 + 32 * cc, hi);
+      int64_t row;
+      if (MODE == KV_PAGED) {
+        const int bb = min(max(blk[cc], 0), a.seq.num_blocks - 1);
+        row = ((int64_t)bb << a.seq.log2_block) + (j & ((1 << a.seq.log2_block) - 1));
+      } else {
+        row = kv_row<MODE>(a.seq, sv, j);
+      }
+      const int64_t off = row * kv_stride + (tid & 7) * 8;
+      kreg[cc] = *reinterpret_cast<const u32x4*>(kbase + off);
+      vreg[cc] = *reinterpret_cast<const u32x4*>(vbase + off);
     }
   };
   auto store_rows = [&](__bf16* dst, int stride, const u32x4 (&reg)[2]) {
@@ -290,16 +310,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   const int vofs = (4 * (lane >> 5) + ((lane & 15) >> 2)) * VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   // one 64-key tile; K/V of tile t are in buffer t % 2, tile t+1 is staged into the other
+  int blk_next[2];  // block ids of tile t+1's rows
   auto body = [&](auto mask_tag, int t) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int buf = t & 1;
     const int j0 = j_begin + BK * t;
     const bool next = t + 1 < n_tiles;
     u32x4 kreg[2], vreg[2];
-    if (next) {
-      load_rows(kbase, t + 1, kreg);
-      load_rows(vbase, t + 1, vreg);
-    }
+    if (next) load_kv(t + 1, blk_next, kreg, vreg);
+    int blk_nn[2];
+    fetch_blk(t + 2, blk_nn);
     f32x16 s0[2], s1[2];
     bf16x8 p0[4], p1[4];
     bool up0, up1;
@@ -313,16 +333,20 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
       store_rows(Ks[buf ^ 1], KS, kreg);
       store_rows(Vs[buf ^ 1], VS, vreg);
     }
+    blk_next[0] = blk_nn[0];
+    blk_next[1] = blk_nn[1];
     __syncthreads();
   };
 
   if (n_tiles > 0) {
     {
-      u32x4 r[2];
-      load_rows(kbase, 0, r);
-      store_rows(Ks[0], KS, r);
-      load_rows(vbase, 0, r);
-      store_rows(Vs[0], VS, r);
+      int blk0[2];
+      u32x4 kr[2], vr[2];
+      fetch_blk(0, blk0);
+      load_kv(0, blk0, kr, vr);
+      fetch_blk(1, blk_next);
+      store_rows(Ks[0], KS, kr);
+      store_rows(Vs[0], VS, vr);
     }
     __syncthreads();
     std::true_type MSK;
