@@ -176,18 +176,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   const int lr = lane & 31;  // row of the 32-wide MFMA tile this lane serves
   const int lg = lane >> 5;  // which half of the K dimension / which 4-row group
 
-  // ---- which (sequence, KV head, tile group): heaviest tile groups first, and
-  // all workgroups of one (sequence, KV head) on the same XCD (dispatch is
-  // round-robin over the 8 XCDs), so its K/V stays in that XCD's L2.
+  // ---- which (sequence, KV head, tile group): all workgroups of one
+  // (sequence, KV head) go to the same XCD (dispatch is round-robin over the 8
+  // XCDs) and are dispatched back to back, heaviest tile group first, so they
+  // stream the same K/V tiles at about the same time out of that XCD's L2.
   const int U = a.B * a.Hkv;
   int unit, rank;
   {
     const int x = blockIdx.x;
     if ((U & 7) == 0) {
-      const int per = U >> 3;
       const int sidx = x >> 3;
-      rank = sidx / per;
-      unit = (x & 7) + 8 * (sidx % per);
+      rank = sidx % a.wg_per_seq;
+      unit = (x & 7) + 8 * (sidx / a.wg_per_seq);
     } else {
       rank = x / U;
       unit = x % U;
