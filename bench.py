@@ -105,6 +105,92 @@ def load_traffic(kind, launches_per_call=1):
     return rec.get("hbm_bytes_per_launch")
 
 
+# ----------------------------------------------------------------------------- HBM traffic from counters
+
+COPY_BYTES = 256 << 20
+
+
+def _read_counter_csv(d, counter):
+    """Per-dispatch values of one counter: list of (kernel name, value in KiB)."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    out = []
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def summarize_counters(fetch_dir, write_dir):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the prefill and decode kernels,
+    scaled by what the same counters read for a plain copy of COPY_BYTES."""
+    import statistics
+
+    fetch = _read_counter_csv(fetch_dir, "FETCH_SIZE")
+    write = _read_counter_csv(write_dir, "WRITE_SIZE")
+
+    def pick(rows, key):
+        vals = [v for n, v in rows if key in n]
+        return statistics.median(vals) if vals else None
+
+    def pick_copy(rows):
+        # the three largest copy dispatches are the timed 256 MiB copies (smaller ones are uploads)
+        vals = sorted(v for n, v in rows if "copyBuffer" in n or "copy_kernel" in n)[-3:]
+        return statistics.median(vals)
+
+    f_copy, w_copy = pick_copy(fetch), pick_copy(write)
+    f_scale = (f_copy * 1024.0) / COPY_BYTES  # counter bytes per true byte read
+    w_scale = (w_copy * 1024.0) / COPY_BYTES
+    res = {}
+    for kind, key, work in (("prefill", "prefill_bf16_kernel", prefill_work(1, 4096, 64, 8, 64, 0)),
+                            ("decode", "decode_split_kernel", decode_work([8192] * 64, 64, 8, 64, 0))):
+        fk, wk = pick(fetch, key), pick(write, key)
+        rd = fk * 1024.0 / f_scale
+        wr = wk * 1024.0 / w_scale
+        rec = {
+            "kernel": key,
+            "workload": "dense prefill B1 S4096 64/8 heads" if kind == "prefill" else "dense decode B64 x 8192 64/8 heads",
+            "fetch_kib_per_dispatch": fk,
+            "write_kib_per_dispatch": wk,
+            "copy_fetch_kib": f_copy,
+            "copy_write_kib": w_copy,
+            "copy_bytes": COPY_BYTES,
+            "fetch_scale": f_scale,
+            "write_scale": w_scale,
+            "hbm_read_bytes_per_launch": rd,
+            "hbm_write_bytes_per_launch": wr,
+            "hbm_bytes_per_launch": rd + wr,
+            "algorithmic_bytes_per_launch": work[1],
+            "source_sha256_16": source_hash(KERNEL_SOURCES[kind]),
+        }
+        res[kind] = rec
+        with open(os.path.join(PROFILES, f"traffic_{kind}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+    lines = ["# HBM traffic per launch from rocprofv3 counters", "",
+             "Commands (repository root, one MI355X; each pass a run of its own):", "",
+             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --counters",
+             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --counters",
+             "    python3 bench.py --summarize-counters gpurun_out/pmc_fetch gpurun_out/pmc_write", "",
+             f"Calibration: a plain device copy of {COPY_BYTES >> 20} MiB reads FETCH_SIZE = {f_copy:.0f} KiB and "
+             f"WRITE_SIZE = {w_copy:.0f} KiB, i.e. {f_scale:.3f} and {w_scale:.3f} counter bytes per true byte; "
+             "kernel counters are divided by these factors.", "",
+             "| kernel | workload | FETCH KiB | WRITE KiB | HBM read MB | HBM write MB | algorithmic MB | traffic / algorithmic |",
+             "|---|---|---|---|---|---|---|---|"]
+    for kind, r in res.items():
+        lines.append(f"| `{r['kernel']}` | {r['workload']} | {r['fetch_kib_per_dispatch']:.0f} | "
+                     f"{r['write_kib_per_dispatch']:.0f} | {r['hbm_read_bytes_per_launch'] / 1e6:.1f} | "
+                     f"{r['hbm_write_bytes_per_launch'] / 1e6:.1f} | {r['algorithmic_bytes_per_launch'] / 1e6:.1f} | "
+                     f"{r['hbm_bytes_per_launch'] / r['algorithmic_bytes_per_launch']:.2f} |")
+    with open(os.path.join(PROFILES, "hbm_traffic.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # ----------------------------------------------------------------------------- CPU oracle baseline
 
 def cpu_baseline(seconds: float):
@@ -209,7 +295,18 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--parts", default="all", help="comma list of stages to run (profiling aid)")
+    ap.add_argument("--counters", action="store_true",
+                    help="run only the dense prefill, the dense decode and a plain 256 MiB device copy "
+                         "(3 dispatches each) for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn the two counter runs into profiles/traffic_*.json and profiles/hbm_traffic.md")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
+    if args.counters:
+        args.parts = "prefill_dense,decode_dense"
 
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -255,6 +352,18 @@ def main():
     if want is not None:
         stages = {k: v for k, v in stages.items() if k in want}
     names = list(stages)
+
+    if args.counters:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        for n in ("prefill_dense", "decode_dense"):
+            for _ in range(3):
+                stages[n]["fn"]()
+        torch.cuda.synchronize()
+        print("counter workload done", flush=True)
+        return
 
     torch.cuda.synchronize()
     for _ in range(args.warmup):
