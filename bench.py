@@ -295,6 +295,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--parts", default="all", help="comma list of stages to run (profiling aid)")
+    ap.add_argument("--long", action="store_true",
+                    help="also time the long-context workloads (prefill S32768, decode B8 x 131072)")
     ap.add_argument("--counters", action="store_true",
                     help="run only the dense prefill, the dense decode and a plain 256 MiB device copy "
                          "(3 dispatches each) for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
@@ -349,6 +351,12 @@ def main():
     # 3. ragged + paged
     if wanted("varlen"):
         add_varlen(stages, gq, gi.c5_ragged(), up, i32, f32, dev)
+    if args.long:
+        long_stages = {}
+        add_prefill(long_stages, gq, gi.c4_prefill(), up, f32, dev)
+        add_decode(long_stages, gq, gi.c4_decode(), up, i32, f32, dev)
+        for k_, v_ in long_stages.items():
+            stages["long_" + k_] = v_
     if want is not None:
         stages = {k: v for k, v in stages.items() if k in want}
     names = list(stages)

@@ -26,10 +26,18 @@ def rng_for(cfg: int, tensor_id: int) -> np.random.Generator:
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
-    """fp32 array -> uint16 bf16 bit patterns, round to nearest even."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    bias = ((u >> 16) & 1) + 0x7FFF
-    return ((u + bias) >> 16).astype(np.uint16)
+    """fp32 array -> uint16 bf16 bit patterns, round to nearest even (finite inputs).
+
+    Works in place-sized uint32 chunks so that gigabyte tensors convert without
+    large temporaries (finite values never carry past bit 31)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).reshape(-1).view(np.uint32)
+    out = np.empty(u.shape, dtype=np.uint16)
+    step = 1 << 24
+    for i in range(0, u.size, step):
+        c = u[i:i + step]
+        r = c + (((c >> 16) & 1) + np.uint32(0x7FFF))
+        out[i:i + step] = (r >> 16).astype(np.uint16)
+    return out.reshape(np.shape(x))
 
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
