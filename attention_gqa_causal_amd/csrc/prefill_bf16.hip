@@ -27,10 +27,16 @@
 // accumulates P V for both (each V operand feeds two MFMAs).  The two
 // workgroups sharing a CU overlap each other's MFMA and VALU phases.  K/V
 // tiles are staged one tile ahead in double-buffered LDS, with one workgroup
-// barrier per tile.  The running max moves lazily (only when a tile max
-// exceeds it by more than 2^8), so the output is almost never rescaled.
-#include <type_traits>
-
+// barrier per tile.
+//
+// The softmax keeps a reference max per row but does not track the running
+// max tile by tile: the weights are exponentiated against the reference as it
+// stands, and the row sum that is accumulated anyway tells whether any weight
+// grew too large (past 2^32).  Only then, on a uniform rare branch, is the
+// tile recomputed against its true max and the output rescaled.  fp32 sums and
+// bf16 weights keep their relative precision at any magnitude, so nothing but
+// overflow needs guarding; with a sink the reference starts at the sink logit,
+// and without one the first visible tile sets it.
 #include "kernels.h"
 
 namespace gqa {
@@ -42,12 +48,13 @@ constexpr int NTHREADS = 64 * NWAVES;
 constexpr int NT_WG = 2 * NWAVES;  // N-tiles per workgroup
 constexpr int KS = 72;          // LDS row stride (elements) of K [key][d]: conflict-free 16-byte row reads
 constexpr int VS = 96;          // LDS row stride (elements) of V [key][d]: conflict-free transposing reads
-constexpr float kLazy = 8.f;    // log2 headroom before the reference max is moved
+constexpr float kRefit = 0x1p32f;  // a lane's per-tile weight sum past this moves the reference max
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -95,74 +102,82 @@ __device__ __forceinline__ void pv_tile(f32x16 (&o)[2][2], const __bf16* vs, con
   }
 }
 
-// Online-softmax step of one N-tile on one 64-key tile: optional mask, running
-// max with lazy update, exponentials, partial row sum of the bf16 weights,
-// bf16 packing into the P^T operand.  Lane holds keys
-// j0 + 32*mt + 8*(r/4) + 4*lg + r%4 of query row lr.  Returns alpha (1 when the
-// reference max did not move) and sets *up when it moved.
-template <bool MASKED>
-__device__ __forceinline__ float softmax_ntile(f32x16 (&s)[2], bf16x8 (&pb)[4], float& m, float& l, bool& up,
-                                               int j0, int p, int W, float c, int lg) {
-  if (MASKED) {
-    // visible iff (key - j0 - 4lg) is in (dl, dh]: compare against per-lane bounds so
-    // the per-register key offsets stay compile-time constants
-    const int dh = p - j0 - 4 * lg;
-    const int dl = W > 0 ? dh - W : -0x40000000;
+// Mask of one N-tile on one 64-key tile.  Lane holds keys
+// j0 + 32*mt + 8*(r/4) + 4*lg + r%4 of query row lr; the key is visible iff
+// (key - j0 - 4lg) lies in (dl, dh] (dl only counts with a window).  Each
+// 32-key half is classified with wave-uniform bounds first: wholly visible
+// halves are left alone, wholly hidden ones are cleared, and only a half that
+// the causal diagonal or the window edge crosses is compared element by element.
+__device__ __forceinline__ void mask_ntile(f32x16 (&s)[2], int j0, int plo, int phi, int W, int dh, int dl) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 2; ++mt) {
+    const int kb = j0 + 32 * mt;  // first key of this half (uniform)
+    const bool hidden = kb > phi || (W > 0 && kb + 31 <= plo - W);
+    if (hidden) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = 32 * mt + 8 * (r >> 2) + (r & 3);
-        if (off > dh || off <= dl) s[mt][r] = -INFINITY;
-      }
-  }
-  // tree max over the 32 scores of this lane, then across the lane pair (l, l^32)
-  float t[11];
+      for (int r = 0; r < 16; ++r) s[mt][r] = -INFINITY;
+      continue;
+    }
+    if (kb + 31 > plo) {  // causal diagonal crosses this half
 #pragma unroll
-  for (int q = 0; q < 10; ++q) {
-    const int a = 3 * q, b = a + 1, cc = a + 2;
-    t[q] = fmaxf(fmaxf(s[a >> 4][a & 15], s[b >> 4][b & 15]), s[cc >> 4][cc & 15]);
+      for (int r = 0; r < 16; ++r)
+        if (32 * mt + 8 * (r >> 2) + (r & 3) > dh) s[mt][r] = -INFINITY;
+    }
+    if (W > 0 && kb <= phi - W) {  // window edge crosses this half
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (32 * mt + 8 * (r >> 2) + (r & 3) <= dl) s[mt][r] = -INFINITY;
+    }
   }
-  t[10] = fmaxf(s[1][14], s[1][15]);
-  const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]);
-  const float u1 = fmaxf(fmaxf(t[3], t[4]), t[5]);
-  const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]);
-  const float u3 = fmaxf(t[9], t[10]);
-  float mx = fmaxf(fmaxf(u0, u1), fmaxf(u2, u3));
-  {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-  }
-  const float mt_ = mx * c;
-  up = mt_ > m + kLazy;
-  const float m_new = up ? mt_ : m;
-  const float alpha = up ? fast_exp2(m - m_new) : 1.f;
-  m = m_new;
+}
+
+// Exponentials of one N-tile against the reference max m (log2 units): the
+// bf16 P^T operand and this lane's partial row sum of the rounded weights.
+__device__ __forceinline__ float exp_ntile(const f32x16 (&s)[2], bf16x8 (&pb)[4], float m, float c) {
   float rs = 0.f;
   const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    bf16x8 tt;
+    u32x4 w;
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      bf16x2 pk;
-      pk[0] = (__bf16)fast_exp2(__builtin_fmaf(s[u >> 1][8 * (u & 1) + e], c, -m_new));
-      pk[1] = (__bf16)fast_exp2(__builtin_fmaf(s[u >> 1][8 * (u & 1) + e + 1], c, -m_new));
-      tt[e] = pk[0];
-      tt[e + 1] = pk[1];
+    for (int e = 0; e < 4; ++e) {
+      const f32x2 x = {fast_exp2(__builtin_fmaf(s[u >> 1][8 * (u & 1) + 2 * e], c, -m)),
+                       fast_exp2(__builtin_fmaf(s[u >> 1][8 * (u & 1) + 2 * e + 1], c, -m))};
+      const bf16x2 pk = __builtin_convertvector(x, bf16x2);
       rs = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, rs, false);
+      w[e] = __builtin_bit_cast(uint32_t, pk);
     }
-    pb[u] = tt;
+    pb[u] = __builtin_bit_cast(bf16x8, w);
   }
-  l = l * alpha + rs;
-  return alpha;
+  return rs;
 }
 
-__device__ __forceinline__ void rescale(f32x16 (&o)[2], float alpha, bool up) {
-  if (__builtin_amdgcn_ballot_w64(up)) {
+// Rare path: some lane's weights on this tile summed past kRefit, i.e. a score
+// rose far above the reference max (always so on the first visible tile when
+// there is no sink).  Recompute the tile's scores, move the reference to the
+// true running max, rescale the output and the sum, and redo the weights.
+__device__ __forceinline__ float refit_ntile(f32x16 (&s)[2], bf16x8 (&pb)[4], float& m, float& l, float& alpha,
+                                             const __bf16* ks, const bf16x8 (&qb)[4], int lr, int lg, float c, int j0,
+                                             int plo, int phi, int W, int dh, int dl) {
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) o[dt] *= alpha;
-  }
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + (32 * mt + lr) * KS + 16 * k + 8 * lg);
+      s[mt] = mfma32(ka, qb[k], k == 0 ? zero16() : s[mt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  mask_ntile(s, j0, plo, phi, W, dh, dl);
+  float mx = s[0][0];
+#pragma unroll
+  for (int r = 1; r < 32; ++r) mx = fmaxf(mx, s[r >> 4][r & 15]);
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+  mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  const float m_new = fmaxf(m, mx * c);
+  alpha = fast_exp2(m - m_new);
+  l *= alpha;
+  m = m_new;
+  return exp_ntile(s, pb, m, c);
 }
 
 template <int MODE, bool VARLEN>
@@ -172,7 +187,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (lets per-wave values live in SGPRs)
   const int lr = lane & 31;  // row of the 32-wide MFMA tile this lane serves
   const int lg = lane >> 5;  // which half of the K dimension / which 4-row group
 
@@ -299,20 +314,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
       *reinterpret_cast<u32x4*>(dst + (chunk >> 3) * stride + (chunk & 7) * 8) = reg[cc];
     }
   };
-  auto tile_masked = [&](int t) {
-    const int j0 = j_begin + BK * t;
-    bool m = false;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) m |= !((j0 + BK - 1 <= pos0[i]) && (W <= 0 || j0 > phi[i] - W));
-    return m;
-  };
+
   // lane's address offset for the transposing V reads (see pv_ntile)
   const int vofs = (4 * (lane >> 5) + ((lane & 15) >> 2)) * VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   // one 64-key tile; K/V of tile t are in buffer t % 2, tile t+1 is staged into the other
   int blk_next[2];  // block ids of tile t+1's rows
-  auto body = [&](auto mask_tag, int t) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  auto body = [&](int t) {
     const int buf = t & 1;
     const int j0 = j_begin + BK * t;
     const bool next = t + 1 < n_tiles;
@@ -322,12 +330,22 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
     fetch_blk(t + 2, blk_nn);
     f32x16 s0[2], s1[2];
     bf16x8 p0[4], p1[4];
-    bool up0, up1;
     qk_tile(s0, s1, Ks[buf], qb, lr, lg);
-    const float al0 = softmax_ntile<MASK>(s0, p0, m_run[0], l_run[0], up0, j0, pos0[0] + lr, W, c, lg);
-    const float al1 = softmax_ntile<MASK>(s1, p1, m_run[1], l_run[1], up1, j0, pos0[1] + lr, W, c, lg);
-    rescale(o[0], al0, up0);
-    rescale(o[1], al1, up1);
+    const int dh0 = pos0[0] + lr - j0 - 4 * lg, dh1 = pos0[1] + lr - j0 - 4 * lg;
+    const int dl0 = W > 0 ? dh0 - W : -0x40000000, dl1 = W > 0 ? dh1 - W : -0x40000000;
+    mask_ntile(s0, j0, pos0[0], phi[0], W, dh0, dl0);
+    mask_ntile(s1, j0, pos0[1], phi[1], W, dh1, dl1);
+    float rs0 = exp_ntile(s0, p0, m_run[0], c);
+    float rs1 = exp_ntile(s1, p1, m_run[1], c);
+    const bool f0 = __builtin_amdgcn_ballot_w64(rs0 > kRefit) != 0;
+    const bool f1 = __builtin_amdgcn_ballot_w64(rs1 > kRefit) != 0;
+    float al0 = 1.f, al1 = 1.f;
+    if (f0) rs0 = refit_ntile(s0, p0, m_run[0], l_run[0], al0, Ks[buf], qb[0], lr, lg, c, j0, pos0[0], phi[0], W, dh0, dl0);
+    if (f1) rs1 = refit_ntile(s1, p1, m_run[1], l_run[1], al1, Ks[buf], qb[1], lr, lg, c, j0, pos0[1], phi[1], W, dh1, dl1);
+    if (f0) { o[0][0] *= al0; o[0][1] *= al0; }
+    if (f1) { o[1][0] *= al1; o[1][1] *= al1; }
+    l_run[0] += rs0;
+    l_run[1] += rs1;
     pv_tile(o, Vs[buf], p0, p1, vofs);
     if (next) {
       store_rows(Ks[buf ^ 1], KS, kreg);
@@ -349,12 +367,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
       store_rows(Vs[0], VS, vr);
     }
     __syncthreads();
-    std::true_type MSK;
-    std::false_type PLN;
-    for (int t = 0; t < n_tiles; ++t) {
-      if (tile_masked(t)) body(MSK, t);
-      else body(PLN, t);
-    }
+    for (int t = 0; t < n_tiles; ++t) body(t);
   }
 
   // ---- epilogue: normalise, round to bf16, store; log-sum-exp
