@@ -15,19 +15,32 @@
 //
 // The scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 // A = rows of the K tile (keys) from LDS, B = Q^T held in registers.  In the
-// result a lane holds 16 keys of ONE query row, so the row max and the output
-// rescale are per lane (one lane^32 exchange for the max).  The output is also
+// result a lane holds 16 keys of ONE query row, so all softmax bookkeeping is
+// per lane (one lane^32 exchange when a max is needed).  The output is also
 // accumulated transposed, O^T += V^T P^T: P^T comes from the score registers as
 // they are (the contraction order over keys is free), and V^T from the V tile,
 // stored in LDS in its natural [key][d] layout and read with the transposing
-// LDS load ds_read_b64_tr_b16.
+// LDS load ds_read_b64_tr_b16.  Each K or V operand read from LDS feeds the
+// MFMAs of both of the wave's N-tiles.
 //
-// Per 64-key tile a wave computes the scores of both its N-tiles (each K
-// operand read from LDS feeds two MFMAs), runs the two softmax steps, then
-// accumulates P V for both (each V operand feeds two MFMAs).  The two
-// workgroups sharing a CU overlap each other's MFMA and VALU phases.  K/V
-// tiles are staged one tile ahead in double-buffered LDS, with one workgroup
-// barrier per tile.
+// Schedule.  A wave issues in order, and a vector instruction cannot issue
+// while the wave is held at an MFMA, so a wave that runs all its MFMAs and
+// then all its exponentials keeps only one unit busy; the other wave on the
+// SIMD does not fill the gap either, since the older wave has issue priority.
+// Each 64-key tile is therefore split into its two 32-key halves, which the
+// softmax below treats independently, and every phase pairs matrix work with
+// independent vector work in a pinned order (one MFMA pair, then about 26
+// vector instructions):
+//   (a) exponentials of half 0   with   scores of half 1
+//   (b) exponentials of half 1   with   P V over half 0
+//   (c) P V over half 1          with   scores of half 0 of the next tile
+// The row sums use fp32 adds: the bf16 dot instruction would halve their
+// count, but it occupies the matrix pipe and stalls the MFMAs beside it.
+//
+// K/V staging.  Tiles go from global memory straight into LDS with 16-byte
+// direct loads (no registers, no LDS store instructions), two tiles ahead,
+// into three LDS buffers: the tile being read, the next one, and the one
+// landing.  One barrier per tile, between (b) and (c), publishes the next tile.
 //
 // The softmax keeps a reference max per row but does not track the running
 // max tile by tile: the weights are exponentiated against the reference as it
@@ -37,6 +50,8 @@
 // bf16 weights keep their relative precision at any magnitude, so nothing but
 // overflow needs guarding; with a sink the reference starts at the sink logit,
 // and without one the first visible tile sets it.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace gqa {
@@ -46,13 +61,15 @@ constexpr int BK = 64;          // keys per tile
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int NT_WG = 2 * NWAVES;  // N-tiles per workgroup
-constexpr int KS = 72;          // LDS row stride (elements) of K [key][d]: conflict-free 16-byte row reads
-constexpr int VS = 96;          // LDS row stride (elements) of V [key][d]: conflict-free transposing reads
+constexpr int RS = 64;          // LDS row (elements) of a K or V tile: one 128-byte key row, no padding
+constexpr int NBUF = 3;         // K/V tiles resident in LDS: current, next, and the one being filled
+constexpr unsigned kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), leaving the other counters alone
 constexpr float kRefit = 0x1p32f;  // a lane's per-tile weight sum past this moves the reference max
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -67,123 +84,151 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// S^T for both N-tiles: keys 32*mt + (MFMA row) of the tile x 32 query rows
-__device__ __forceinline__ void qk_tile(f32x16 (&s0)[2], f32x16 (&s1)[2], const __bf16* ks, const bf16x8 (&qb)[2][4],
+// LDS tiles hold K and V in their natural [key][d] layout, one 128-byte row
+// per key, with the eight 16-byte chunks of row r stored in the order
+// c ^ (r & 7).  The swizzle spreads the rows that one read instruction touches
+// over all banks, and it lets a wave fill 8 whole rows with one 16-byte
+// global-to-LDS load per lane (lane i lands at byte 16i of the wave's slice, so
+// it fetches logical chunk (i & 7) ^ (i >> 3) of row i >> 3).
+// Element offset of logical 16-byte chunk cc of a row whose index is r (mod 8).
+__device__ __forceinline__ int kchunk(int cc, int r) { return ((cc ^ r) & 7) * 8; }
+
+// S^T of key half h (keys 32h .. 32h+31 of the tile, one per MFMA row) for
+// both N-tiles; each K operand read from LDS feeds two MFMAs.
+__device__ __forceinline__ void qk_half(f32x16& s0, f32x16& s1, const __bf16* ks, const bf16x8 (&qb)[2][4], int h,
                                         int lr, int lg) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + (32 * mt + lr) * KS + 16 * k + 8 * lg);
-      s0[mt] = mfma32(ka, qb[0][k], k == 0 ? zero16() : s0[mt]);
-      s1[mt] = mfma32(ka, qb[1][k], k == 0 ? zero16() : s1[mt]);
-    }
+    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + (32 * h + lr) * RS + kchunk(2 * k + lg, lr));
+    s0 = mfma32(ka, qb[0][k], k == 0 ? zero16() : s0);
+    s1 = mfma32(ka, qb[1][k], k == 0 ? zero16() : s1);
   }
 }
 
-// O^T += V^T P^T for one N-tile.  In 16-lane group c of the wave, lane j reads 4
-// consecutive d of key row (j/4); the transposing load hands lane i of the
-// group the 4 keys at d = dbase + i.  The key order of k-step u matches the
-// score registers: 16u + {4lg..4lg+3, 8+4lg..8+4lg+3}.
-__device__ __forceinline__ void pv_tile(f32x16 (&o)[2][2], const __bf16* vs, const bf16x8 (&p0)[4],
-                                        const bf16x8 (&p1)[4], int vofs) {
+// O^T += V^T P^T over key half h (k-steps u = 2h, 2h+1) for both N-tiles.  In
+// 16-lane group c of the wave, lane j reads 4 consecutive d of key row (j/4);
+// the transposing load hands lane i of the group the 4 keys at d = dbase + i.
+// The key order of k-step u matches the score registers:
+// 16u + {4lg..4lg+3, 8+4lg..8+4lg+3}.
+__device__ __forceinline__ bf16x8 v_operand(const __bf16* vs, int u, int dt, const int (&vofs)[2]) {
+  const __bf16* base = vs + vofs[dt] + 16 * u * RS;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * RS));
+  const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ void pv_half(f32x16 (&o)[2][2], const __bf16* vs, const bf16x8 (&p0)[2],
+                                        const bf16x8 (&p1)[2], int h, const int (&vofs)[2]) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int uu = 0; uu < 2; ++uu) {
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) {
-      const __bf16* base = vs + vofs + 16 * u * VS + 32 * dt;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * VS));
-      const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      const bf16x8 va = __builtin_bit_cast(bf16x8, w);
-      o[0][dt] = mfma32(va, p0[u], o[0][dt]);
-      o[1][dt] = mfma32(va, p1[u], o[1][dt]);
+      const bf16x8 va = v_operand(vs, 2 * h + uu, dt, vofs);
+      o[0][dt] = mfma32(va, p0[uu], o[0][dt]);
+      o[1][dt] = mfma32(va, p1[uu], o[1][dt]);
     }
   }
 }
 
-// Mask of one N-tile on one 64-key tile.  Lane holds keys
-// j0 + 32*mt + 8*(r/4) + 4*lg + r%4 of query row lr; the key is visible iff
-// (key - j0 - 4lg) lies in (dl, dh] (dl only counts with a window).  Each
-// 32-key half is classified with wave-uniform bounds first: wholly visible
-// halves are left alone, wholly hidden ones are cleared, and only a half that
-// the causal diagonal or the window edge crosses is compared element by element.
-__device__ __forceinline__ void mask_ntile(f32x16 (&s)[2], int j0, int plo, int phi, int W, int dh, int dl) {
+// Mask of one N-tile on key half h.  Lane holds keys
+// j0 + 32h + 8*(r/4) + 4*lg + r%4 of query row lr; the key is visible iff
+// (key - j0 - 4lg) lies in (dl, dh] (dl only counts with a window).  The half
+// is classified with wave-uniform bounds first: wholly visible is left alone,
+// wholly hidden is cleared, and only a half that the causal diagonal or the
+// window edge crosses is compared element by element.
+__device__ __forceinline__ void mask_half(f32x16& s, int h, int j0, int plo, int phi, int W, int dh, int dl) {
+  const int kb = j0 + 32 * h;  // first key of this half (uniform)
+  if (kb > phi || (W > 0 && kb + 31 <= plo - W)) {
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int kb = j0 + 32 * mt;  // first key of this half (uniform)
-    const bool hidden = kb > phi || (W > 0 && kb + 31 <= plo - W);
-    if (hidden) {
+    for (int r = 0; r < 16; ++r) s[r] = -INFINITY;
+    return;
+  }
+  if (kb + 31 > plo) {  // causal diagonal crosses this half
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[mt][r] = -INFINITY;
-      continue;
-    }
-    if (kb + 31 > plo) {  // causal diagonal crosses this half
+    for (int r = 0; r < 16; ++r)
+      if (32 * h + 8 * (r >> 2) + (r & 3) > dh) s[r] = -INFINITY;
+  }
+  if (W > 0 && kb <= phi - W) {  // window edge crosses this half
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (32 * mt + 8 * (r >> 2) + (r & 3) > dh) s[mt][r] = -INFINITY;
-    }
-    if (W > 0 && kb <= phi - W) {  // window edge crosses this half
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (32 * mt + 8 * (r >> 2) + (r & 3) <= dl) s[mt][r] = -INFINITY;
-    }
+    for (int r = 0; r < 16; ++r)
+      if (32 * h + 8 * (r >> 2) + (r & 3) <= dl) s[r] = -INFINITY;
   }
 }
 
-// Exponentials of one N-tile against the reference max m (log2 units): the
-// bf16 P^T operand and this lane's partial row sum of the rounded weights.
-__device__ __forceinline__ float exp_ntile(const f32x16 (&s)[2], bf16x8 (&pb)[4], float m, float c) {
-  float rs = 0.f;
-  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+// Exponentials of one N-tile's key half against the reference max m (log2
+// units): the two bf16 P^T operands of that half and this lane's partial row
+// sum of the weights.  The sum is taken with plain fp32 adds: the bf16 dot
+// instruction would do it in half the instructions, but it occupies the matrix
+// pipe and so stalls the MFMAs this work is meant to run beside.
+__device__ __forceinline__ float exp_half(const f32x16& s, bf16x8 (&pb)[2], float m, float c) {
+  float ra = 0.f, rb = 0.f;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int uu = 0; uu < 2; ++uu) {
     u32x4 w;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const f32x2 x = {fast_exp2(__builtin_fmaf(s[u >> 1][8 * (u & 1) + 2 * e], c, -m)),
-                       fast_exp2(__builtin_fmaf(s[u >> 1][8 * (u & 1) + 2 * e + 1], c, -m))};
-      const bf16x2 pk = __builtin_convertvector(x, bf16x2);
-      rs = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, rs, false);
-      w[e] = __builtin_bit_cast(uint32_t, pk);
+      const f32x2 x = {fast_exp2(__builtin_fmaf(s[8 * uu + 2 * e], c, -m)),
+                       fast_exp2(__builtin_fmaf(s[8 * uu + 2 * e + 1], c, -m))};
+      ra += x[0];
+      rb += x[1];
+      w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
     }
-    pb[u] = __builtin_bit_cast(bf16x8, w);
+    pb[uu] = __builtin_bit_cast(bf16x8, w);
   }
-  return rs;
+  return ra + rb;
 }
 
-// Rare path: some lane's weights on this tile summed past kRefit, i.e. a score
-// rose far above the reference max (always so on the first visible tile when
-// there is no sink).  Recompute the tile's scores, move the reference to the
-// true running max, rescale the output and the sum, and redo the weights.
-__device__ __forceinline__ float refit_ntile(f32x16 (&s)[2], bf16x8 (&pb)[4], float& m, float& l, float& alpha,
-                                             const __bf16* ks, const bf16x8 (&qb)[4], int lr, int lg, float c, int j0,
-                                             int plo, int phi, int W, int dh, int dl) {
+// One eighth of a tile's exponentials for one N-tile: the 8 scores of
+// k-step group uu of a key half (one bf16 P^T operand) and their partial sum.
+__device__ __forceinline__ float exp_chunk(const f32x16& s, bf16x8& pb, int uu, float m, float c) {
+  float ra = 0.f, rb = 0.f;
+  u32x4 w;
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
+  for (int e = 0; e < 4; ++e) {
+    const f32x2 x = {fast_exp2(__builtin_fmaf(s[8 * uu + 2 * e], c, -m)),
+                     fast_exp2(__builtin_fmaf(s[8 * uu + 2 * e + 1], c, -m))};
+    ra += x[0];
+    rb += x[1];
+    w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+  }
+  pb = __builtin_bit_cast(bf16x8, w);
+  return ra + rb;
+}
+
+__device__ __forceinline__ void fence_schedule() { __builtin_amdgcn_sched_barrier(0); }
+
+// Rare path: some lane's weights on this key half summed past kRefit, i.e. a
+// score rose far above the reference max (always so on the first visible half
+// when there is no sink).  Recompute the half's scores, move the reference to
+// the true running max, and redo the weights; the caller rescales the output
+// by the returned alpha (the row sum is rescaled here).
+__device__ __forceinline__ float refit_half(f32x16& s, bf16x8 (&pb)[2], float& m, float& l, float& alpha,
+                                            const __bf16* ks, const bf16x8 (&qb)[4], int h, int lr, int lg, float c,
+                                            int j0, int plo, int phi, int W, int dh, int dl) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + (32 * mt + lr) * KS + 16 * k + 8 * lg);
-      s[mt] = mfma32(ka, qb[k], k == 0 ? zero16() : s[mt]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  mask_ntile(s, j0, plo, phi, W, dh, dl);
-  float mx = s[0][0];
+  for (int k = 0; k < 4; ++k) {
+    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + (32 * h + lr) * RS + kchunk(2 * k + lg, lr));
+    s = mfma32(ka, qb[k], k == 0 ? zero16() : s);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  mask_half(s, h, j0, plo, phi, W, dh, dl);
+  float mx = s[0];
 #pragma unroll
-  for (int r = 1; r < 32; ++r) mx = fmaxf(mx, s[r >> 4][r & 15]);
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
   mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   const float m_new = fmaxf(m, mx * c);
   alpha = fast_exp2(m - m_new);
   l *= alpha;
   m = m_new;
-  return exp_ntile(s, pb, m, c);
+  return exp_half(s, pb, m, c);
 }
 
 template <int MODE, bool VARLEN>
 __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BK * KS];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BK * VS];
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[NBUF][BK * RS];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[NBUF][BK * RS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -272,102 +317,180 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
     for (int dt = 0; dt < 2; ++dt) o[i][dt] = zero16();
   }
 
-  // ---- global -> register -> LDS staging: 512 16-byte chunks per K or V tile, 2 of each per thread
+  // ---- global -> LDS staging with 16-byte direct loads: wave w fills rows
+  // 16w .. 16w+15 of a tile, 8 rows per instruction.  With a paged cache the
+  // block ids of the rows are fetched one tile ahead of the loads.  Rows past
+  // the key range repeat row hi (they are masked, and the loads stay in bounds).
   const int64_t kv_stride = (int64_t)a.Hkv * kHeadDim;
   const __bf16* kbase = a.k + g * kHeadDim;
   const __bf16* vbase = a.v + g * kHeadDim;
-  // This thread moves rows r0 and r0 + 32 of every tile (16 bytes at d = 8*(tid%8)).
-  // With a paged cache their block ids are fetched one tile ahead, so no K/V
-  // load waits on the block table.  Rows past the key range repeat row hi (they
-  // are masked, and the loads stay in bounds).
-  const int r0 = tid >> 3;
+  const int dma_chunk = ((lane & 7) ^ (lane >> 3)) * 8;  // logical chunk this lane's LDS slot holds
   auto fetch_blk = [&](int t, int (&blk)[2]) {
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      blk[cc] = 0;
+    for (int i = 0; i < 2; ++i) {
+      blk[i] = 0;
       if (MODE == KV_PAGED) {
-        const int j = min(j_begin + BK * t + r0 + 32 * cc, hi);
-        blk[cc] = a.seq.block_table[(int64_t)b * a.seq.max_blocks + (j >> a.seq.log2_block)];
+        const int j = min(j_begin + BK * t + 16 * wave + 8 * i + (lane >> 3), hi);
+        blk[i] = a.seq.block_table[(int64_t)b * a.seq.max_blocks + (j >> a.seq.log2_block)];
       }
     }
   };
-  auto load_kv = [&](int t, const int (&blk)[2], u32x4 (&kreg)[2], u32x4 (&vreg)[2]) {
+  auto dma_tile = [&](int t, const int (&blk)[2], int buf) {
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const int j = min(j_begin + BK * t + r0 + 32 * cc, hi);
+    for (int i = 0; i < 2; ++i) {
+      const int j = min(j_begin + BK * t + 16 * wave + 8 * i + (lane >> 3), hi);
       int64_t row;
       if (MODE == KV_PAGED) {
-        const int bb = min(max(blk[cc], 0), a.seq.num_blocks - 1);
+        const int bb = min(max(blk[i], 0), a.seq.num_blocks - 1);
         row = ((int64_t)bb << a.seq.log2_block) + (j & ((1 << a.seq.log2_block) - 1));
       } else {
         row = kv_row<MODE>(a.seq, sv, j);
       }
-      const int64_t off = row * kv_stride + (tid & 7) * 8;
-      kreg[cc] = *reinterpret_cast<const u32x4*>(kbase + off);
-      vreg[cc] = *reinterpret_cast<const u32x4*>(vbase + off);
+      const int64_t off = row * kv_stride + dma_chunk;
+      const int lofs = (16 * wave + 8 * i) * RS;  // wave-uniform slice of 8 rows
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + off), (lds_void*)(&Ks[buf][lofs]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + off), (lds_void*)(&Vs[buf][lofs]), 16, 0, 0);
     }
   };
-  auto store_rows = [&](__bf16* dst, int stride, const u32x4 (&reg)[2]) {
+
+
+  // Per-lane element offsets of the transposing V reads (see pv_half): key
+  // row rk = 4*(lane/32) + (lane%16)/4 of each 8-row group, 4 consecutive d
+  // from d = 32*dt + 16*((lane/16)%2) + 4*(lane%4).
+  int vofs[2];
+  {
+    const int rk = 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int c0 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const int chunk = tid + cc * NTHREADS;
-      *reinterpret_cast<u32x4*>(dst + (chunk >> 3) * stride + (chunk & 7) * 8) = reg[cc];
-    }
-  };
+    for (int dt = 0; dt < 2; ++dt) vofs[dt] = rk * RS + kchunk(4 * dt + c0, rk) + 4 * (lane & 1);
+  }
 
-  // lane's address offset for the transposing V reads (see pv_ntile)
-  const int vofs = (4 * (lane >> 5) + ((lane & 15) >> 2)) * VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-  // one 64-key tile; K/V of tile t are in buffer t % 2, tile t+1 is staged into the other
-  int blk_next[2];  // block ids of tile t+1's rows
-  auto body = [&](int t) {
-    const int buf = t & 1;
-    const int j0 = j_begin + BK * t;
-    const bool next = t + 1 < n_tiles;
-    u32x4 kreg[2], vreg[2];
-    if (next) load_kv(t + 1, blk_next, kreg, vreg);
-    int blk_nn[2];
-    fetch_blk(t + 2, blk_nn);
-    f32x16 s0[2], s1[2];
-    bf16x8 p0[4], p1[4];
-    qk_tile(s0, s1, Ks[buf], qb, lr, lg);
-    const int dh0 = pos0[0] + lr - j0 - 4 * lg, dh1 = pos0[1] + lr - j0 - 4 * lg;
-    const int dl0 = W > 0 ? dh0 - W : -0x40000000, dl1 = W > 0 ? dh1 - W : -0x40000000;
-    mask_ntile(s0, j0, pos0[0], phi[0], W, dh0, dl0);
-    mask_ntile(s1, j0, pos0[1], phi[1], W, dh1, dl1);
-    float rs0 = exp_ntile(s0, p0, m_run[0], c);
-    float rs1 = exp_ntile(s1, p1, m_run[1], c);
-    const bool f0 = __builtin_amdgcn_ballot_w64(rs0 > kRefit) != 0;
-    const bool f1 = __builtin_amdgcn_ballot_w64(rs1 > kRefit) != 0;
-    float al0 = 1.f, al1 = 1.f;
-    if (f0) rs0 = refit_ntile(s0, p0, m_run[0], l_run[0], al0, Ks[buf], qb[0], lr, lg, c, j0, pos0[0], phi[0], W, dh0, dl0);
-    if (f1) rs1 = refit_ntile(s1, p1, m_run[1], l_run[1], al1, Ks[buf], qb[1], lr, lg, c, j0, pos0[1], phi[1], W, dh1, dl1);
-    if (f0) { o[0][0] *= al0; o[0][1] *= al0; }
-    if (f1) { o[1][0] *= al1; o[1][1] *= al1; }
-    l_run[0] += rs0;
-    l_run[1] += rs1;
-    pv_tile(o, Vs[buf], p0, p1, vofs);
-    if (next) {
-      store_rows(Ks[buf ^ 1], KS, kreg);
-      store_rows(Vs[buf ^ 1], VS, vreg);
-    }
-    blk_next[0] = blk_nn[0];
-    blk_next[1] = blk_nn[1];
-    __syncthreads();
-  };
-
+  // Tile t runs in three phases, each pairing vector work with independent
+  // matrix work so that both units stay busy within the wave:
+  //   (a) weights of key half 0          | scores of key half 1
+  //   (b) weights of key half 1          | P V over key half 0
+  //   -- wait for tile t+1's loads, barrier: tile t+1 is in LDS --
+  //   (c) P V over key half 1            | scores of key half 0 of tile t+1
+  //       and the loads of tile t+2 are issued
+  // Three LDS buffers: tile t is read until (c) of tile t, tile t+1 from (c)
+  // of tile t on, and tile t+2 lands in the buffer that tile t-1 left, which
+  // every wave finished reading before the barrier of tile t.
+  f32x16 sA[2], sB[2];  // scores of key halves 0 and 1, per N-tile
+  int blk_next[2];      // block ids of the next tile to load
   if (n_tiles > 0) {
     {
       int blk0[2];
-      u32x4 kr[2], vr[2];
       fetch_blk(0, blk0);
-      load_kv(0, blk0, kr, vr);
-      fetch_blk(1, blk_next);
-      store_rows(Ks[0], KS, kr);
-      store_rows(Vs[0], VS, vr);
+      dma_tile(0, blk0, 0);
+      fetch_blk(1, blk0);
+      if (n_tiles > 1) dma_tile(1, blk0, 1);
+      fetch_blk(2, blk_next);
     }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    for (int t = 0; t < n_tiles; ++t) body(t);
+    qk_half(sA[0], sA[1], Ks[0], qb, 0, lr, lg);
+    int cur = 0;
+    auto body = [&](auto mask_tag, int t) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
+      const int j0 = j_begin + BK * t;
+      const bool has_next = t + 1 < n_tiles;
+      const int dh0 = pos0[0] + lr - j0 - 4 * lg, dh1 = pos0[1] + lr - j0 - 4 * lg;
+      const int dl0 = W > 0 ? dh0 - W : -0x40000000, dl1 = W > 0 ? dh1 - W : -0x40000000;
+      bf16x8 pA0[2], pA1[2], pB0[2], pB1[2];
+      // (a): the four k-steps of the half-1 scores, each followed by a quarter
+      // of the half-0 exponentials (the order is pinned so that every MFMA
+      // pair runs while the vector work after it issues)
+      if (MASK) {
+        mask_half(sA[0], 0, j0, pos0[0], phi[0], W, dh0, dl0);
+        mask_half(sA[1], 0, j0, pos0[1], phi[1], W, dh1, dl1);
+      }
+      float r0 = 0.f, r1 = 0.f;
+      {
+        bf16x8 ka[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          ka[k] = *reinterpret_cast<const bf16x8*>(Ks[cur] + (32 + lr) * RS + kchunk(2 * k + lg, lr));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          fence_schedule();
+          sB[0] = mfma32(ka[k], qb[0][k], k == 0 ? zero16() : sB[0]);
+          sB[1] = mfma32(ka[k], qb[1][k], k == 0 ? zero16() : sB[1]);
+          fence_schedule();
+          if (k < 2) r0 += exp_chunk(sA[0], pA0[k], k, m_run[0], c);
+          else r1 += exp_chunk(sA[1], pA1[k - 2], k - 2, m_run[1], c);
+        }
+        fence_schedule();
+      }
+      {
+        const bool f0 = __builtin_amdgcn_ballot_w64(r0 > kRefit) != 0;
+        const bool f1 = __builtin_amdgcn_ballot_w64(r1 > kRefit) != 0;
+        float al0 = 1.f, al1 = 1.f;
+        if (f0) r0 = refit_half(sA[0], pA0, m_run[0], l_run[0], al0, Ks[cur], qb[0], 0, lr, lg, c, j0, pos0[0], phi[0], W, dh0, dl0);
+        if (f1) r1 = refit_half(sA[1], pA1, m_run[1], l_run[1], al1, Ks[cur], qb[1], 0, lr, lg, c, j0, pos0[1], phi[1], W, dh1, dl1);
+        if (f0) { o[0][0] *= al0; o[0][1] *= al0; }
+        if (f1) { o[1][0] *= al1; o[1][1] *= al1; }
+      }
+      l_run[0] += r0;
+      l_run[1] += r1;
+      // (b): P V over key half 0 in four steps, each followed by a quarter of
+      // the half-1 exponentials
+      if (MASK) {
+        mask_half(sB[0], 1, j0, pos0[0], phi[0], W, dh0, dl0);
+        mask_half(sB[1], 1, j0, pos0[1], phi[1], W, dh1, dl1);
+      }
+      r0 = 0.f;
+      r1 = 0.f;
+      {
+        bf16x8 va[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) va[i] = v_operand(Vs[cur], i >> 1, i & 1, vofs);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int uu = i >> 1, dt = i & 1;
+          fence_schedule();
+          o[0][dt] = mfma32(va[i], pA0[uu], o[0][dt]);
+          o[1][dt] = mfma32(va[i], pA1[uu], o[1][dt]);
+          fence_schedule();
+          if (i < 2) r0 += exp_chunk(sB[0], pB0[i], i, m_run[0], c);
+          else r1 += exp_chunk(sB[1], pB1[i - 2], i - 2, m_run[1], c);
+        }
+        fence_schedule();
+      }
+      {
+        const bool f0 = __builtin_amdgcn_ballot_w64(r0 > kRefit) != 0;
+        const bool f1 = __builtin_amdgcn_ballot_w64(r1 > kRefit) != 0;
+        float al0 = 1.f, al1 = 1.f;
+        if (f0) r0 = refit_half(sB[0], pB0, m_run[0], l_run[0], al0, Ks[cur], qb[0], 1, lr, lg, c, j0, pos0[0], phi[0], W, dh0, dl0);
+        if (f1) r1 = refit_half(sB[1], pB1, m_run[1], l_run[1], al1, Ks[cur], qb[1], 1, lr, lg, c, j0, pos0[1], phi[1], W, dh1, dl1);
+        if (f0) { o[0][0] *= al0; o[0][1] *= al0; }
+        if (f1) { o[1][0] *= al1; o[1][1] *= al1; }
+      }
+      l_run[0] += r0;
+      l_run[1] += r1;
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's loads of tile t+1 have landed
+      __syncthreads();
+      // (c)
+      if (t + 2 < n_tiles) dma_tile(t + 2, blk_next, nxt == NBUF - 1 ? 0 : nxt + 1);
+      fetch_blk(t + 3, blk_next);
+      pv_half(o, Vs[cur], pB0, pB1, 1, vofs);
+      if (has_next) qk_half(sA[0], sA[1], Ks[nxt], qb, 0, lr, lg);
+      cur = nxt;
+    };
+    // The tiles that need no mask for either of this wave's N-tiles form one
+    // run [pb, pe): past the window edge of the last row and before the
+    // causal diagonal of the first row.  Three loops, one body each.
+    const int p_first = min(pos0[0], pos0[1]);
+    const int p_last = max(phi[0], phi[1]);
+    const int t_lo = W > 0 ? max(0, (p_last - W - j_begin + BK) / BK) : 0;  // first t with j0 > p_last - W
+    const int t_hi = p_first - j_begin - (BK - 1) >= 0 ? (p_first - j_begin - (BK - 1)) / BK : -1;  // last t with j0 + 63 <= p_first
+    const int pb = min(t_lo, n_tiles);
+    const int pe = max(pb, min(t_hi + 1, n_tiles));
+    std::true_type MSK;
+    std::false_type PLN;
+    for (int t = 0; t < pb; ++t) body(MSK, t);
+    for (int t = pb; t < pe; ++t) body(PLN, t);
+    for (int t = pe; t < n_tiles; ++t) body(MSK, t);
   }
 
   // ---- epilogue: normalise, round to bf16, store; log-sum-exp
