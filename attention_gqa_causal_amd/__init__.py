@@ -9,6 +9,9 @@ Functions (names follow the C ABI in ``include/gqa_attn.h``):
 * ``attn_prefill(q, k, v, sinks, window=0, scale=None)``
 * ``attn_decode(q, kv_cache, seqlens, sinks, window=0, scale=None)``
 * ``attn_varlen_paged(q, kv_cache, block_table, cu_seqlens_q, seqlens_k, sinks, ...)``
+* ``kv_ring_append(k_new, v_new, kv_ring, seqlens, cu_seqlens_q=None)`` and
+  ``attn_decode_ring(q, kv_ring, seqlens, sinks, scale=None)``: the W-slot ring
+  cache of sliding-window layers (position p in slot p % W)
 
 The computation is causal grouped-query attention with a learned per-head sink
 logit and an optional sliding window (0 = dense), as described on the pages
@@ -27,6 +30,8 @@ __all__ = [
     "attn_prefill",
     "attn_decode",
     "attn_varlen_paged",
+    "kv_ring_append",
+    "attn_decode_ring",
     "decode_workspace_size",
     "varlen_workspace_size",
     "lib",
@@ -72,6 +77,9 @@ _SIGNATURES = {
     "gqa_attn_varlen_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "gqa_attn_varlen_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _P, _P, _P,
                                    _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "gqa_kv_ring_append": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "gqa_attn_decode_ring_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "gqa_attn_decode_ring": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
 }
 
 
@@ -270,4 +278,62 @@ def attn_varlen_paged(q, kv_cache, block_table, cu_seqlens_q, seqlens_k, sinks=N
                                        _ptr(sinks), _ptr(out), _ptr(lse), B, Tq, int(max_q_len), int(max_kv_len),
                                        Hq, Hkv, D, int(window), _scale(scale), dt,
                                        _ptr(workspace), ws_have, _stream(dev)))
+    return (out, lse) if return_lse else out
+
+
+def kv_ring_append(k_new, v_new, kv_ring, seqlens, cu_seqlens_q=None):
+    """Write new tokens' K/V rows into the W-slot rings of a sliding-window layer (in place).
+
+    kv_ring = (k_ring, v_ring) each [B, W, Hkv, 64]; k_new/v_new [T, Hkv, 64] of the
+    same dtype.  Without cu_seqlens_q, T == B and row b is sequence b's newest token
+    (position seqlens[b] - 1); with cu_seqlens_q [B+1] int32 the rows of sequence b
+    are its newest q_len positions.  seqlens [B] int32 counts the new rows.
+    """
+    kr, vr = _split_cache(kv_ring)
+    dev = kr.device
+    dt = _dtype_code(kr)
+    _check_tensor(kr, "k_ring", kr.dtype, dev, 4)
+    _check_tensor(vr, "v_ring", kr.dtype, dev, 4)
+    _need(vr.shape == kr.shape, "k_ring and v_ring must have the same shape")
+    B, W, Hkv, D = kr.shape
+    _check_tensor(k_new, "k_new", kr.dtype, dev, 3)
+    _check_tensor(v_new, "v_new", kr.dtype, dev, 3)
+    _need(v_new.shape == k_new.shape and k_new.shape[1:] == (Hkv, D), "k_new/v_new must be [T, Hkv, D]")
+    T = k_new.shape[0]
+    _check_tensor(seqlens, "seqlens", torch.int32, dev, 1)
+    _need(seqlens.shape[0] == B, "seqlens must have B entries")
+    if cu_seqlens_q is not None:
+        _check_tensor(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev, 1)
+        _need(cu_seqlens_q.shape[0] == B + 1, "cu_seqlens_q must have B+1 entries")
+    _check(lib().gqa_kv_ring_append(_ptr(k_new), _ptr(v_new), _ptr(cu_seqlens_q), _ptr(seqlens), _ptr(kr), _ptr(vr),
+                                    B, T, W, Hkv, D, dt, _stream(dev)))
+
+
+def attn_decode_ring(q, kv_ring, seqlens, sinks=None, scale=None, return_lse: bool = False, workspace=None):
+    """Decode on a sliding-window layer against its ring cache.
+
+    q [B, Hq, 64]; kv_ring = (k_ring, v_ring) each [B, W, Hkv, 64] holding the last
+    min(seqlens[b], W) positions (slot p % W); seqlens [B] int32 counts the new token.
+    The window is the ring size W.  Returns out [B, Hq, 64] (and lse [B, Hq]).
+    """
+    dev = q.device
+    _check_tensor(q, "q", q.dtype, dev, 3)
+    dt = _dtype_code(q)
+    B, Hq, D = q.shape
+    kr, vr = _split_cache(kv_ring)
+    _check_tensor(kr, "k_ring", q.dtype, dev, 4)
+    _check_tensor(vr, "v_ring", q.dtype, dev, 4)
+    _need(kr.shape[0] == B and kr.shape[3] == D and vr.shape == kr.shape, "rings must be [B, W, Hkv, D]")
+    W, Hkv = kr.shape[1], kr.shape[2]
+    _check_tensor(seqlens, "seqlens", torch.int32, dev, 1)
+    _need(seqlens.shape[0] == B, "seqlens must have B entries")
+    sinks = _sinks_arg(sinks, Hq, dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None
+    ws_bytes = int(lib().gqa_attn_decode_ring_workspace_size(B, W, Hq, Hkv, D, dt))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().gqa_attn_decode_ring(_ptr(q), _ptr(kr), _ptr(vr), _ptr(seqlens), _ptr(sinks), _ptr(out), _ptr(lse),
+                                      B, W, Hq, Hkv, D, _scale(scale), dt, _ptr(workspace), ws_have, _stream(dev)))
     return (out, lse) if return_lse else out

@@ -80,6 +80,7 @@ float scale_log2_of(float scale, int D) {
 struct SplitPlan {
   int n_splits;
   int split_len;
+  int solo;  // one unit per wave (short key ranges, many units)
 };
 
 // Split of the decode key range: enough workgroups to keep about 16 per CU in
@@ -89,8 +90,15 @@ SplitPlan plan_splits(int B, int Hkv, int G, int Lmax, int window) {
   const int eff = window > 0 ? (window < Lmax ? window : Lmax) : Lmax;
   const int n_hc = (G + 15) / 16;
   const long units = (long)B * Hkv * n_hc;
-  SplitPlan p{1, 64};
+  SplitPlan p{1, 64, 0};
   if (eff <= 0 || units <= 0) return p;
+  // Short ranges over many units: one wave per unit fills the chip by itself
+  // and skips the cross-wave merge (at most 8 tiles of 64 keys per wave).
+  if (eff <= 512 && units >= 8L * num_cus() && env_int("GQA_DECODE_SOLO", 1) != 0) {
+    p.solo = 1;
+    p.split_len = (eff + 63) & ~63;
+    return p;
+  }
   const long target = 16L * num_cus();
   long want = (target + units - 1) / units;
   const long max_by_len = eff / 1024;
@@ -115,7 +123,7 @@ size_t decode_ws_bytes(const SplitPlan& p, int B, int Hq) {
 
 extern "C" {
 
-int gqa_attn_version(void) { return 100; }
+int gqa_attn_version(void) { return 200; }
 
 const char* gqa_attn_status_string(int status) {
   switch (status) {
@@ -221,6 +229,7 @@ int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, con
   a.ws_acc = need ? (float*)workspace + (size_t)B * Hq * p.n_splits * 2 : nullptr;
   a.varlen_q = 0;
   a.lse_sb = Hq; a.lse_sh = 1; a.lse_row0 = 0;
+  a.solo = p.solo;
   if ((long long)B * Hkv * a.n_hc * a.n_splits > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
   hipError_t e = launch_decode_bf16(a, KV_BATCHED, st);
   return e == hipSuccess ? ok() : hip_fail(e, "decode bf16 launch");
@@ -316,9 +325,47 @@ int gqa_attn_varlen_paged(const void* q, const void* k_cache, const void* v_cach
   a.ws_acc = need ? (float*)workspace + (size_t)B * Hq * p.n_splits * 2 : nullptr;
   a.varlen_q = 1;
   a.lse_sb = 0; a.lse_sh = Tq; a.lse_row0 = 1;
+  a.solo = p.solo;
   if ((long long)B * Hkv * a.n_hc * a.n_splits > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
   hipError_t e = launch_decode_bf16(a, mode, st);
   return e == hipSuccess ? ok() : hip_fail(e, "varlen decode launch");
+}
+
+int gqa_kv_ring_append(const void* k_new, const void* v_new, const int32_t* cu_seqlens_q, const int32_t* seqlens,
+                       void* k_ring, void* v_ring, int B, int T, int W, int Hkv, int D, int dtype, void* stream) {
+  if (dtype != GQA_BF16 && dtype != GQA_FP32) return fail(GQA_ERR_UNSUPPORTED, "dtype %d is not GQA_BF16 or GQA_FP32", dtype);
+  if (D != kHeadDim) return fail(GQA_ERR_UNSUPPORTED, "head_dim %d is not supported (only 64)", D);
+  if (B < 0 || T < 0 || Hkv <= 0) return fail(GQA_ERR_INVALID_ARG, "bad size (B=%d, T=%d, Hkv=%d)", B, T, Hkv);
+  if (W <= 0) return fail(GQA_ERR_INVALID_ARG, "ring size W=%d must be >= 1", W);
+  if (!cu_seqlens_q && T != B)
+    return fail(GQA_ERR_INVALID_ARG, "without cu_seqlens_q there is one new row per sequence (T=%d, B=%d)", T, B);
+  if (B == 0 || T == 0) return ok();
+  if (!k_new || !v_new || !k_ring || !v_ring || !seqlens)
+    return fail(GQA_ERR_INVALID_ARG, "k_new, v_new, k_ring, v_ring and seqlens must be non-NULL");
+  RingAppendArgs a{};
+  a.k_new = (const char*)k_new; a.v_new = (const char*)v_new;
+  a.k_ring = (char*)k_ring; a.v_ring = (char*)v_ring;
+  a.cu_seqlens_q = cu_seqlens_q; a.seqlens = seqlens;
+  a.T = T; a.B = B; a.W = W;
+  a.row_bytes = Hkv * D * (dtype == GQA_BF16 ? 2 : 4);
+  hipError_t e = launch_ring_append(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "ring append launch");
+}
+
+size_t gqa_attn_decode_ring_workspace_size(int B, int W, int Hq, int Hkv, int D, int dtype) {
+  return gqa_attn_decode_workspace_size(B, W, Hq, Hkv, D, 0, dtype);
+}
+
+int gqa_attn_decode_ring(const void* q, const void* k_ring, const void* v_ring, const int32_t* seqlens,
+                         const float* sinks, void* out, float* lse, int B, int W, int Hq, int Hkv, int D,
+                         float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (W <= 0) return fail(GQA_ERR_INVALID_ARG, "ring size W=%d must be >= 1", W);
+  // The ring holds exactly the positions of the window ending at the query:
+  // min(seqlens[b], W) slots, all visible.  Key order does not enter the
+  // result, so this is dense attention over the valid slots of a W-slot cache
+  // (the kernels clamp each length to W).
+  return gqa_attn_decode(q, k_ring, v_ring, seqlens, sinks, out, lse, B, W, Hq, Hkv, D, 0, scale, dtype,
+                         workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -14,6 +14,11 @@
 // writes a partial (max, sum, unnormalised output) and a combine kernel merges
 // the splits.
 //
+// Short key ranges with many (sequence, KV head) units (window or ring layers
+// at large batch) take the "solo" form instead: each wave owns a whole unit,
+// walks its tiles in order and finishes it itself, with no split and no
+// cross-wave merge.
+//
 // Each wave streams whole 128-byte K and V rows of its key tiles with
 // non-temporal loads (the access pattern that reaches the highest HBM rate),
 // stages them in its own LDS slice, and computes S^T = K Q^T on
@@ -43,7 +48,7 @@ __device__ __forceinline__ u32x4 load_stream(const __bf16* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-template <int MODE>
+template <int MODE, bool SOLO>
 __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a) {
   // per wave: K tile then V tile; after the key loop the same memory holds the
   // 4-wave merge buffers
@@ -56,10 +61,11 @@ __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a)
   const int lq = lane >> 4;  // lane quarter
 
   // blockIdx -> (split, head chunk, KV head, sequence); splits of one
-  // (sequence, KV head) are consecutive
-  int x = blockIdx.x;
-  const int split = x % a.n_splits;
-  x /= a.n_splits;
+  // (sequence, KV head) are consecutive.  Solo: one unit per wave, one split.
+  int x = SOLO ? (int)blockIdx.x * 4 + wave : (int)blockIdx.x;
+  if (SOLO && x >= a.B * a.Hkv * a.n_hc) return;  // wave-uniform; the solo form has no workgroup barrier
+  const int split = SOLO ? 0 : x % a.n_splits;
+  if (!SOLO) x /= a.n_splits;
   const int hc = x % a.n_hc;
   x /= a.n_hc;
   const int g = x % a.Hkv;
@@ -132,13 +138,14 @@ __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a)
   // transposing V reads (see below): lane's row/column offset within the V tile
   const int vofs = (4 * lq + ((lane & 15) >> 2)) * VSD + 4 * (lane & 3);
 
-  int j0 = s_lo + wave * DT;
+  constexpr int STEP = SOLO ? DT : 4 * DT;  // a wave's tiles: all of them, or every 4th
+  int j0 = s_lo + (SOLO ? 0 : wave * DT);
   if (j0 < s_hi) {
     fetch_blk(j0);
     load(j0);
-    fetch_blk(j0 + 4 * DT);
+    fetch_blk(j0 + STEP);
   }
-  for (; j0 < s_hi; j0 += 4 * DT) {
+  for (; j0 < s_hi; j0 += STEP) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int key = 8 * i + (lane >> 3);
@@ -146,10 +153,10 @@ __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a)
       *reinterpret_cast<u32x4*>(Vw + key * VSD + 8 * (lane & 7)) = vreg[i];
     }
     wave_lds_sync();  // the tile is visible to every lane of the wave
-    const int jn = j0 + 4 * DT;
+    const int jn = j0 + STEP;
     if (jn < s_hi) {
       load(jn);  // next tile in flight during this one's math
-      fetch_blk(jn + 4 * DT);
+      fetch_blk(jn + STEP);
     }
 
     // S^T: 4 blocks of 16 keys x 16 heads; A operand = K rows 16*kb + lc, d 32*ks + 8*lq
@@ -216,6 +223,34 @@ __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a)
       }
     }
     wave_lds_sync();  // all lanes done reading the tile before the next overwrite
+  }
+
+  if (SOLO) {
+    // the wave holds its unit's whole key range: fold in the sink and finish.
+    // Lane holds O^T[d = 16*dt + 4*lq + r][head lc]; m_run is uniform over lq.
+    float lt = l_run + __shfl_xor(l_run, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (lc < n_heads) {
+      const int hq = h_base + lc;
+      const float s2 = a.sinks ? a.sinks[hq] * kLog2e : -INFINITY;
+      const float Mf = fmaxf(m_run, s2);
+      const float sc = fast_exp2(m_run - Mf);
+      const float Z = fast_exp2(s2 - Mf) + lt * sc;
+      const float inv = Z > 0.f ? sc / Z : (Z == 0.f ? 0.f : Z);
+      __bf16* op = a.out + (q_row * a.Hq + hq) * (int64_t)kHeadDim + 4 * lq;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+        w[1] = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+        *reinterpret_cast<u32x2*>(op + 16 * dt) = w;
+      }
+      if (a.lse && lq == 0) {
+        const float v = (Z == 0.f) ? -INFINITY : (Mf + __log2f(Z)) * kLn2;
+        a.lse[(int64_t)b * a.lse_sb + (int64_t)hq * a.lse_sh + (a.lse_row0 ? sv.q_row0 : 0)] = v;
+      }
+    }
+    return;
   }
 
   // ---- merge the 4 waves: per head max m, sum l, output acc[d]
@@ -322,14 +357,26 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, int kv_mode, hipStream_t s) {
-  const int grid = a.B * a.Hkv * a.n_hc * a.n_splits;
-  if (grid <= 0) return hipSuccess;
+  const int units = a.B * a.Hkv * a.n_hc;
+  if (units <= 0) return hipSuccess;
+  if (a.solo) {
+    if (a.n_splits != 1) return hipErrorInvalidValue;
+    const int grid = (units + 3) / 4;
+    if (kv_mode == KV_BATCHED)
+      hipLaunchKernelGGL((decode_split_kernel<KV_BATCHED, true>), dim3(grid), dim3(DTHREADS), 0, s, a);
+    else if (kv_mode == KV_PAGED)
+      hipLaunchKernelGGL((decode_split_kernel<KV_PAGED, true>), dim3(grid), dim3(DTHREADS), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<KV_PACKED, true>), dim3(grid), dim3(DTHREADS), 0, s, a);
+    return hipGetLastError();
+  }
+  const int grid = units * a.n_splits;
   if (kv_mode == KV_BATCHED)
-    hipLaunchKernelGGL((decode_split_kernel<KV_BATCHED>), dim3(grid), dim3(DTHREADS), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<KV_BATCHED, false>), dim3(grid), dim3(DTHREADS), 0, s, a);
   else if (kv_mode == KV_PAGED)
-    hipLaunchKernelGGL((decode_split_kernel<KV_PAGED>), dim3(grid), dim3(DTHREADS), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<KV_PAGED, false>), dim3(grid), dim3(DTHREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<KV_PACKED>), dim3(grid), dim3(DTHREADS), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<KV_PACKED, false>), dim3(grid), dim3(DTHREADS), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.Hq), dim3(64), 0, s, a);

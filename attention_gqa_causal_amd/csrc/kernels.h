@@ -46,6 +46,7 @@ struct DecodeArgs {
   int64_t lse_sb;    // lse index = b*lse_sb + h*lse_sh (+ q_row0 when lse_row0)
   int64_t lse_sh;
   int lse_row0;
+  int solo;          // one (sequence, KV head, head chunk) per wave, whole key range (n_splits == 1)
 };
 
 // fp32 I/O path: one wave per (query row, query head).
@@ -67,9 +68,23 @@ struct Fp32Args {
   int lse_row0;
 };
 
+// KV append into per-sequence rings of W slots (position p in slot p % W).
+struct RingAppendArgs {
+  const char* k_new;            // [T, Hkv, D] rows of new tokens
+  const char* v_new;
+  char* k_ring;                 // [B, W, Hkv, D]
+  char* v_ring;
+  const int32_t* cu_seqlens_q;  // [B+1] or NULL (then T == B, one new token per sequence)
+  const int32_t* seqlens;       // [B] positions including the new tokens
+  int64_t T;
+  int B, W;
+  int row_bytes;                // Hkv * D * element size
+};
+
 int prefill_ntiles_per_wg();  // N-tiles (32 rows of one head) per prefill workgroup
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int kv_mode, bool varlen_q, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int kv_mode, hipStream_t s);
 hipError_t launch_fp32(const Fp32Args& a, int kv_mode, hipStream_t s);
+hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t s);
 
 }  // namespace gqa

@@ -7,7 +7,11 @@ already resident in HBM:
   2. batched decode        B64, cache 8192, same heads -- dense, then window 128;
   3. ragged + paged        16 sequences, lengths U{128..8192}, 512-token
      prefill chunks and single-token decode steps, 16-token pages under a
-     permuted block table -- dense, then window 128.
+     permuted block table -- dense, then window 128;
+  4. ring cache of a windowed layer (128 slots per sequence): append of one
+     new token per sequence (B64), then decode from the rings at position 8191
+     for B64 and for B4096 (the B4096 rings hold as many bytes as the dense
+     B64 x 8192 cache).
 `value` is the prefill throughput of the layer pair (1), in algorithmic
 TFLOP/s (4*D*Hq per visible query-key pair), timed with HIP events on the
 stream the kernels run on; every stage's own time, TFLOP/s, GB/s and roofline
@@ -285,6 +289,32 @@ def add_varlen(stages, gq, r, up, i32, f32, dev):
             workspace=ws)), flop=fl, bytes=by, bound="mfma" if W == 0 else "hbm")
 
 
+def add_ring(stages, gq, up, i32, f32, dev):
+    import torch
+
+    import gqa_inputs as gi
+
+    for B in (64, 4096):
+        r = gi.c6_ring(B)
+        Hq, Hkv, D = r.q.shape[1], r.k_ring.shape[2], r.q.shape[2]
+        rq, rk, rv, rsl, rs = up(r.q), up(r.k_ring), up(r.v_ring), i32(r.seqlens), f32(r.sinks)
+        n_read = [min(int(L), r.W) for L in r.seqlens]
+        fl, by = decode_work(n_read, Hq, Hkv, D, 0)
+        nbytes = gq.decode_workspace_size(B, r.W, Hq, Hkv, D, 0)
+        ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+        stages[f"ring_decode_w128_b{B}"] = dict(
+            fn=(lambda rq=rq, rk=rk, rv=rv, rsl=rsl, rs=rs, ws=ws: gq.attn_decode_ring(rq, (rk, rv), rsl, rs,
+                                                                                      workspace=ws)),
+            flop=fl, bytes=by, bound="hbm")
+        if B == 64:
+            kn = up(gi.make_tensor(68, gi.T_K, (B, Hkv, D), 1.0, "bf16"))
+            vn = up(gi.make_tensor(68, gi.T_V, (B, Hkv, D), 1.0, "bf16"))
+            row = Hkv * D * 2
+            stages["ring_append_b64"] = dict(
+                fn=(lambda kn=kn, vn=vn, rk=rk, rv=rv, rsl=rsl: gq.kv_ring_append(kn, vn, (rk, rv), rsl)),
+                flop=0, bytes=4 * B * row, bound="hbm")
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -351,6 +381,9 @@ def main():
     # 3. ragged + paged
     if wanted("varlen"):
         add_varlen(stages, gq, gi.c5_ragged(), up, i32, f32, dev)
+    # 4. ring cache of a windowed layer
+    if wanted("ring"):
+        add_ring(stages, gq, up, i32, f32, dev)
     if args.long:
         long_stages = {}
         add_prefill(long_stages, gq, gi.c4_prefill(), up, f32, dev)
@@ -426,7 +459,8 @@ def main():
         "config": {
             "workload": "layer-shaped prefill B1 S4096 Hq64 Hkv8 D64 bf16, dense layer then 128-token sliding-window "
                         "layer (value); each step also runs batched decode B64 cache 8192 (dense, window 128) and "
-                        "ragged+paged 16 sequences (dense, window 128)",
+                        "ragged+paged 16 sequences (dense, window 128), and a windowed layer's 128-slot ring cache (append B64; "
+                        "decode B64 and B4096)",
             "global_batch": 1,
             "seq_len": 4096,
             "parallelism": "single GPU",

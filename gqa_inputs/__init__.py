@@ -263,6 +263,41 @@ def c5_ragged(cfg: int = 5) -> Varlen:
     return varlen_problem(cfg, kv, q, 64, 8, 64, block_size=16, maxblk=512, dtype="bf16", std=1.0)
 
 
+@dataclass
+class Ring:
+    """Decode step of a windowed layer against its ring cache of W slots per sequence."""
+
+    q: Tensor        # [B, Hq, D]
+    k_ring: Tensor   # [B, W, Hkv, D]
+    v_ring: Tensor
+    seqlens: np.ndarray  # [B] int32, positions including the new token
+    sinks: np.ndarray
+    scale: float
+    W: int
+
+
+def ring_problem(cfg: int, B: int, W: int, seqlens, Hq: int = 64, Hkv: int = 8, D: int = 64, dtype: str = "bf16",
+                 std: float = 1.0, sink_kind: str = "normal", scale: float | None = None) -> Ring:
+    """Ring contents drawn directly (every slot filled); seqlens given, or 'random' in [1, 3W]."""
+    if isinstance(seqlens, str) and seqlens == "random":
+        seqlens = rng_for(cfg, T_LEN).integers(1, 3 * W + 1, size=B)
+    seqlens = np.broadcast_to(np.asarray(seqlens, dtype=np.int32), (B,)).copy()
+    return Ring(
+        q=make_tensor(cfg, T_Q, (B, Hq, D), std, dtype),
+        k_ring=make_tensor(cfg, T_K, (B, W, Hkv, D), std, dtype),
+        v_ring=make_tensor(cfg, T_V, (B, W, Hkv, D), std, dtype),
+        seqlens=seqlens,
+        sinks=make_sinks(cfg, Hq, sink_kind),
+        scale=(1.0 / math.sqrt(D)) if scale is None else float(scale),
+        W=W,
+    )
+
+
+def c6_ring(B: int = 64) -> Ring:
+    """Windowed-layer decode from a 128-slot ring: B sequences at position 8191, 64/8 heads, bf16 N(0,1)."""
+    return ring_problem(6, B, 128, 8192)
+
+
 def to_torch(t: Tensor, device):
     """Device tensor holding exactly the bits of ``t`` (bf16 or fp32)."""
     import torch

@@ -152,6 +152,53 @@ int gqa_attn_varlen_paged(const void* q, const void* k_cache, const void* v_cach
                           int window, float scale, int dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Ring-buffer KV cache of sliding-window layers.
+ *
+ * A windowed layer attends to the last W positions only («GPT-OSS vs Qwen3»,
+ * section "Utilisation de Sliding Window Attention": 128 tokens, to bound the
+ * memory use), so its cache needs W slots per sequence instead of the whole
+ * history: position p of sequence b lives in slot p % W.
+ *   k_ring, v_ring [B, W, Hkv, D] (dtype as below).
+ */
+
+/*
+ * Writes the K and V rows of new tokens into their ring slots, bit for bit.
+ *   k_new, v_new [T, Hkv, D].
+ *   cu_seqlens_q == NULL: T == B, row b is the newest token of sequence b, at
+ *     position seqlens[b] - 1 (the decode step).
+ *   cu_seqlens_q [B+1] int32 (device, non-decreasing): sequence b's new rows
+ *     are cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1, the newest q_len positions:
+ *     row t at position seqlens[b] - q_len + t (a prefill chunk).
+ *   seqlens [B] int32 (device): positions of sequence b including the new rows.
+ * Only positions p >= seqlens[b] - W are written; of a chunk longer than the
+ * ring the older rows would only be overwritten by newer ones of the same
+ * call.  Rows with a negative position are skipped.  dtype sets the element
+ * size (GQA_BF16: 2 bytes, GQA_FP32: 4).  Errors as for every entry point;
+ * the caller orders this call before the attention that reads the ring.
+ */
+int gqa_kv_ring_append(const void* k_new, const void* v_new,
+                       const int32_t* cu_seqlens_q, const int32_t* seqlens,
+                       void* k_ring, void* v_ring,
+                       int B, int T, int W, int Hkv, int D, int dtype, void* stream);
+
+/*
+ * Decode on a windowed layer against its ring: the new query of sequence b
+ * (position seqlens[b] - 1; seqlens counts the new token, whose K/V row is
+ * already appended) attends to the min(seqlens[b], W) positions the ring
+ * holds, which are exactly the window of W keys ending at the query.  q, out,
+ * lse, sinks, scale and dtype as for gqa_attn_decode; the workspace must hold
+ * gqa_attn_decode_ring_workspace_size(...) bytes (0 for W <= 1024).
+ */
+size_t gqa_attn_decode_ring_workspace_size(int B, int W, int Hq, int Hkv, int D, int dtype);
+
+int gqa_attn_decode_ring(const void* q, const void* k_ring, const void* v_ring,
+                         const int32_t* seqlens, const float* sinks,
+                         void* out, float* lse,
+                         int B, int W, int Hq, int Hkv, int D,
+                         float scale, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

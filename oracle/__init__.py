@@ -7,7 +7,9 @@ link this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
 library and imports nothing from it.
 
 ``oracle.attention`` is the plain fp64 NumPy definition; ``oracle.brute`` is an
-independent pure-Python scalar enumeration of the same definition.
+independent pure-Python scalar enumeration of the same definition;
+``oracle.ring`` is the W-slot ring cache of windowed layers (append by position,
+decode through the windowed definition).
 
 Sources (the web pages this method is taken from):
 
@@ -48,4 +50,11 @@ from .attention import (  # noqa: F401
     probabilities,
     varlen_ref,
     visible_mask,
+)
+from .ring import (  # noqa: F401
+    decode_ring_ref,
+    ring_append_ref,
+    ring_from_history,
+    ring_positions,
+    ring_slot,
 )

@@ -1,0 +1,101 @@
+"""Ring-buffer KV cache of sliding-window layers (test infrastructure only).
+
+«GPT-OSS vs Qwen3», section "Utilisation de Sliding Window Attention": some
+layers attend only to the most recent 128 tokens, so as to use less memory.
+A windowed layer therefore never needs more than its last W positions; the
+plainest store for them is a ring of W slots per sequence, position p in slot
+p mod W (the slot rule is this reading; the pages name no layout).
+
+Everything here is plain NumPy.  ``decode_ring_ref`` does not trust the ring
+to hold the right positions: it recovers each slot's position from the slot
+rule, keeps the positions the window allows, and calls the windowed
+definition ``attention.attend`` with those positions.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import _default_scale, attend, kv_head
+
+
+def ring_slot(p: int, W: int) -> int:
+    """Slot of position p in a ring of W slots."""
+    return p % W
+
+
+def ring_positions(L: int, W: int) -> np.ndarray:
+    """Positions a ring of W slots holds after positions 0..L-1 were appended in order:
+    the last min(L, W) of them."""
+    return np.arange(max(0, L - W), L, dtype=np.int64)
+
+
+def ring_append_ref(k_ring, v_ring, k_new, v_new, seqlens, W: int, cu_seqlens_q=None):
+    """Rings after appending new rows (copies; inputs are not modified).
+
+    k_ring/v_ring [B, W, Hkv, D]; k_new/v_new [T, Hkv, D].  Without cu_seqlens_q
+    row b is the newest token of sequence b (position seqlens[b] - 1); with it,
+    sequence b's rows are its newest q_len positions.  Rows are applied in
+    position order, so of a chunk longer than W the newest rows remain.
+    """
+    k_ring = np.array(k_ring, copy=True)
+    v_ring = np.array(v_ring, copy=True)
+    B = k_ring.shape[0]
+    for b in range(B):
+        L = int(seqlens[b])
+        if cu_seqlens_q is None:
+            rows = [b]
+        else:
+            rows = list(range(int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])))
+        q_len = len(rows)
+        for t, r in enumerate(rows):
+            p = L - q_len + t
+            if p < 0:
+                continue
+            s = ring_slot(p, W)
+            k_ring[b, s] = k_new[r]
+            v_ring[b, s] = v_new[r]
+    return k_ring, v_ring
+
+
+def ring_from_history(k_full, v_full, seqlens, W: int):
+    """Rings of W slots built by appending positions 0..L-1 of each sequence one at a time.
+
+    k_full/v_full [B, Lmax, Hkv, D].  Slots never written stay zero.
+    """
+    B, _, Hkv, D = k_full.shape
+    k_ring = np.zeros((B, W, Hkv, D), dtype=k_full.dtype)
+    v_ring = np.zeros((B, W, Hkv, D), dtype=v_full.dtype)
+    for b in range(B):
+        for p in range(int(seqlens[b])):
+            k_ring[b, ring_slot(p, W)] = k_full[b, p]
+            v_ring[b, ring_slot(p, W)] = v_full[b, p]
+    return k_ring, v_ring
+
+
+def decode_ring_ref(q, k_ring, v_ring, seqlens, sinks, W: int, scale=None):
+    """Decode on a windowed layer from its ring.
+
+    q [B, Hq, D]; rings [B, W, Hkv, D]; seqlens[b] counts the new token (query at
+    position seqlens[b] - 1).  The keys are the positions the ring holds, each
+    read from its slot, under the window-W causal mask of the definition.
+    Returns o [B, Hq, D], lse [B, Hq].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_ring = np.asarray(k_ring, dtype=np.float64)
+    v_ring = np.asarray(v_ring, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv = k_ring.shape[2]
+    scale = _default_scale(D, scale)
+    sinks = np.full((Hq,), -np.inf) if sinks is None else np.asarray(sinks, dtype=np.float64)
+    o = np.zeros((B, Hq, v_ring.shape[3]))
+    lse = np.zeros((B, Hq))
+    for b in range(B):
+        L = int(seqlens[b])
+        pos = ring_positions(L, W)
+        slots = pos % W
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            ob, lb = attend(q[b, h][None], k_ring[b, slots, g], v_ring[b, slots, g], [L - 1], pos,
+                            sinks[h], W, scale)
+            o[b, h], lse[b, h] = ob[0], lb[0]
+    return o, lse

@@ -20,7 +20,7 @@ DUMMY = P(256)  # never dereferenced: every call below fails validation first
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gqa_attn_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gqa_\w+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -29,12 +29,12 @@ def L():
 
 
 def test_library_loads(L):
-    assert L.gqa_attn_version() == 100
+    assert L.gqa_attn_version() == 200
 
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -154,3 +154,55 @@ def test_no_oracle_on_product_path():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 src = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "import oracle" not in src and "from oracle" not in src, f
+
+
+def ring_append(L, B=4, T=4, W=128, Hkv=8, D=64, dt=0, cu=None, seqlens=DUMMY, kn=DUMMY, vn=DUMMY,
+                kr=DUMMY, vr=DUMMY):
+    return L.gqa_kv_ring_append(kn, vn, cu, seqlens, kr, vr, B, T, W, Hkv, D, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=128), -2),
+    (dict(dt=7), -2),
+    (dict(W=0), -1),
+    (dict(W=-5), -1),
+    (dict(T=3), -1),           # one new row per sequence without cu_seqlens_q
+    (dict(B=-1), -1),
+    (dict(Hkv=0), -1),
+    (dict(seqlens=None), -1),
+    (dict(kr=None), -1),
+])
+def test_ring_append_rejects(L, kw, code):
+    assert ring_append(L, **kw) == code
+    assert L.gqa_attn_last_error() != b""
+
+
+def test_ring_append_empty_is_ok(L):
+    assert ring_append(L, B=0, T=0, seqlens=None, kn=None, vn=None, kr=None, vr=None) == 0
+    assert ring_append(L, B=3, T=0, cu=DUMMY, seqlens=None, kn=None, vn=None, kr=None, vr=None) == 0
+
+
+def ring_decode(L, B=2, W=128, Hq=64, Hkv=8, D=64, scale=0.0, dt=0, q=DUMMY, seqlens=DUMMY, ws=None, ws_bytes=0):
+    return L.gqa_attn_decode_ring(q, DUMMY, DUMMY, seqlens, None, DUMMY, None, B, W, Hq, Hkv, D, scale, dt,
+                                  ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=0), -1),
+    (dict(D=32), -2),
+    (dict(Hq=12), -2),
+    (dict(scale=-1.0), -1),
+    (dict(seqlens=None), -1),
+    (dict(q=None), -1),
+])
+def test_ring_decode_rejects(L, kw, code):
+    assert ring_decode(L, **kw) == code
+
+
+def test_ring_decode_workspace(L):
+    # one split for a 128-slot ring; a long ring needs split partials
+    assert L.gqa_attn_decode_ring_workspace_size(64, 128, 64, 8, 64, 0) == 0
+    assert L.gqa_attn_decode_ring_workspace_size(8, 65536, 64, 8, 64, 0) > 0
+    big = L.gqa_attn_decode_ring_workspace_size(8, 65536, 64, 8, 64, 0)
+    assert ring_decode(L, B=8, W=65536, ws=None, ws_bytes=0) == -3
+    assert ring_decode(L, B=8, W=65536, ws=DUMMY, ws_bytes=big - 1) == -3
