@@ -3,7 +3,9 @@
 The definition, for one sequence, query head h and a query at position p:
 
     G   = Hq / Hkv,  g = h // G                       (grouped KV heads)
-    J   = { j : j <= p  and  (W <= 0  or  j > p - W) } (causal, last W keys)
+    J   = { j : j <= p  and  (W <= 0  or  j > p - W  or  j < n) }
+                                                       (causal, last W keys, plus the
+                                                        first n "sink tokens" when asked)
     x_j = scale * <q, k_j[g]>                          (scaled dot product)
     s   = sinks[h]                                     (learned sink logit)
     m   = max(s, max_{j in J} x_j)
@@ -40,25 +42,28 @@ def kv_head(h: int, hq: int, hkv: int) -> int:
     return h // (hq // hkv)
 
 
-def visible_mask(q_pos: np.ndarray, k_pos: np.ndarray, window: int) -> np.ndarray:
+def visible_mask(q_pos: np.ndarray, k_pos: np.ndarray, window: int, sink_tokens: int = 0) -> np.ndarray:
     """Boolean [n_q, n_k]: key position j is visible from query position p.
 
     Causal (decoder-only, autoregressive: «OpenAI lance gpt-oss-20b, qui tient
     sur 16 Go», opening section): j <= p.  Sliding window («GPT-OSS vs Qwen3»,
     "Utilisation de Sliding Window Attention"): only the last W tokens,
     read as j > p - W, i.e. exactly W keys counting the query's own position.
-    W <= 0 means dense.
+    W <= 0 means dense.  Sink tokens («GPT-OSS vs Qwen3», "Attention Bias et
+    Sinks": the classical sink is a token at the start of the sequence that is
+    always attended): the first ``sink_tokens`` positions stay visible past the
+    window edge (still causal).
     """
     p = np.asarray(q_pos, dtype=np.int64)[:, None]
     j = np.asarray(k_pos, dtype=np.int64)[None, :]
     vis = j <= p
     if window > 0:
-        vis &= j > p - window
+        vis &= (j > p - window) | (j < sink_tokens)
     return vis
 
 
 def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos, k_pos, sink: float,
-           window: int, scale: float, return_probs: bool = False):
+           window: int, scale: float, return_probs: bool = False, sink_tokens: int = 0):
     """Single-head attention of query rows against a set of keys.
 
     q: [n, D], k: [L, D], v: [L, Dv] (fp64), q_pos: [n], k_pos: [L].
@@ -69,7 +74,7 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos, k_pos, sink: floa
     v = np.asarray(v, dtype=np.float64)
     n, L = q.shape[0], k.shape[0]
     s = float(sink)
-    vis = visible_mask(q_pos, k_pos, window)
+    vis = visible_mask(q_pos, k_pos, window, sink_tokens)
     x = scale * (q @ k.T) if L else np.zeros((n, 0))
     xm = np.where(vis, x, -np.inf)
     row_max = xm.max(axis=1) if L else np.full((n,), -np.inf)
@@ -102,7 +107,7 @@ def _default_scale(D: int, scale) -> float:
     return 1.0 / math.sqrt(D) if (scale is None or scale <= 0) else float(scale)
 
 
-def prefill_rows_ref(q, k, v, sinks, window: int = 0, scale=None, rows=None, heads=None):
+def prefill_rows_ref(q, k, v, sinks, window: int = 0, scale=None, rows=None, heads=None, sink_tokens: int = 0):
     """Prefill (self-attention of a whole sequence), optionally on a subset of query rows.
 
     q: [B, S, Hq, D], k/v: [B, S, Hkv, D], sinks: [Hq] (or None = no sink).
@@ -125,16 +130,16 @@ def prefill_rows_ref(q, k, v, sinks, window: int = 0, scale=None, rows=None, hea
         for h in heads:
             g = kv_head(h, Hq, Hkv)
             o[b, :, h], lse[b, h] = attend(q[b, rows, h], k[b, :, g], v[b, :, g], rows, k_pos,
-                                           sinks[h], window, scale)
+                                           sinks[h], window, scale, sink_tokens=sink_tokens)
     return o, lse
 
 
-def prefill_ref(q, k, v, sinks, window: int = 0, scale=None):
+def prefill_ref(q, k, v, sinks, window: int = 0, scale=None, sink_tokens: int = 0):
     """Full prefill: o [B, S, Hq, D], lse [B, Hq, S]."""
-    return prefill_rows_ref(q, k, v, sinks, window, scale)
+    return prefill_rows_ref(q, k, v, sinks, window, scale, sink_tokens=sink_tokens)
 
 
-def decode_ref(q, k_cache, v_cache, seqlens, sinks, window: int = 0, scale=None):
+def decode_ref(q, k_cache, v_cache, seqlens, sinks, window: int = 0, scale=None, sink_tokens: int = 0):
     """One new query token per sequence against a contiguous KV cache.
 
     q: [B, Hq, D]; caches [B, Lmax, Hkv, D]; seqlens[b] counts the cached
@@ -157,7 +162,7 @@ def decode_ref(q, k_cache, v_cache, seqlens, sinks, window: int = 0, scale=None)
         for h in range(Hq):
             g = kv_head(h, Hq, Hkv)
             ob, lb = attend(q[b, h][None], k_cache[b, :L, g], v_cache[b, :L, g], [L - 1], k_pos,
-                            sinks[h], window, scale)
+                            sinks[h], window, scale, sink_tokens=sink_tokens)
             o[b, h], lse[b, h] = ob[0], lb[0]
     return o, lse
 
@@ -174,7 +179,7 @@ def gather_paged(cache, block_table_row, block_size: int, L: int):
 
 
 def varlen_ref(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, sinks, window: int = 0, scale=None,
-               block_table=None, block_size: int = 16, cu_seqlens_k=None, rows=None):
+               block_table=None, block_size: int = 16, cu_seqlens_k=None, rows=None, sink_tokens: int = 0):
     """Packed variable-length queries against a paged (or packed) KV cache.
 
     q: [Tq, Hq, D].  Sequence b owns query rows cu_seqlens_q[b]..cu_seqlens_q[b+1]-1
@@ -213,13 +218,14 @@ def varlen_ref(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, sinks, window: int 
         k_pos = np.arange(L)
         for h in range(Hq):
             g = kv_head(h, Hq, Hkv)
-            ob, lb = attend(q[sel, h], kb[:, g], vb[:, g], q_pos, k_pos, sinks[h], window, scale)
+            ob, lb = attend(q[sel, h], kb[:, g], vb[:, g], q_pos, k_pos, sinks[h], window, scale,
+                            sink_tokens=sink_tokens)
             o[sel, h] = ob
             lse[h, sel] = lb
     return o, lse
 
 
-def probabilities(q, k, v, sinks, window: int = 0, scale=None):
+def probabilities(q, k, v, sinks, window: int = 0, scale=None, sink_tokens: int = 0):
     """Attention weights of a prefill: p [B, Hq, S, S] (zero off the visible set) and
     sink_mass [B, Hq, S]; p summed over keys plus sink_mass is one in every row."""
     q = np.asarray(q, dtype=np.float64)
@@ -235,5 +241,6 @@ def probabilities(q, k, v, sinks, window: int = 0, scale=None):
             g = kv_head(h, Hq, Hkv)
             _, _, P[b, h], SM[b, h] = attend(q[b, :, h], np.asarray(k, dtype=np.float64)[b, :, g],
                                              np.asarray(v, dtype=np.float64)[b, :, g], pos, pos,
-                                             sinks[h], window, scale, return_probs=True)
+                                             sinks[h], window, scale, return_probs=True,
+                                             sink_tokens=sink_tokens)
     return P, SM
