@@ -6,8 +6,8 @@ no fallback: if the library is not built, every call raises.
 
 Functions (names follow the C ABI in ``include/gqa_attn.h``):
 
-* ``attn_prefill(q, k, v, sinks, window=0, scale=None)``
-* ``attn_decode(q, kv_cache, seqlens, sinks, window=0, scale=None)``
+* ``attn_prefill(q, k, v, sinks, window=0, scale=None, sink_tokens=0)``
+* ``attn_decode(q, kv_cache, seqlens, sinks, window=0, scale=None, sink_tokens=0)``
 * ``attn_varlen_paged(q, kv_cache, block_table, cu_seqlens_q, seqlens_k, sinks, ...)``
 * ``kv_ring_append(k_new, v_new, kv_ring, seqlens, cu_seqlens_q=None)`` and
   ``attn_decode_ring(q, kv_ring, seqlens, sinks, scale=None)``: the W-slot ring
@@ -71,12 +71,12 @@ _SIGNATURES = {
     "gqa_attn_version": (_I, []),
     "gqa_attn_status_string": (ctypes.c_char_p, [_I]),
     "gqa_attn_last_error": (ctypes.c_char_p, []),
-    "gqa_attn_prefill": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
-    "gqa_attn_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
-    "gqa_attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
-    "gqa_attn_varlen_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "gqa_attn_prefill": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "gqa_attn_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "gqa_attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "gqa_attn_varlen_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "gqa_attn_varlen_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _P, _P, _P,
-                                   _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+                                   _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "gqa_kv_ring_append": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "gqa_attn_decode_ring_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "gqa_attn_decode_ring": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
@@ -156,7 +156,8 @@ def _split_cache(kv_cache):
     return kv_cache[0], kv_cache[1]
 
 
-def attn_prefill(q, k, v, sinks=None, window: int = 0, scale=None, return_lse: bool = False, out=None):
+def attn_prefill(q, k, v, sinks=None, window: int = 0, scale=None, return_lse: bool = False, out=None,
+                 sink_tokens: int = 0):
     """Causal self-attention over whole sequences.
 
     q [B, S, Hq, 64], k/v [B, S, Hkv, 64] (bf16 or fp32, same dtype, on the GPU);
@@ -178,16 +179,16 @@ def attn_prefill(q, k, v, sinks=None, window: int = 0, scale=None, return_lse: b
         _need(out.shape == q.shape, "out must match q")
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev) if return_lse else None
     _check(lib().gqa_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(out), _ptr(lse),
-                                  B, S, Hq, Hkv, D, int(window), _scale(scale), dt, _stream(dev)))
+                                  B, S, Hq, Hkv, D, int(window), int(sink_tokens), _scale(scale), dt, _stream(dev)))
     return (out, lse) if return_lse else out
 
 
-def decode_workspace_size(B, Lmax, Hq, Hkv, D=64, window=0, dtype=GQA_BF16) -> int:
-    return int(lib().gqa_attn_decode_workspace_size(B, Lmax, Hq, Hkv, D, int(window), dtype))
+def decode_workspace_size(B, Lmax, Hq, Hkv, D=64, window=0, dtype=GQA_BF16, sink_tokens=0) -> int:
+    return int(lib().gqa_attn_decode_workspace_size(B, Lmax, Hq, Hkv, D, int(window), int(sink_tokens), dtype))
 
 
 def attn_decode(q, kv_cache, seqlens, sinks=None, window: int = 0, scale=None, return_lse: bool = False,
-                workspace=None):
+                workspace=None, sink_tokens: int = 0):
     """One new query token per sequence against a contiguous KV cache.
 
     q [B, Hq, 64]; kv_cache = (k_cache, v_cache) each [B, Lmax, Hkv, 64], or one
@@ -208,23 +209,24 @@ def attn_decode(q, kv_cache, seqlens, sinks=None, window: int = 0, scale=None, r
     sinks = _sinks_arg(sinks, Hq, dev)
     out = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None
-    ws_bytes = int(lib().gqa_attn_decode_workspace_size(B, Lmax, Hq, Hkv, D, int(window), dt))
+    ws_bytes = int(lib().gqa_attn_decode_workspace_size(B, Lmax, Hq, Hkv, D, int(window), int(sink_tokens), dt))
     if ws_bytes and workspace is None:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().gqa_attn_decode(_ptr(q), _ptr(kc), _ptr(vc), _ptr(seqlens), _ptr(sinks), _ptr(out), _ptr(lse),
-                                 B, Lmax, Hq, Hkv, D, int(window), _scale(scale), dt,
+                                 B, Lmax, Hq, Hkv, D, int(window), int(sink_tokens), _scale(scale), dt,
                                  _ptr(workspace), ws_have, _stream(dev)))
     return (out, lse) if return_lse else out
 
 
-def varlen_workspace_size(B, max_q_len, max_kv_len, Hq, Hkv, D=64, window=0, dtype=GQA_BF16) -> int:
-    return int(lib().gqa_attn_varlen_workspace_size(B, max_q_len, max_kv_len, Hq, Hkv, D, int(window), dtype))
+def varlen_workspace_size(B, max_q_len, max_kv_len, Hq, Hkv, D=64, window=0, dtype=GQA_BF16, sink_tokens=0) -> int:
+    return int(lib().gqa_attn_varlen_workspace_size(B, max_q_len, max_kv_len, Hq, Hkv, D, int(window),
+                                                    int(sink_tokens), dtype))
 
 
 def attn_varlen_paged(q, kv_cache, block_table, cu_seqlens_q, seqlens_k, sinks=None, window: int = 0, scale=None,
                       max_q_len: int | None = None, max_kv_len: int | None = None, cu_seqlens_k=None,
-                      return_lse: bool = False, workspace=None):
+                      return_lse: bool = False, workspace=None, sink_tokens: int = 0):
     """Packed variable-length queries over a paged KV cache (mixed prefill chunks and decode steps).
 
     q [Tq, Hq, 64]; kv_cache = (k_cache, v_cache) each [num_blocks, block_size, Hkv, 64]
@@ -269,14 +271,15 @@ def attn_varlen_paged(q, kv_cache, block_table, cu_seqlens_q, seqlens_k, sinks=N
     sinks = _sinks_arg(sinks, Hq, dev)
     out = torch.empty_like(q)
     lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev) if return_lse else None
-    ws_bytes = int(lib().gqa_attn_varlen_workspace_size(B, max_q_len, max_kv_len, Hq, Hkv, D, int(window), dt))
+    ws_bytes = int(lib().gqa_attn_varlen_workspace_size(B, max_q_len, max_kv_len, Hq, Hkv, D, int(window),
+                                                        int(sink_tokens), dt))
     if ws_bytes and workspace is None:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().gqa_attn_varlen_paged(_ptr(q), _ptr(kc), _ptr(vc), _ptr(cu_seqlens_q), _ptr(seqlens_k),
                                        _ptr(block_table), max_blocks, block_size, _ptr(cu_seqlens_k), num_blocks,
                                        _ptr(sinks), _ptr(out), _ptr(lse), B, Tq, int(max_q_len), int(max_kv_len),
-                                       Hq, Hkv, D, int(window), _scale(scale), dt,
+                                       Hq, Hkv, D, int(window), int(sink_tokens), _scale(scale), dt,
                                        _ptr(workspace), ws_have, _stream(dev)))
     return (out, lse) if return_lse else out
 

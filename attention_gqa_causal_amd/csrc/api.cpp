@@ -62,12 +62,13 @@ int env_int(const char* name, int dflt) {
   return atoi(s);
 }
 
-int check_common(int Hq, int Hkv, int D, int window, float scale, int dtype) {
+int check_common(int Hq, int Hkv, int D, int window, int sink_tokens, float scale, int dtype) {
   if (dtype != GQA_BF16 && dtype != GQA_FP32) return fail(GQA_ERR_UNSUPPORTED, "dtype %d is not GQA_BF16 or GQA_FP32", dtype);
   if (Hq <= 0 || Hkv <= 0) return fail(GQA_ERR_INVALID_ARG, "head counts must be positive (Hq=%d, Hkv=%d)", Hq, Hkv);
   if (Hq % Hkv != 0) return fail(GQA_ERR_UNSUPPORTED, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   if (D != kHeadDim) return fail(GQA_ERR_UNSUPPORTED, "head_dim %d is not supported (only 64)", D);
   if (window < 0) return fail(GQA_ERR_INVALID_ARG, "window %d is negative (0 = dense)", window);
+  if (sink_tokens < 0) return fail(GQA_ERR_INVALID_ARG, "sink_tokens %d is negative", sink_tokens);
   if (std::isnan(scale) || scale < 0.f) return fail(GQA_ERR_INVALID_ARG, "scale must be >= 0 (0 = 1/sqrt(D))");
   return GQA_OK;
 }
@@ -86,8 +87,10 @@ struct SplitPlan {
 // Split of the decode key range: enough workgroups to keep about 16 per CU in
 // the queue (the streaming loads then overlap the merge of finished ones),
 // while every split keeps at least 1024 keys (4 tiles of 64 per wave).
-SplitPlan plan_splits(int B, int Hkv, int G, int Lmax, int window) {
-  const int eff = window > 0 ? (window < Lmax ? window : Lmax) : Lmax;
+SplitPlan plan_splits(int B, int Hkv, int G, int Lmax, int window, int sink_tokens) {
+  // keys read per sequence at most: the window plus the sink tokens below it
+  const long wk = window > 0 ? (long)window + sink_tokens : (long)Lmax;
+  const int eff = (int)(wk < Lmax ? wk : Lmax);
   const int n_hc = (G + 15) / 16;
   const long units = (long)B * Hkv * n_hc;
   SplitPlan p{1, 64, 0};
@@ -123,7 +126,7 @@ size_t decode_ws_bytes(const SplitPlan& p, int B, int Hq) {
 
 extern "C" {
 
-int gqa_attn_version(void) { return 200; }
+int gqa_attn_version(void) { return 300; }
 
 const char* gqa_attn_status_string(int status) {
   switch (status) {
@@ -139,8 +142,9 @@ const char* gqa_attn_status_string(int status) {
 const char* gqa_attn_last_error(void) { return g_err; }
 
 int gqa_attn_prefill(const void* q, const void* k, const void* v, const float* sinks, void* out, float* lse,
-                     int B, int S, int Hq, int Hkv, int D, int window, float scale, int dtype, void* stream) {
-  int rc = check_common(Hq, Hkv, D, window, scale, dtype);
+                     int B, int S, int Hq, int Hkv, int D, int window, int sink_tokens, float scale, int dtype,
+                     void* stream) {
+  int rc = check_common(Hq, Hkv, D, window, sink_tokens, scale, dtype);
   if (rc) return rc;
   if (B < 0 || S < 0) return fail(GQA_ERR_INVALID_ARG, "negative size (B=%d, S=%d)", B, S);
   if (B == 0 || S == 0) return ok();
@@ -159,7 +163,7 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, const float* s
     Fp32Args a{};
     a.q = (const float*)q; a.k = (const float*)k; a.v = (const float*)v; a.sinks = sinks;
     a.out = (float*)out; a.lse = lse; a.seq = seq;
-    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = window; a.scale_log2 = sl2;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = window; a.sink_tokens = sink_tokens; a.scale_log2 = sl2;
     a.max_q_len = S; a.varlen_q = 0;
     a.lse_sb = (int64_t)Hq * S; a.lse_sh = S; a.lse_row0 = 0;
     hipError_t e = launch_fp32(a, KV_BATCHED, st);
@@ -169,7 +173,7 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, const float* s
   PrefillArgs a{};
   a.q = (const __bf16*)q; a.k = (const __bf16*)k; a.v = (const __bf16*)v; a.sinks = sinks;
   a.out = (__bf16*)out; a.lse = lse; a.seq = seq;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = window; a.scale_log2 = sl2;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = window; a.sink_tokens = sink_tokens; a.scale_log2 = sl2;
   const long ntiles = (long)((S + 31) / 32) * G;
   a.wg_per_seq = (int)((ntiles + prefill_ntiles_per_wg() - 1) / prefill_ntiles_per_wg());
   a.skip_single = 0;
@@ -179,16 +183,20 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, const float* s
   return e == hipSuccess ? ok() : hip_fail(e, "prefill bf16 launch");
 }
 
-size_t gqa_attn_decode_workspace_size(int B, int Lmax, int Hq, int Hkv, int D, int window, int dtype) {
-  if (dtype != GQA_BF16 || B <= 0 || Lmax <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D != kHeadDim || window < 0) return 0;
-  const SplitPlan p = plan_splits(B, Hkv, Hq / Hkv, Lmax, window);
+size_t gqa_attn_decode_workspace_size(int B, int Lmax, int Hq, int Hkv, int D, int window, int sink_tokens,
+                                      int dtype) {
+  if (dtype != GQA_BF16 || B <= 0 || Lmax <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D != kHeadDim || window < 0 ||
+      sink_tokens < 0)
+    return 0;
+  const SplitPlan p = plan_splits(B, Hkv, Hq / Hkv, Lmax, window, sink_tokens);
   return decode_ws_bytes(p, B, Hq);
 }
 
 int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
                     const float* sinks, void* out, float* lse, int B, int Lmax, int Hq, int Hkv, int D,
-                    int window, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_common(Hq, Hkv, D, window, scale, dtype);
+                    int window, int sink_tokens, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  int rc = check_common(Hq, Hkv, D, window, sink_tokens, scale, dtype);
   if (rc) return rc;
   if (B < 0 || Lmax < 0) return fail(GQA_ERR_INVALID_ARG, "negative size (B=%d, Lmax=%d)", B, Lmax);
   if (B == 0) return ok();
@@ -208,14 +216,14 @@ int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, con
     Fp32Args a{};
     a.q = (const float*)q; a.k = (const float*)k_cache; a.v = (const float*)v_cache; a.sinks = sinks;
     a.out = (float*)out; a.lse = lse; a.seq = seq;
-    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = window; a.scale_log2 = sl2;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = window; a.sink_tokens = sink_tokens; a.scale_log2 = sl2;
     a.max_q_len = 1; a.varlen_q = 0;
     a.lse_sb = Hq; a.lse_sh = 1; a.lse_row0 = 0;
     hipError_t e = launch_fp32(a, KV_BATCHED, st);
     return e == hipSuccess ? ok() : hip_fail(e, "decode fp32 launch");
   }
 
-  const SplitPlan p = plan_splits(B, Hkv, G, Lmax, window);
+  const SplitPlan p = plan_splits(B, Hkv, G, Lmax, window, sink_tokens);
   const size_t need = decode_ws_bytes(p, B, Hq);
   if (need && (!workspace || workspace_bytes < need))
     return fail(GQA_ERR_WORKSPACE, "decode needs a workspace of %zu bytes (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
@@ -223,7 +231,7 @@ int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, con
   a.q = (const __bf16*)q; a.k = (const __bf16*)k_cache; a.v = (const __bf16*)v_cache; a.sinks = sinks;
   a.out = (__bf16*)out; a.lse = lse; a.seq = seq;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.n_hc = (G + 15) / 16;
-  a.window = window; a.scale_log2 = sl2;
+  a.window = window; a.sink_tokens = sink_tokens; a.scale_log2 = sl2;
   a.n_splits = p.n_splits; a.split_len = p.split_len;
   a.ws_ml = (float*)workspace;
   a.ws_acc = need ? (float*)workspace + (size_t)B * Hq * p.n_splits * 2 : nullptr;
@@ -236,11 +244,11 @@ int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, con
 }
 
 size_t gqa_attn_varlen_workspace_size(int B, int max_q_len, int max_kv_len, int Hq, int Hkv, int D, int window,
-                                      int dtype) {
+                                      int sink_tokens, int dtype) {
   if (dtype != GQA_BF16 || B <= 0 || max_q_len <= 0 || max_kv_len <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv ||
-      D != kHeadDim || window < 0)
+      D != kHeadDim || window < 0 || sink_tokens < 0)
     return 0;
-  const SplitPlan p = plan_splits(B, Hkv, Hq / Hkv, max_kv_len, window);
+  const SplitPlan p = plan_splits(B, Hkv, Hq / Hkv, max_kv_len, window, sink_tokens);
   return decode_ws_bytes(p, B, Hq);
 }
 
@@ -248,8 +256,9 @@ int gqa_attn_varlen_paged(const void* q, const void* k_cache, const void* v_cach
                           const int32_t* seqlens_k, const int32_t* block_table, int max_blocks, int block_size,
                           const int32_t* cu_seqlens_k, int num_blocks, const float* sinks, void* out, float* lse,
                           int B, int Tq, int max_q_len, int max_kv_len, int Hq, int Hkv, int D, int window,
-                          float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_common(Hq, Hkv, D, window, scale, dtype);
+                          int sink_tokens, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  int rc = check_common(Hq, Hkv, D, window, sink_tokens, scale, dtype);
   if (rc) return rc;
   if (B < 0 || Tq < 0 || max_q_len < 0 || max_kv_len < 0)
     return fail(GQA_ERR_INVALID_ARG, "negative size (B=%d, Tq=%d, max_q_len=%d, max_kv_len=%d)", B, Tq, max_q_len, max_kv_len);
@@ -290,14 +299,14 @@ int gqa_attn_varlen_paged(const void* q, const void* k_cache, const void* v_cach
     Fp32Args a{};
     a.q = (const float*)q; a.k = (const float*)k_cache; a.v = (const float*)v_cache; a.sinks = sinks;
     a.out = (float*)out; a.lse = lse; a.seq = seq;
-    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = window; a.scale_log2 = sl2;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = window; a.sink_tokens = sink_tokens; a.scale_log2 = sl2;
     a.max_q_len = max_q_len; a.varlen_q = 1;
     a.lse_sb = 0; a.lse_sh = Tq; a.lse_row0 = 1;
     hipError_t e = launch_fp32(a, mode, st);
     return e == hipSuccess ? ok() : hip_fail(e, "varlen fp32 launch");
   }
 
-  const SplitPlan p = plan_splits(B, Hkv, G, max_kv_len, window);
+  const SplitPlan p = plan_splits(B, Hkv, G, max_kv_len, window, sink_tokens);
   const size_t need = decode_ws_bytes(p, B, Hq);
   if (need && (!workspace || workspace_bytes < need))
     return fail(GQA_ERR_WORKSPACE, "varlen needs a workspace of %zu bytes (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
@@ -306,7 +315,7 @@ int gqa_attn_varlen_paged(const void* q, const void* k_cache, const void* v_cach
     PrefillArgs a{};
     a.q = (const __bf16*)q; a.k = (const __bf16*)k_cache; a.v = (const __bf16*)v_cache; a.sinks = sinks;
     a.out = (__bf16*)out; a.lse = lse; a.seq = seq;
-    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = window; a.scale_log2 = sl2;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = window; a.sink_tokens = sink_tokens; a.scale_log2 = sl2;
     const long ntiles = (long)((max_q_len + 31) / 32) * G;
     a.wg_per_seq = (int)((ntiles + prefill_ntiles_per_wg() - 1) / prefill_ntiles_per_wg());
     a.skip_single = 1;
@@ -319,7 +328,7 @@ int gqa_attn_varlen_paged(const void* q, const void* k_cache, const void* v_cach
   a.q = (const __bf16*)q; a.k = (const __bf16*)k_cache; a.v = (const __bf16*)v_cache; a.sinks = sinks;
   a.out = (__bf16*)out; a.lse = lse; a.seq = seq;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.n_hc = (G + 15) / 16;
-  a.window = window; a.scale_log2 = sl2;
+  a.window = window; a.sink_tokens = sink_tokens; a.scale_log2 = sl2;
   a.n_splits = p.n_splits; a.split_len = p.split_len;
   a.ws_ml = (float*)workspace;
   a.ws_acc = need ? (float*)workspace + (size_t)B * Hq * p.n_splits * 2 : nullptr;
@@ -353,7 +362,7 @@ int gqa_kv_ring_append(const void* k_new, const void* v_new, const int32_t* cu_s
 }
 
 size_t gqa_attn_decode_ring_workspace_size(int B, int W, int Hq, int Hkv, int D, int dtype) {
-  return gqa_attn_decode_workspace_size(B, W, Hq, Hkv, D, 0, dtype);
+  return gqa_attn_decode_workspace_size(B, W, Hq, Hkv, D, 0, 0, dtype);
 }
 
 int gqa_attn_decode_ring(const void* q, const void* k_ring, const void* v_ring, const int32_t* seqlens,
@@ -364,7 +373,7 @@ int gqa_attn_decode_ring(const void* q, const void* k_ring, const void* v_ring, 
   // min(seqlens[b], W) slots, all visible.  Key order does not enter the
   // result, so this is dense attention over the valid slots of a W-slot cache
   // (the kernels clamp each length to W).
-  return gqa_attn_decode(q, k_ring, v_ring, seqlens, sinks, out, lse, B, W, Hq, Hkv, D, 0, scale, dtype,
+  return gqa_attn_decode(q, k_ring, v_ring, seqlens, sinks, out, lse, B, W, Hq, Hkv, D, 0, 0, scale, dtype,
                          workspace, workspace_bytes, stream);
 }
 

@@ -4,7 +4,8 @@
 // query heads of its group («GPT-OSS-20B : Architecture MoE & Résumé du Model
 // Card» §3.3, 8 query heads per KV head), and on sliding-window layers only the
 // last W positions are read («GPT-OSS vs Qwen3», "Utilisation de Sliding Window
-// Attention").  The sink logit («GPT-OSS vs Qwen3», "Attention Bias et Sinks")
+// Attention"), plus the start-of-sequence sink tokens when asked («GPT-OSS vs
+// Qwen3», "Attention Bias et Sinks").  The sink logit («GPT-OSS vs Qwen3», "Attention Bias et Sinks")
 // enters once, when the partial results are merged.
 //
 // Work decomposition: a workgroup owns (sequence, KV head, chunk of up to 16
@@ -76,8 +77,13 @@ __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a)
   const int L = sv.kv_len;
   const int W = a.window;
   const int lo_all = W > 0 ? max(0, L - W) : 0;
-  const int s_lo = lo_all + split * a.split_len;
-  const int s_hi = min(L, s_lo + a.split_len);  // exclusive
+  // Keys read: the sink tokens below the window, then the window, numbered by
+  // a "virtual" index v in [0, nv): key v for v < ns, lo_all + v - ns after.
+  // Splits and tiles run over v.
+  const int ns = W > 0 ? min(a.sink_tokens, lo_all) : 0;
+  const int nv = ns + (L - lo_all);
+  const int s_lo = split * a.split_len;
+  const int s_hi = min(nv, s_lo + a.split_len);  // exclusive
   const int h_base = g * a.G + hc * 16;
   const int n_heads = min(16, a.G - hc * 16);
   const int64_t q_row = a.varlen_q ? sv.q_row0 : (int64_t)b;
@@ -109,12 +115,13 @@ __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a)
   // ahead, so no K/V load waits on the block table.
   u32x4 kreg[8], vreg[8];
   int blk[8];
+  auto key_of = [&](int v) { return v < ns ? v : lo_all + (v - ns); };
   auto fetch_blk = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       blk[i] = 0;
       if (MODE == KV_PAGED) {
-        const int j = min(j0 + 8 * i + (lane >> 3), s_hi - 1);
+        const int j = key_of(min(j0 + 8 * i + (lane >> 3), s_hi - 1));
         blk[i] = a.seq.block_table[(int64_t)b * a.seq.max_blocks + (j >> a.seq.log2_block)];
       }
     }
@@ -122,7 +129,7 @@ __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a)
   auto load = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int j = min(j0 + 8 * i + (lane >> 3), s_hi - 1);
+      const int j = key_of(min(j0 + 8 * i + (lane >> 3), s_hi - 1));
       int64_t row;
       if (MODE == KV_PAGED) {
         const int bb = min(max(blk[i], 0), a.seq.num_blocks - 1);

@@ -3,7 +3,8 @@
 //
 // Same definition as the bf16 kernels (sink + window causal GQA attention of
 // «GPT-OSS vs Qwen3», sections "Introduction de Grouped Query Attention",
-// "Utilisation de Sliding Window Attention" and "Attention Bias et Sinks"), but
+// "Utilisation de Sliding Window Attention" and "Attention Bias et Sinks", with
+// optional start-of-sequence sink tokens kept visible past the window), but
 // every product, exponential and sum is fp32 and nothing is rounded to bf16.
 // One wave owns one (query row, query head): per 64-key chunk each lane scores
 // one key (64-term fp32 dot product), the wave takes the online-softmax step,
@@ -30,6 +31,10 @@ __global__ __launch_bounds__(64) void attn_fp32_kernel(Fp32Args a) {
   const int p = sv.kv_len - sv.q_len + t;
   const int W = a.window;
   const int lo = W > 0 ? max(0, p - W + 1) : 0;
+  // keys visited: the sink tokens below the window, then the window itself,
+  // numbered 0 .. nv-1 ("virtual" index v -> key v, or lo + v - ns)
+  const int ns = W > 0 ? min(a.sink_tokens, lo) : 0;
+  const int nv = ns + (p - lo + 1);
   const int64_t qrow = sv.q_row0 + t;
   const int64_t kv_stride = (int64_t)a.Hkv * kHeadDim;
 
@@ -40,11 +45,13 @@ __global__ __launch_bounds__(64) void attn_fp32_kernel(Fp32Args a) {
   float acc = 0.f;
   __syncthreads();
 
-  for (int j0 = lo; j0 <= p; j0 += 64) {
-    const int j = j0 + lane;
+  for (int v0 = 0; v0 < nv; v0 += 64) {
+    const int vi = v0 + lane;
+    const bool live = vi < nv;
+    const int j = vi < ns ? vi : lo + (vi - ns);
     float x = -INFINITY;
     int64_t row = 0;
-    if (j <= p) {
+    if (live) {
       row = kv_row<MODE>(a.seq, sv, j);
       const float* kp = a.k + row * kv_stride + g * kHeadDim;
       float dot = 0.f;
@@ -54,14 +61,14 @@ __global__ __launch_bounds__(64) void attn_fp32_kernel(Fp32Args a) {
     const float mx = wave_max(x);
     const float m_new = fmaxf(m_run, mx);
     const float alpha = exp2f(m_run - m_new);
-    const float pj = (j <= p) ? exp2f(x - m_new) : 0.f;
+    const float pj = live ? exp2f(x - m_new) : 0.f;
     l_run = l_run * alpha + wave_sum(pj);
     acc *= alpha;
     m_run = m_new;
     ps[lane] = pj;
     rows[lane] = row;
     __syncthreads();
-    const int n = min(64, p - j0 + 1);
+    const int n = min(64, nv - v0);
     for (int jj = 0; jj < n; ++jj) acc = __builtin_fmaf(ps[jj], a.v[rows[jj] * kv_stride + g * kHeadDim + lane], acc);
     __syncthreads();
   }

@@ -17,6 +17,7 @@ struct PrefillArgs {
   SeqArgs seq;
   int B, Hq, Hkv, G;
   int window;
+  int sink_tokens;   // first positions that stay visible past the window (window > 0)
   float scale_log2;  // softmax scale times log2(e)
   int wg_per_seq;    // workgroups per (sequence, KV head)
   int skip_single;   // sequences with q_len == 1 are left to the decode kernel
@@ -37,6 +38,7 @@ struct DecodeArgs {
   SeqArgs seq;
   int B, Hq, Hkv, G, n_hc;
   int window;
+  int sink_tokens;   // first positions that stay visible past the window (window > 0)
   float scale_log2;
   int n_splits;
   int split_len;     // keys per split, a multiple of 64
@@ -60,6 +62,7 @@ struct Fp32Args {
   SeqArgs seq;
   int B, Hq, Hkv, G;
   int window;
+  int sink_tokens;   // first positions that stay visible past the window (window > 0)
   float scale_log2;
   int max_q_len;
   int varlen_q;

@@ -132,14 +132,20 @@ __device__ __forceinline__ void pv_half(f32x16 (&o)[2][2], const __bf16* vs, con
 }
 
 // Mask of one N-tile on key half h.  Lane holds keys
-// j0 + 32h + 8*(r/4) + 4*lg + r%4 of query row lr; the key is visible iff
-// (key - j0 - 4lg) lies in (dl, dh] (dl only counts with a window).  The half
-// is classified with wave-uniform bounds first: wholly visible is left alone,
-// wholly hidden is cleared, and only a half that the causal diagonal or the
-// window edge crosses is compared element by element.
-__device__ __forceinline__ void mask_half(f32x16& s, int h, int j0, int plo, int phi, int W, int dh, int dl) {
+// j0 + 32h + 8*(r/4) + 4*lg + r%4 of query row lr; with off = 32h + 8*(r/4) +
+// r%4 the key is visible iff off <= dh (causal) and, on a windowed layer,
+// off > dl (inside the window) or off < ds (one of the first st positions, the
+// start-of-sequence sink tokens).  dh, dl, ds are per-lane bounds, so the
+// per-register offsets stay compile-time constants.  The half is classified
+// with wave-uniform bounds first: wholly visible is left alone, wholly hidden
+// is cleared, and only a half that the causal diagonal or the window edge
+// crosses is compared element by element.
+__device__ __forceinline__ void mask_half(f32x16& s, int h, int j0, int plo, int phi, int W, int st, int dh, int dl,
+                                          int ds) {
   const int kb = j0 + 32 * h;  // first key of this half (uniform)
-  if (kb > phi || (W > 0 && kb + 31 <= plo - W)) {
+  const bool any_sink = kb < st;
+  const bool all_sink = kb + 31 < st;
+  if (kb > phi || (W > 0 && !any_sink && kb + 31 <= plo - W)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = -INFINITY;
     return;
@@ -149,10 +155,18 @@ __device__ __forceinline__ void mask_half(f32x16& s, int h, int j0, int plo, int
     for (int r = 0; r < 16; ++r)
       if (32 * h + 8 * (r >> 2) + (r & 3) > dh) s[r] = -INFINITY;
   }
-  if (W > 0 && kb <= phi - W) {  // window edge crosses this half
+  if (W > 0 && !all_sink && kb <= phi - W) {  // window edge crosses this half
+    if (any_sink) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (32 * h + 8 * (r >> 2) + (r & 3) <= dl) s[r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        const int off = 32 * h + 8 * (r >> 2) + (r & 3);
+        if (off <= dl && off >= ds) s[r] = -INFINITY;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (32 * h + 8 * (r >> 2) + (r & 3) <= dl) s[r] = -INFINITY;
+    }
   }
 }
 
@@ -205,14 +219,14 @@ __device__ __forceinline__ void fence_schedule() { __builtin_amdgcn_sched_barrie
 // by the returned alpha (the row sum is rescaled here).
 __device__ __forceinline__ float refit_half(f32x16& s, bf16x8 (&pb)[2], float& m, float& l, float& alpha,
                                             const __bf16* ks, const bf16x8 (&qb)[4], int h, int lr, int lg, float c,
-                                            int j0, int plo, int phi, int W, int dh, int dl) {
+                                            int j0, int plo, int phi, int W, int st, int dh, int dl, int ds) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + (32 * h + lr) * RS + kchunk(2 * k + lg, lr));
     s = mfma32(ka, qb[k], k == 0 ? zero16() : s);
     __builtin_amdgcn_sched_barrier(0);
   }
-  mask_half(s, h, j0, plo, phi, W, dh, dl);
+  mask_half(s, h, j0, plo, phi, W, st, dh, dl, ds);
   float mx = s[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
@@ -288,7 +302,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   const int lo = W > 0 ? max(0, p_min - W + 1) : 0;
   const int hi = min(p_max, sv.kv_len - 1);  // inclusive
   const int j_begin = lo & ~(BK - 1);
-  const int n_tiles = hi >= j_begin ? (hi - j_begin) / BK + 1 : 0;
+  // Start-of-sequence sink tokens below the window: their tiles come first
+  // (tile t < n_st starts at key BK*t), then the window's tiles.
+  const int st = W > 0 ? a.sink_tokens : 0;
+  const int n_st = (min(st, j_begin) + BK - 1) / BK;
+  const int n_tiles = n_st + (hi >= j_begin ? (hi - j_begin) / BK + 1 : 0);
+  auto tile_j0 = [&](int t) { return t < n_st ? BK * t : j_begin + BK * (t - n_st); };
 
   // ---- Q^T operands (B of S^T = K Q^T): lane holds row lr, d = 16*k + 8*lg .. +7
   bf16x8 qb[2][4];
@@ -330,7 +349,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
     for (int i = 0; i < 2; ++i) {
       blk[i] = 0;
       if (MODE == KV_PAGED) {
-        const int j = min(j_begin + BK * t + 16 * wave + 8 * i + (lane >> 3), hi);
+        const int j = min(tile_j0(t) + 16 * wave + 8 * i + (lane >> 3), hi);
         blk[i] = a.seq.block_table[(int64_t)b * a.seq.max_blocks + (j >> a.seq.log2_block)];
       }
     }
@@ -338,7 +357,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   auto dma_tile = [&](int t, const int (&blk)[2], int buf) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int j = min(j_begin + BK * t + 16 * wave + 8 * i + (lane >> 3), hi);
+      const int j = min(tile_j0(t) + 16 * wave + 8 * i + (lane >> 3), hi);
       int64_t row;
       if (MODE == KV_PAGED) {
         const int bb = min(max(blk[i], 0), a.seq.num_blocks - 1);
@@ -393,17 +412,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
     auto body = [&](auto mask_tag, int t) {
       constexpr bool MASK = decltype(mask_tag)::value;
       const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
-      const int j0 = j_begin + BK * t;
+      const int j0 = tile_j0(t);
       const bool has_next = t + 1 < n_tiles;
       const int dh0 = pos0[0] + lr - j0 - 4 * lg, dh1 = pos0[1] + lr - j0 - 4 * lg;
       const int dl0 = W > 0 ? dh0 - W : -0x40000000, dl1 = W > 0 ? dh1 - W : -0x40000000;
+      const int ds = st - j0 - 4 * lg;  // off < ds: a sink token
       bf16x8 pA0[2], pA1[2], pB0[2], pB1[2];
       // (a): the four k-steps of the half-1 scores, each followed by a quarter
       // of the half-0 exponentials (the order is pinned so that every MFMA
       // pair runs while the vector work after it issues)
       if (MASK) {
-        mask_half(sA[0], 0, j0, pos0[0], phi[0], W, dh0, dl0);
-        mask_half(sA[1], 0, j0, pos0[1], phi[1], W, dh1, dl1);
+        mask_half(sA[0], 0, j0, pos0[0], phi[0], W, st, dh0, dl0, ds);
+        mask_half(sA[1], 0, j0, pos0[1], phi[1], W, st, dh1, dl1, ds);
       }
       float r0 = 0.f, r1 = 0.f;
       {
@@ -426,8 +446,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
         const bool f0 = __builtin_amdgcn_ballot_w64(r0 > kRefit) != 0;
         const bool f1 = __builtin_amdgcn_ballot_w64(r1 > kRefit) != 0;
         float al0 = 1.f, al1 = 1.f;
-        if (f0) r0 = refit_half(sA[0], pA0, m_run[0], l_run[0], al0, Ks[cur], qb[0], 0, lr, lg, c, j0, pos0[0], phi[0], W, dh0, dl0);
-        if (f1) r1 = refit_half(sA[1], pA1, m_run[1], l_run[1], al1, Ks[cur], qb[1], 0, lr, lg, c, j0, pos0[1], phi[1], W, dh1, dl1);
+        if (f0) r0 = refit_half(sA[0], pA0, m_run[0], l_run[0], al0, Ks[cur], qb[0], 0, lr, lg, c, j0, pos0[0], phi[0], W, st, dh0, dl0, ds);
+        if (f1) r1 = refit_half(sA[1], pA1, m_run[1], l_run[1], al1, Ks[cur], qb[1], 0, lr, lg, c, j0, pos0[1], phi[1], W, st, dh1, dl1, ds);
         if (f0) { o[0][0] *= al0; o[0][1] *= al0; }
         if (f1) { o[1][0] *= al1; o[1][1] *= al1; }
       }
@@ -436,8 +456,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
       // (b): P V over key half 0 in four steps, each followed by a quarter of
       // the half-1 exponentials
       if (MASK) {
-        mask_half(sB[0], 1, j0, pos0[0], phi[0], W, dh0, dl0);
-        mask_half(sB[1], 1, j0, pos0[1], phi[1], W, dh1, dl1);
+        mask_half(sB[0], 1, j0, pos0[0], phi[0], W, st, dh0, dl0, ds);
+        mask_half(sB[1], 1, j0, pos0[1], phi[1], W, st, dh1, dl1, ds);
       }
       r0 = 0.f;
       r1 = 0.f;
@@ -461,8 +481,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
         const bool f0 = __builtin_amdgcn_ballot_w64(r0 > kRefit) != 0;
         const bool f1 = __builtin_amdgcn_ballot_w64(r1 > kRefit) != 0;
         float al0 = 1.f, al1 = 1.f;
-        if (f0) r0 = refit_half(sB[0], pB0, m_run[0], l_run[0], al0, Ks[cur], qb[0], 1, lr, lg, c, j0, pos0[0], phi[0], W, dh0, dl0);
-        if (f1) r1 = refit_half(sB[1], pB1, m_run[1], l_run[1], al1, Ks[cur], qb[1], 1, lr, lg, c, j0, pos0[1], phi[1], W, dh1, dl1);
+        if (f0) r0 = refit_half(sB[0], pB0, m_run[0], l_run[0], al0, Ks[cur], qb[0], 1, lr, lg, c, j0, pos0[0], phi[0], W, st, dh0, dl0, ds);
+        if (f1) r1 = refit_half(sB[1], pB1, m_run[1], l_run[1], al1, Ks[cur], qb[1], 1, lr, lg, c, j0, pos0[1], phi[1], W, st, dh1, dl1, ds);
         if (f0) { o[0][0] *= al0; o[0][1] *= al0; }
         if (f1) { o[1][0] *= al1; o[1][1] *= al1; }
       }
@@ -477,15 +497,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
       if (has_next) qk_half(sA[0], sA[1], Ks[nxt], qb, 0, lr, lg);
       cur = nxt;
     };
-    // The tiles that need no mask for either of this wave's N-tiles form one
-    // run [pb, pe): past the window edge of the last row and before the
-    // causal diagonal of the first row.  Three loops, one body each.
+    // The window tiles that need no mask for either of this wave's N-tiles
+    // form one run [pb, pe): past the window edge of the last row and before
+    // the causal diagonal of the first row.  Three loops, one body each (the
+    // sink tiles lead the first).
     const int p_first = min(pos0[0], pos0[1]);
     const int p_last = max(phi[0], phi[1]);
     const int t_lo = W > 0 ? max(0, (p_last - W - j_begin + BK) / BK) : 0;  // first t with j0 > p_last - W
     const int t_hi = p_first - j_begin - (BK - 1) >= 0 ? (p_first - j_begin - (BK - 1)) / BK : -1;  // last t with j0 + 63 <= p_first
-    const int pb = min(t_lo, n_tiles);
-    const int pe = max(pb, min(t_hi + 1, n_tiles));
+    const int n_wt = n_tiles - n_st;  // window tiles; the sink tiles all take the masked body
+    const int pb = n_st + min(t_lo, n_wt);
+    const int pe = max(pb, n_st + min(t_hi + 1, n_wt));
     std::true_type MSK;
     std::false_type PLN;
     for (int t = 0; t < pb; ++t) body(MSK, t);

@@ -3,8 +3,10 @@
 A step is one pass over every stage of the path, on seeded synthetic inputs
 already resident in HBM:
   1. layer-shaped prefill  B1 S4096, 64 query / 8 KV heads, D64, bf16 -- one
-     dense layer, then one 128-token sliding-window layer;
-  2. batched decode        B64, cache 8192, same heads -- dense, then window 128;
+     dense layer, one 128-token sliding-window layer, and one windowed layer
+     that keeps 4 start-of-sequence sink tokens visible;
+  2. batched decode        B64, cache 8192, same heads -- dense, window 128,
+     window 128 with 4 sink tokens;
   3. ragged + paged        16 sequences, lengths U{128..8192}, 512-token
      prefill chunks and single-token decode steps, 16-token pages under a
      permuted block table -- dense, then window 128;
@@ -59,8 +61,19 @@ def prefill_work(B, S, Hq, Hkv, D, window, elt=2):
     return flop, byts
 
 
-def decode_work(seqlens, Hq, Hkv, D, window, elt=2):
-    n_read = [min(L, window) if window > 0 else L for L in seqlens]
+def prefill_work_sink_tokens(B, S, Hq, Hkv, D, window, n_sink, elt=2):
+    """Work of a windowed prefill whose first n_sink positions stay visible."""
+    import numpy as np
+
+    p = np.arange(S, dtype=np.int64)
+    keys = np.minimum(window, p + 1) + np.minimum(n_sink, np.maximum(0, p - window + 1))
+    flop = 4 * D * Hq * B * int(keys.sum())
+    byts = elt * (2 * B * S * Hq * D + 2 * B * S * Hkv * D)
+    return flop, byts
+
+
+def decode_work(seqlens, Hq, Hkv, D, window, elt=2, n_sink=0):
+    n_read = [(min(L, window) + min(n_sink, max(0, L - window))) if window > 0 else L for L in seqlens]
     flop = 4 * D * Hq * sum(n_read)
     byts = elt * (2 * sum(n_read) * Hkv * D + 2 * len(seqlens) * Hq * D)
     return flop, byts
@@ -257,6 +270,11 @@ def add_prefill(stages, gq, p, up, f32, dev):
         fl, by = prefill_work(B, S, Hq, Hkv, D, W)
         stages[name] = dict(fn=(lambda W=W: gq.attn_prefill(pq, pk, pv, ps, window=W, out=pout)), flop=fl, bytes=by,
                             bound="mfma" if W == 0 else "hbm")
+    # windowed layer with 4 start-of-sequence sink tokens kept visible
+    fl, by = prefill_work_sink_tokens(B, S, Hq, Hkv, D, 128, 4)
+    stages["prefill_swa128_sink4"] = dict(
+        fn=(lambda: gq.attn_prefill(pq, pk, pv, ps, window=128, sink_tokens=4, out=pout)), flop=fl, bytes=by,
+        bound="hbm")
 
 
 def add_decode(stages, gq, d, up, i32, f32, dev):
@@ -271,6 +289,12 @@ def add_decode(stages, gq, d, up, i32, f32, dev):
         ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
         stages[name] = dict(fn=(lambda W=W, ws=ws: gq.attn_decode(dq, (dk, dv), dsl, ds, window=W, workspace=ws)),
                             flop=fl, bytes=by, bound="hbm")
+    fl, by = decode_work([int(x) for x in d.seqlens], Hq, Hkv, D, 128, n_sink=4)
+    nbytes = gq.decode_workspace_size(Bd, Ld, Hq, Hkv, D, 128, sink_tokens=4)
+    ws4 = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+    stages["decode_swa128_sink4"] = dict(
+        fn=(lambda: gq.attn_decode(dq, (dk, dv), dsl, ds, window=128, sink_tokens=4, workspace=ws4)),
+        flop=fl, bytes=by, bound="hbm")
 
 
 def add_varlen(stages, gq, r, up, i32, f32, dev):

@@ -11,7 +11,7 @@
  *                                         Architecture MoE & Résumé du Model
  *                                         Card», §3.3 (64 query heads over 8
  *                                         KV heads, 8 per KV head).
- *   J = { j : j <= p, and j > p - W when W > 0 }
+ *   J = { j : j <= p, and (j > p - W or j < n_sink) when W > 0 }
  *                                      -- causal (decoder-only, autoregressive:
  *                                         «OpenAI lance gpt-oss-20b, qui tient
  *                                         sur 16 Go», opening section); a
@@ -20,6 +20,13 @@
  *                                         («GPT-OSS vs Qwen3», section
  *                                         "Utilisation de Sliding Window
  *                                         Attention": the last 128 tokens).
+ *                                         n_sink ("sink_tokens") keeps the
+ *                                         first positions visible past the
+ *                                         window edge: the classical
+ *                                         start-of-sequence sink tokens of
+ *                                         «GPT-OSS vs Qwen3», section
+ *                                         "Attention Bias et Sinks" (0 = none;
+ *                                         no effect on dense layers).
  *   x_j = scale * <q, k_j[g]>,  s = sinks[h]
  *   o   = sum_{j in J} e^{x_j} v_j[g] / (e^{s} + sum_{j in J} e^{x_j})
  *   lse = ln(e^{s} + sum_{j in J} e^{x_j})
@@ -44,7 +51,8 @@
  *   - lse: optional fp32 output (NULL = not written), natural-log units.
  *   - head_dim D must be 64; Hq must be a positive multiple of Hkv.
  *   - window: 0 = dense causal; W > 0 = the W most recent keys; W < 0 is an
- *     error.
+ *     error.  sink_tokens: >= 0 positions at the start of every sequence that
+ *     windowed layers keep visible; negative is an error.
  *   - scale: scale > 0 is used as given; scale == 0 selects 1/sqrt(D); a
  *     negative or NaN scale is an error.
  *   - stream: a hipStream_t (NULL = the default stream).  Every launch is
@@ -96,7 +104,7 @@ const char* gqa_attn_last_error(void);
 int gqa_attn_prefill(const void* q, const void* k, const void* v, const float* sinks,
                      void* out, float* lse,
                      int B, int S, int Hq, int Hkv, int D,
-                     int window, float scale, int dtype, void* stream);
+                     int window, int sink_tokens, float scale, int dtype, void* stream);
 
 /*
  * Decode: one new query token per sequence against a contiguous KV cache.
@@ -106,16 +114,17 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, const float* s
  *   lse [B, Hq] fp32 (optional)
  * The sequence is split over up to `gqa_attn_decode_workspace_size`-sized
  * partials; pass a workspace of at least that many bytes (may be NULL when
- * that size is 0).  On windowed layers only the last W positions are read.
+ * that size is 0).  On windowed layers only the last W positions (and the
+ * sink tokens below them) are read.
  */
 size_t gqa_attn_decode_workspace_size(int B, int Lmax, int Hq, int Hkv, int D,
-                                      int window, int dtype);
+                                      int window, int sink_tokens, int dtype);
 
 int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* seqlens, const float* sinks,
                     void* out, float* lse,
                     int B, int Lmax, int Hq, int Hkv, int D,
-                    int window, float scale, int dtype,
+                    int window, int sink_tokens, float scale, int dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -140,7 +149,7 @@ int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
  *   lse [Hq, Tq] fp32 (optional).
  */
 size_t gqa_attn_varlen_workspace_size(int B, int max_q_len, int max_kv_len, int Hq, int Hkv,
-                                      int D, int window, int dtype);
+                                      int D, int window, int sink_tokens, int dtype);
 
 int gqa_attn_varlen_paged(const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
@@ -149,7 +158,7 @@ int gqa_attn_varlen_paged(const void* q, const void* k_cache, const void* v_cach
                           const float* sinks, void* out, float* lse,
                           int B, int Tq, int max_q_len, int max_kv_len,
                           int Hq, int Hkv, int D,
-                          int window, float scale, int dtype,
+                          int window, int sink_tokens, float scale, int dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*

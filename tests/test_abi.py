@@ -29,7 +29,7 @@ def L():
 
 
 def test_library_loads(L):
-    assert L.gqa_attn_version() == 200
+    assert L.gqa_attn_version() == 300
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -48,8 +48,9 @@ def test_status_strings(L):
     assert L.gqa_attn_status_string(-99) == b"GQA_ERR_UNKNOWN"
 
 
-def prefill(L, q=DUMMY, k=DUMMY, v=DUMMY, out=DUMMY, B=1, S=16, Hq=64, Hkv=8, D=64, window=0, scale=0.0, dt=0):
-    return L.gqa_attn_prefill(q, k, v, None, out, None, B, S, Hq, Hkv, D, window, scale, dt, None)
+def prefill(L, q=DUMMY, k=DUMMY, v=DUMMY, out=DUMMY, B=1, S=16, Hq=64, Hkv=8, D=64, window=0, scale=0.0, dt=0,
+            sink_tokens=0):
+    return L.gqa_attn_prefill(q, k, v, None, out, None, B, S, Hq, Hkv, D, window, sink_tokens, scale, dt, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -59,6 +60,8 @@ def prefill(L, q=DUMMY, k=DUMMY, v=DUMMY, out=DUMMY, B=1, S=16, Hq=64, Hkv=8, D=
     (dict(Hq=0), -1),
     (dict(Hkv=-1), -1),
     (dict(window=-1), -1),
+    (dict(sink_tokens=-1), -1),
+    (dict(window=128, sink_tokens=-4), -1),
     (dict(scale=float("nan")), -1),
     (dict(scale=-0.5), -1),
     (dict(dt=7), -2),
@@ -79,22 +82,27 @@ def test_prefill_empty_is_noop(L):
     assert L.gqa_attn_last_error() == b""
 
 
-def decode(L, ws=None, ws_bytes=0, seqlens=DUMMY, B=64, Lmax=8192, Hq=64, Hkv=8, D=64, window=0, dt=0):
-    return L.gqa_attn_decode(DUMMY, DUMMY, DUMMY, seqlens, None, DUMMY, None, B, Lmax, Hq, Hkv, D, window, 0.0, dt,
-                             ws, ws_bytes, None)
+def decode(L, ws=None, ws_bytes=0, seqlens=DUMMY, B=64, Lmax=8192, Hq=64, Hkv=8, D=64, window=0, dt=0,
+           sink_tokens=0):
+    return L.gqa_attn_decode(DUMMY, DUMMY, DUMMY, seqlens, None, DUMMY, None, B, Lmax, Hq, Hkv, D, window, sink_tokens,
+                             0.0, dt, ws, ws_bytes, None)
 
 
 def test_decode_workspace_rules(L):
     # a long single-batch decode is split, so it needs a workspace
-    need = L.gqa_attn_decode_workspace_size(8, 131072, 64, 8, 64, 0, 0)
+    need = L.gqa_attn_decode_workspace_size(8, 131072, 64, 8, 64, 0, 0, 0)
     assert need > 0 and need % 4 == 0
     assert decode(L, B=8, Lmax=131072) == -3
     assert decode(L, ws=DUMMY, ws_bytes=need - 4, B=8, Lmax=131072) == -3
     # fp32 and invalid shapes need none
-    assert L.gqa_attn_decode_workspace_size(8, 131072, 64, 8, 64, 0, 1) == 0
-    assert L.gqa_attn_decode_workspace_size(8, 131072, 64, 8, 32, 0, 0) == 0
+    assert L.gqa_attn_decode_workspace_size(8, 131072, 64, 8, 64, 0, 0, 1) == 0
+    assert L.gqa_attn_decode_workspace_size(8, 131072, 64, 8, 32, 0, 0, 0) == 0
+    assert L.gqa_attn_decode_workspace_size(8, 131072, 64, 8, 64, 128, -1, 0) == 0
     # a sliding window caps the work per sequence: never more partials than dense
-    assert L.gqa_attn_decode_workspace_size(8, 131072, 64, 8, 64, 128, 0) <= need
+    assert L.gqa_attn_decode_workspace_size(8, 131072, 64, 8, 64, 128, 0, 0) <= need
+    # sink tokens add keys to a windowed layer's range (never beyond the dense plan)
+    assert L.gqa_attn_decode_workspace_size(8, 131072, 64, 8, 64, 4096, 0, 0) <= \
+        L.gqa_attn_decode_workspace_size(8, 131072, 64, 8, 64, 4096, 60000, 0) <= need
 
 
 def test_decode_rejects(L):
@@ -102,17 +110,18 @@ def test_decode_rejects(L):
     assert decode(L, D=80) == -2
     assert decode(L, Lmax=0) == -1
     assert decode(L, window=-5) == -1
+    assert decode(L, window=128, sink_tokens=-1) == -1
     assert decode(L, B=0) == 0
 
 
 def varlen(L, table=DUMMY, cu_k=None, bs=16, maxblk=512, nblk=100, B=16, Tq=100, mq=64, mk=8192, window=0,
            cu_q=DUMMY, ws=None, ws_bytes=0, D=64):
     return L.gqa_attn_varlen_paged(DUMMY, DUMMY, DUMMY, cu_q, DUMMY, table, maxblk, bs, cu_k, nblk, None, DUMMY, None,
-                                   B, Tq, mq, mk, 64, 8, D, window, 0.0, 0, ws, ws_bytes, None)
+                                   B, Tq, mq, mk, 64, 8, D, window, 0, 0.0, 0, ws, ws_bytes, None)
 
 
 def test_varlen_rejects(L):
-    need = L.gqa_attn_varlen_workspace_size(16, 64, 8192, 64, 8, 64, 0, 0)
+    need = L.gqa_attn_varlen_workspace_size(16, 64, 8192, 64, 8, 64, 0, 0, 0)
     assert varlen(L, bs=12, ws=DUMMY, ws_bytes=need) == -2          # block size not a power of two
     assert varlen(L, bs=2048, ws=DUMMY, ws_bytes=need) == -2
     assert varlen(L, table=None, cu_k=None) == -1                 # packed needs cu_seqlens_k
