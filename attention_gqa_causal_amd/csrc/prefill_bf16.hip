@@ -140,11 +140,12 @@ __device__ __forceinline__ void pv_half(f32x16 (&o)[2][2], const __bf16* vs, con
 // with wave-uniform bounds first: wholly visible is left alone, wholly hidden
 // is cleared, and only a half that the causal diagonal or the window edge
 // crosses is compared element by element.
+template <bool STK>
 __device__ __forceinline__ void mask_half(f32x16& s, int h, int j0, int plo, int phi, int W, int st, int dh, int dl,
                                           int ds) {
   const int kb = j0 + 32 * h;  // first key of this half (uniform)
-  const bool any_sink = kb < st;
-  const bool all_sink = kb + 31 < st;
+  const bool any_sink = STK && kb < st;
+  const bool all_sink = STK && kb + 31 < st;
   if (kb > phi || (W > 0 && !any_sink && kb + 31 <= plo - W)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = -INFINITY;
@@ -217,6 +218,7 @@ __device__ __forceinline__ void fence_schedule() { __builtin_amdgcn_sched_barrie
 // when there is no sink).  Recompute the half's scores, move the reference to
 // the true running max, and redo the weights; the caller rescales the output
 // by the returned alpha (the row sum is rescaled here).
+template <bool STK>
 __device__ __forceinline__ float refit_half(f32x16& s, bf16x8 (&pb)[2], float& m, float& l, float& alpha,
                                             const __bf16* ks, const bf16x8 (&qb)[4], int h, int lr, int lg, float c,
                                             int j0, int plo, int phi, int W, int st, int dh, int dl, int ds) {
@@ -226,7 +228,7 @@ __device__ __forceinline__ float refit_half(f32x16& s, bf16x8 (&pb)[2], float& m
     s = mfma32(ka, qb[k], k == 0 ? zero16() : s);
     __builtin_amdgcn_sched_barrier(0);
   }
-  mask_half(s, h, j0, plo, phi, W, st, dh, dl, ds);
+  mask_half<STK>(s, h, j0, plo, phi, W, st, dh, dl, ds);
   float mx = s[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
@@ -239,7 +241,9 @@ __device__ __forceinline__ float refit_half(f32x16& s, bf16x8 (&pb)[2], float& m
   return exp_half(s, pb, m, c);
 }
 
-template <int MODE, bool VARLEN>
+// STK: the layer keeps start-of-sequence sink tokens visible past its window
+// (a separate instantiation, so that other layers carry none of its code).
+template <int MODE, bool VARLEN, bool STK>
 __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 Ks[NBUF][BK * RS];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[NBUF][BK * RS];
@@ -304,8 +308,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   const int j_begin = lo & ~(BK - 1);
   // Start-of-sequence sink tokens below the window: their tiles come first
   // (tile t < n_st starts at key BK*t), then the window's tiles.
-  const int st = W > 0 ? a.sink_tokens : 0;
-  const int n_st = (min(st, j_begin) + BK - 1) / BK;
+  const int st = STK && W > 0 ? a.sink_tokens : 0;
+  const int n_st = STK ? (min(st, j_begin) + BK - 1) / BK : 0;
   const int n_tiles = n_st + (hi >= j_begin ? (hi - j_begin) / BK + 1 : 0);
   auto tile_j0 = [&](int t) { return t < n_st ? BK * t : j_begin + BK * (t - n_st); };
 
@@ -416,14 +420,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
       const bool has_next = t + 1 < n_tiles;
       const int dh0 = pos0[0] + lr - j0 - 4 * lg, dh1 = pos0[1] + lr - j0 - 4 * lg;
       const int dl0 = W > 0 ? dh0 - W : -0x40000000, dl1 = W > 0 ? dh1 - W : -0x40000000;
-      const int ds = st - j0 - 4 * lg;  // off < ds: a sink token
+      const int ds = STK ? st - j0 - 4 * lg : 0;  // off < ds: a sink token
       bf16x8 pA0[2], pA1[2], pB0[2], pB1[2];
       // (a): the four k-steps of the half-1 scores, each followed by a quarter
       // of the half-0 exponentials (the order is pinned so that every MFMA
       // pair runs while the vector work after it issues)
       if (MASK) {
-        mask_half(sA[0], 0, j0, pos0[0], phi[0], W, st, dh0, dl0, ds);
-        mask_half(sA[1], 0, j0, pos0[1], phi[1], W, st, dh1, dl1, ds);
+        mask_half<STK>(sA[0], 0, j0, pos0[0], phi[0], W, st, dh0, dl0, ds);
+        mask_half<STK>(sA[1], 0, j0, pos0[1], phi[1], W, st, dh1, dl1, ds);
       }
       float r0 = 0.f, r1 = 0.f;
       {
@@ -446,8 +450,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
         const bool f0 = __builtin_amdgcn_ballot_w64(r0 > kRefit) != 0;
         const bool f1 = __builtin_amdgcn_ballot_w64(r1 > kRefit) != 0;
         float al0 = 1.f, al1 = 1.f;
-        if (f0) r0 = refit_half(sA[0], pA0, m_run[0], l_run[0], al0, Ks[cur], qb[0], 0, lr, lg, c, j0, pos0[0], phi[0], W, st, dh0, dl0, ds);
-        if (f1) r1 = refit_half(sA[1], pA1, m_run[1], l_run[1], al1, Ks[cur], qb[1], 0, lr, lg, c, j0, pos0[1], phi[1], W, st, dh1, dl1, ds);
+        if (f0) r0 = refit_half<STK>(sA[0], pA0, m_run[0], l_run[0], al0, Ks[cur], qb[0], 0, lr, lg, c, j0, pos0[0], phi[0], W, st, dh0, dl0, ds);
+        if (f1) r1 = refit_half<STK>(sA[1], pA1, m_run[1], l_run[1], al1, Ks[cur], qb[1], 0, lr, lg, c, j0, pos0[1], phi[1], W, st, dh1, dl1, ds);
         if (f0) { o[0][0] *= al0; o[0][1] *= al0; }
         if (f1) { o[1][0] *= al1; o[1][1] *= al1; }
       }
@@ -456,8 +460,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
       // (b): P V over key half 0 in four steps, each followed by a quarter of
       // the half-1 exponentials
       if (MASK) {
-        mask_half(sB[0], 1, j0, pos0[0], phi[0], W, st, dh0, dl0, ds);
-        mask_half(sB[1], 1, j0, pos0[1], phi[1], W, st, dh1, dl1, ds);
+        mask_half<STK>(sB[0], 1, j0, pos0[0], phi[0], W, st, dh0, dl0, ds);
+        mask_half<STK>(sB[1], 1, j0, pos0[1], phi[1], W, st, dh1, dl1, ds);
       }
       r0 = 0.f;
       r1 = 0.f;
@@ -481,8 +485,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
         const bool f0 = __builtin_amdgcn_ballot_w64(r0 > kRefit) != 0;
         const bool f1 = __builtin_amdgcn_ballot_w64(r1 > kRefit) != 0;
         float al0 = 1.f, al1 = 1.f;
-        if (f0) r0 = refit_half(sB[0], pB0, m_run[0], l_run[0], al0, Ks[cur], qb[0], 1, lr, lg, c, j0, pos0[0], phi[0], W, st, dh0, dl0, ds);
-        if (f1) r1 = refit_half(sB[1], pB1, m_run[1], l_run[1], al1, Ks[cur], qb[1], 1, lr, lg, c, j0, pos0[1], phi[1], W, st, dh1, dl1, ds);
+        if (f0) r0 = refit_half<STK>(sB[0], pB0, m_run[0], l_run[0], al0, Ks[cur], qb[0], 1, lr, lg, c, j0, pos0[0], phi[0], W, st, dh0, dl0, ds);
+        if (f1) r1 = refit_half<STK>(sB[1], pB1, m_run[1], l_run[1], al1, Ks[cur], qb[1], 1, lr, lg, c, j0, pos0[1], phi[1], W, st, dh1, dl1, ds);
         if (f0) { o[0][0] *= al0; o[0][1] *= al0; }
         if (f1) { o[1][0] *= al1; o[1][1] *= al1; }
       }
@@ -550,14 +554,21 @@ int prefill_ntiles_per_wg() { return NT_WG; }
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int kv_mode, bool varlen_q, hipStream_t s) {
   const int grid = a.B * a.Hkv * a.wg_per_seq;
   if (grid <= 0) return hipSuccess;
+  const bool stk = a.window > 0 && a.sink_tokens > 0;
+#define GQA_LAUNCH(M, V)                                                                               \
+  do {                                                                                                 \
+    if (stk) hipLaunchKernelGGL((prefill_bf16_kernel<M, V, true>), dim3(grid), dim3(NTHREADS), 0, s, a); \
+    else hipLaunchKernelGGL((prefill_bf16_kernel<M, V, false>), dim3(grid), dim3(NTHREADS), 0, s, a);    \
+  } while (0)
   if (!varlen_q && kv_mode == KV_BATCHED)
-    hipLaunchKernelGGL((prefill_bf16_kernel<KV_BATCHED, false>), dim3(grid), dim3(NTHREADS), 0, s, a);
+    GQA_LAUNCH(KV_BATCHED, false);
   else if (varlen_q && kv_mode == KV_PAGED)
-    hipLaunchKernelGGL((prefill_bf16_kernel<KV_PAGED, true>), dim3(grid), dim3(NTHREADS), 0, s, a);
+    GQA_LAUNCH(KV_PAGED, true);
   else if (varlen_q && kv_mode == KV_PACKED)
-    hipLaunchKernelGGL((prefill_bf16_kernel<KV_PACKED, true>), dim3(grid), dim3(NTHREADS), 0, s, a);
+    GQA_LAUNCH(KV_PACKED, true);
   else
     return hipErrorInvalidValue;
+#undef GQA_LAUNCH
   return hipGetLastError();
 }
 
