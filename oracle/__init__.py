@@ -9,7 +9,8 @@ library and imports nothing from it.
 ``oracle.attention`` is the plain fp64 NumPy definition; ``oracle.brute`` is an
 independent pure-Python scalar enumeration of the same definition;
 ``oracle.ring`` is the W-slot ring cache of windowed layers (append by position,
-decode through the windowed definition).
+decode through the windowed definition); ``oracle.rope`` is the rotary position
+encoding of new tokens and their KV-cache append.
 
 Sources (the web pages this method is taken from):
 
@@ -50,6 +51,12 @@ from .attention import (  # noqa: F401
     probabilities,
     varlen_ref,
     visible_mask,
+)
+from .rope import (  # noqa: F401
+    default_inv_freq,
+    new_positions,
+    rope_append_ref,
+    rope_ref,
 )
 from .ring import (  # noqa: F401
     decode_ring_ref,
