@@ -9,6 +9,9 @@ Functions (names follow the C ABI in ``include/gqa_attn.h``):
 * ``attn_prefill(q, k, v, sinks, window=0, scale=None, sink_tokens=0)``
 * ``attn_decode(q, kv_cache, seqlens, sinks, window=0, scale=None, sink_tokens=0)``
 * ``attn_varlen_paged(q, kv_cache, block_table, cu_seqlens_q, seqlens_k, sinks, ...)``
+* ``rope_append(q, k, v, seqlens, kv_cache, inv_freq=None, ...)``: rotary
+  encoding of new rows fused with their KV-cache append (contiguous, paged or
+  ring cache); ``rope_inv_freq(D)`` is the default frequency table
 * ``kv_ring_append(k_new, v_new, kv_ring, seqlens, cu_seqlens_q=None)`` and
   ``attn_decode_ring(q, kv_ring, seqlens, sinks, scale=None)``: the W-slot ring
   cache of sliding-window layers (position p in slot p % W)
@@ -31,6 +34,8 @@ __all__ = [
     "attn_decode",
     "attn_varlen_paged",
     "kv_ring_append",
+    "rope_append",
+    "rope_inv_freq",
     "attn_decode_ring",
     "decode_workspace_size",
     "varlen_workspace_size",
@@ -80,6 +85,8 @@ _SIGNATURES = {
     "gqa_kv_ring_append": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "gqa_attn_decode_ring_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "gqa_attn_decode_ring": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "gqa_rope_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _I, _I, _P, _I, _I, _I,
+                             _I, _I, _I, _I, _I, _I, _P]),
 }
 
 
@@ -340,3 +347,66 @@ def attn_decode_ring(q, kv_ring, seqlens, sinks=None, scale=None, return_lse: bo
     _check(lib().gqa_attn_decode_ring(_ptr(q), _ptr(kr), _ptr(vr), _ptr(seqlens), _ptr(sinks), _ptr(out), _ptr(lse),
                                       B, W, Hq, Hkv, D, _scale(scale), dt, _ptr(workspace), ws_have, _stream(dev)))
     return (out, lse) if return_lse else out
+
+
+ROPE_INTERLEAVED = 0
+ROPE_HALVES = 1
+
+
+def rope_inv_freq(D: int = 64, base: float = 10000.0, device=None) -> torch.Tensor:
+    """The default RoPE frequency table θ_i = base^(-2i/D), i < D/2, fp32 (formed in fp64, rounded once)."""
+    i = torch.arange(D // 2, dtype=torch.float64)
+    t = (base ** (-2.0 * i / D)).to(torch.float32)
+    return t if device is None else t.to(device)
+
+
+def rope_append(q, k, v, seqlens, kv_cache, inv_freq=None, q_out=None, cu_seqlens_q=None, pairing=ROPE_INTERLEAVED,
+                mscale: float = 1.0, block_table=None, ring: bool = False):
+    """Rotate new rows' queries and keys and append keys and values to the cache.
+
+    q [T, Hq, 64], k/v [T, Hkv, 64] (bf16 or fp32); seqlens [B] int32 counts the new rows;
+    without cu_seqlens_q, T == B (one row per sequence).  kv_cache = (k_cache, v_cache):
+    contiguous [B, L, Hkv, 64]; paged [num_blocks, block_size, Hkv, 64] with block_table
+    [B, max_blocks]; or, with ring=True, rings [B, W, Hkv, 64].  Returns q_out [T, Hq, 64]
+    (pass q_out=q to rotate in place).
+    """
+    dev = q.device
+    dt = _dtype_code(q)
+    _check_tensor(q, "q", q.dtype, dev, 3)
+    T, Hq, D = q.shape
+    _check_tensor(k, "k", q.dtype, dev, 3)
+    _check_tensor(v, "v", q.dtype, dev, 3)
+    _need(k.shape[0] == T and k.shape[2] == D and v.shape == k.shape, "k/v must be [T, Hkv, D]")
+    Hkv = k.shape[1]
+    kc, vc = _split_cache(kv_cache)
+    _check_tensor(kc, "k_cache", q.dtype, dev, 4)
+    _check_tensor(vc, "v_cache", q.dtype, dev, 4)
+    _need(vc.shape == kc.shape and kc.shape[2] == Hkv and kc.shape[3] == D, "caches must be [.., .., Hkv, D]")
+    _check_tensor(seqlens, "seqlens", torch.int32, dev, 1)
+    B = seqlens.shape[0]
+    if cu_seqlens_q is not None:
+        _check_tensor(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev, 1)
+        _need(cu_seqlens_q.shape[0] == B + 1, "cu_seqlens_q must have B+1 entries")
+    if inv_freq is None:
+        inv_freq = rope_inv_freq(D, device=dev)
+    _check_tensor(inv_freq, "inv_freq", torch.float32, dev, 1)
+    _need(inv_freq.shape[0] == D // 2, "inv_freq must have D/2 entries")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    else:
+        _check_tensor(q_out, "q_out", q.dtype, dev, 3)
+        _need(q_out.shape == q.shape, "q_out must match q")
+    if block_table is not None:
+        _check_tensor(block_table, "block_table", torch.int32, dev, 2)
+        _need(block_table.shape[0] == B, "block_table must have B rows")
+        kind, cache_len = 1, 0
+        max_blocks, block_size, num_blocks = block_table.shape[1], kc.shape[1], kc.shape[0]
+    else:
+        _need(kc.shape[0] == B, "a contiguous or ring cache has B rows")
+        kind, cache_len = (2 if ring else 0), kc.shape[1]
+        max_blocks, block_size, num_blocks = 0, 0, 0
+    _check(lib().gqa_rope_append(_ptr(q), _ptr(k), _ptr(v), _ptr(q_out), _ptr(cu_seqlens_q), _ptr(seqlens),
+                                 _ptr(inv_freq), float(mscale), int(pairing), _ptr(kc), _ptr(vc), kind, cache_len,
+                                 _ptr(block_table), max_blocks, block_size, num_blocks, B, T, Hq, Hkv, D, dt,
+                                 _stream(dev)))
+    return q_out

@@ -126,7 +126,7 @@ size_t decode_ws_bytes(const SplitPlan& p, int B, int Hq) {
 
 extern "C" {
 
-int gqa_attn_version(void) { return 300; }
+int gqa_attn_version(void) { return 301; }
 
 const char* gqa_attn_status_string(int status) {
   switch (status) {
@@ -359,6 +359,44 @@ int gqa_kv_ring_append(const void* k_new, const void* v_new, const int32_t* cu_s
   a.row_bytes = Hkv * D * (dtype == GQA_BF16 ? 2 : 4);
   hipError_t e = launch_ring_append(a, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "ring append launch");
+}
+
+int gqa_rope_append(const void* q, const void* k, const void* v, void* q_out, const int32_t* cu_seqlens_q,
+                    const int32_t* seqlens, const float* inv_freq, float mscale, int pairing, void* k_cache,
+                    void* v_cache, int cache_kind, int cache_len, const int32_t* block_table, int max_blocks,
+                    int block_size, int num_blocks, int B, int T, int Hq, int Hkv, int D, int dtype, void* stream) {
+  if (dtype != GQA_BF16 && dtype != GQA_FP32) return fail(GQA_ERR_UNSUPPORTED, "dtype %d is not GQA_BF16 or GQA_FP32", dtype);
+  if (D != kHeadDim) return fail(GQA_ERR_UNSUPPORTED, "head_dim %d is not supported (only 64)", D);
+  if (B < 0 || T < 0 || Hq <= 0 || Hkv <= 0)
+    return fail(GQA_ERR_INVALID_ARG, "bad size (B=%d, T=%d, Hq=%d, Hkv=%d)", B, T, Hq, Hkv);
+  if (pairing != 0 && pairing != 1) return fail(GQA_ERR_INVALID_ARG, "pairing %d is not 0 or 1", pairing);
+  if (std::isnan(mscale) || std::isinf(mscale)) return fail(GQA_ERR_INVALID_ARG, "mscale must be finite");
+  if (!cu_seqlens_q && T != B)
+    return fail(GQA_ERR_INVALID_ARG, "without cu_seqlens_q there is one new row per sequence (T=%d, B=%d)", T, B);
+  int log2b = 0;
+  if (cache_kind == 0 || cache_kind == 2) {
+    if (cache_len <= 0) return fail(GQA_ERR_INVALID_ARG, "cache_len %d must be >= 1", cache_len);
+  } else if (cache_kind == 1) {
+    if (block_size < 1 || block_size > 1024 || (block_size & (block_size - 1)))
+      return fail(GQA_ERR_UNSUPPORTED, "block_size %d is not a power of two in [1, 1024]", block_size);
+    if (max_blocks <= 0 || num_blocks <= 0) return fail(GQA_ERR_INVALID_ARG, "max_blocks and num_blocks must be >= 1");
+    if (!block_table && B > 0 && T > 0) return fail(GQA_ERR_INVALID_ARG, "a paged cache needs block_table");
+    while ((1 << log2b) < block_size) ++log2b;
+  } else {
+    return fail(GQA_ERR_INVALID_ARG, "cache_kind %d is not 0 (contiguous), 1 (paged) or 2 (ring)", cache_kind);
+  }
+  if (B == 0 || T == 0) return ok();
+  if (!q || !k || !v || !q_out || !seqlens || !inv_freq || !k_cache || !v_cache)
+    return fail(GQA_ERR_INVALID_ARG, "q, k, v, q_out, seqlens, inv_freq, k_cache and v_cache must be non-NULL");
+  RopeAppendArgs a{};
+  a.q = q; a.k = k; a.v = v; a.q_out = q_out; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.inv_freq = inv_freq; a.cu_seqlens_q = cu_seqlens_q; a.seqlens = seqlens; a.block_table = block_table;
+  a.T = T; a.B = B; a.Hq = Hq; a.Hkv = Hkv;
+  a.cache_kind = cache_kind; a.cache_len = cache_len;
+  a.max_blocks = max_blocks; a.log2_block = log2b; a.num_blocks = num_blocks;
+  a.pairing = pairing; a.mscale = mscale; a.fp32 = dtype == GQA_FP32;
+  hipError_t e = launch_rope_append(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "rope append launch");
 }
 
 size_t gqa_attn_decode_ring_workspace_size(int B, int W, int Hq, int Hkv, int D, int dtype) {

@@ -84,10 +84,33 @@ struct RingAppendArgs {
   int row_bytes;                // Hkv * D * element size
 };
 
+// Rotary encoding of new rows fused with their KV-cache append.
+struct RopeAppendArgs {
+  const void* q;                // [T, Hq, D]
+  const void* k;                // [T, Hkv, D]
+  const void* v;                // [T, Hkv, D]
+  void* q_out;                  // [T, Hq, D] (may be q)
+  void* k_cache;
+  void* v_cache;
+  const float* inv_freq;        // [D/2]
+  const int32_t* cu_seqlens_q;  // [B+1] or NULL (one row per sequence)
+  const int32_t* seqlens;       // [B]
+  const int32_t* block_table;   // paged cache only
+  int64_t T;
+  int B, Hq, Hkv;
+  int cache_kind;               // 0 contiguous [B, cache_len, ..], 1 paged, 2 ring of cache_len slots
+  int cache_len;
+  int max_blocks, log2_block, num_blocks;
+  int pairing;                  // 0: (2i, 2i+1); 1: (i, i + D/2)
+  float mscale;
+  int fp32;
+};
+
 int prefill_ntiles_per_wg();  // N-tiles (32 rows of one head) per prefill workgroup
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int kv_mode, bool varlen_q, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int kv_mode, hipStream_t s);
 hipError_t launch_fp32(const Fp32Args& a, int kv_mode, hipStream_t s);
 hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t s);
+hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s);
 
 }  // namespace gqa

@@ -1,0 +1,189 @@
+// Rotary position encoding of new tokens, fused with their KV-cache append.
+//
+// «GPT-OSS-20B : Architecture MoE & Résumé du Model Card», §3.4: a token at
+// position m is rotated with the frequencies θ_i = 10000^(-2i/d); «GPT-OSS vs
+// Qwen3», "Adoption de RoPE": the query and key vectors are turned by an angle
+// that depends on the position.  Pair i of a head, (a, b), becomes
+// (a cos - b sin, a sin + b cos) at angle m·inv_freq[i]; the pairs are
+// (2i, 2i+1) or (i, i + d/2).  The frequency table is an input (θ_i by
+// default), and `mscale` scales cos and sin alike.
+//
+// One pass over the new rows: the queries are rotated into q_out (which may
+// be q itself), the keys are rotated and written with the values into the
+// cache slot of their position (contiguous, paged or ring cache).  The angle
+// m·inv_freq[i] is formed in fp64, where the product of an integer position
+// and an fp32 frequency is exact, so positions up to the 131 072-token context
+// keep full accuracy; the rotation itself is fp32.
+//
+// One wave per new row, 8 lanes per head: lane c = lane % 8 of a head owns the
+// pairs 4c .. 4c+3 and moves 16 contiguous bytes of them per load; cos and sin
+// of its 4 pairs are computed once per row and reused for every head.
+#include "kernels.h"
+
+namespace gqa {
+namespace {
+
+constexpr int RP_THREADS = 256;  // 4 waves, one row each
+
+template <typename T>
+struct Elt;
+template <>
+struct Elt<__bf16> {
+  static __device__ __forceinline__ float get(const __bf16* p, int i) { return (float)p[i]; }
+  static __device__ __forceinline__ void put(__bf16* p, int i, float v) { p[i] = (__bf16)v; }
+};
+template <>
+struct Elt<float> {
+  static __device__ __forceinline__ float get(const float* p, int i) { return p[i]; }
+  static __device__ __forceinline__ void put(float* p, int i, float v) { p[i] = v; }
+};
+
+// Copy of n elements through 16-byte words (n * sizeof(T) is a multiple of 16).
+template <typename T, int N>
+__device__ __forceinline__ void load_n(T (&dst)[N], const T* src) {
+  static_assert((N * sizeof(T)) % 8 == 0, "whole 8-byte words");
+  if constexpr ((N * sizeof(T)) % 16 == 0) {
+    typedef uint32_t w4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int i = 0; i < (int)(N * sizeof(T) / 16); ++i)
+      reinterpret_cast<w4*>(dst)[i] = reinterpret_cast<const w4*>(src)[i];
+  } else {
+    typedef uint32_t w2 __attribute__((ext_vector_type(2)));
+    reinterpret_cast<w2*>(dst)[0] = reinterpret_cast<const w2*>(src)[0];
+  }
+}
+template <typename T, int N>
+__device__ __forceinline__ void store_n(T* dst, const T (&src)[N]) {
+  if constexpr ((N * sizeof(T)) % 16 == 0) {
+    typedef uint32_t w4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int i = 0; i < (int)(N * sizeof(T) / 16); ++i)
+      reinterpret_cast<w4*>(dst)[i] = reinterpret_cast<const w4*>(src)[i];
+  } else {
+    typedef uint32_t w2 __attribute__((ext_vector_type(2)));
+    reinterpret_cast<w2*>(dst)[0] = reinterpret_cast<const w2*>(src)[0];
+  }
+}
+
+// Rotate this lane's 4 pairs of one head in place (src -> dst may alias).
+template <typename T, int PAIRING>
+__device__ __forceinline__ void rotate_head(T* dst, const T* src, int c, const float (&cs)[4], const float (&sn)[4]) {
+  if (PAIRING == 0) {
+    // pairs (2i, 2i+1), i = 4c .. 4c+3: elements 8c .. 8c+7
+    T x[8];
+    load_n<T, 8>(x, src + 8 * c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = Elt<T>::get(x, 2 * j), b = Elt<T>::get(x, 2 * j + 1);
+      Elt<T>::put(x, 2 * j, __builtin_fmaf(a, cs[j], -b * sn[j]));
+      Elt<T>::put(x, 2 * j + 1, __builtin_fmaf(a, sn[j], b * cs[j]));
+    }
+    store_n<T, 8>(dst + 8 * c, x);
+  } else {
+    // pairs (i, i + 32), i = 4c .. 4c+3: elements 4c .. 4c+3 and 32+4c .. 32+4c+3
+    T x[4], y[4];
+    load_n<T, 4>(x, src + 4 * c);
+    load_n<T, 4>(y, src + 32 + 4 * c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = Elt<T>::get(x, j), b = Elt<T>::get(y, j);
+      Elt<T>::put(x, j, __builtin_fmaf(a, cs[j], -b * sn[j]));
+      Elt<T>::put(y, j, __builtin_fmaf(a, sn[j], b * cs[j]));
+    }
+    store_n<T, 4>(dst + 4 * c, x);
+    store_n<T, 4>(dst + 32 + 4 * c, y);
+  }
+}
+
+template <typename T, int PAIRING>
+__global__ __launch_bounds__(RP_THREADS) void rope_append_kernel(RopeAppendArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (RP_THREADS / 64) + (threadIdx.x >> 6);
+  if (row >= a.T) return;
+
+  // sequence and position of this row (the newest q_len positions of its sequence)
+  int b, t, q_len;
+  if (a.cu_seqlens_q) {
+    if (row >= a.cu_seqlens_q[a.B]) return;
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.cu_seqlens_q[mid] <= row) lo = mid;
+      else hi = mid - 1;
+    }
+    b = lo;
+    q_len = a.cu_seqlens_q[b + 1] - a.cu_seqlens_q[b];
+    t = (int)(row - a.cu_seqlens_q[b]);
+    if (t < 0 || t >= q_len) return;
+  } else {
+    b = (int)row;
+    t = 0;
+    q_len = 1;
+  }
+  const int L = a.seqlens[b];
+  const int p = L - q_len + t;
+  const int c = lane & 7;   // lane within its head group: pairs 4c .. 4c+3
+  const int hg = lane >> 3; // head group: heads hg, hg + 8, ...
+
+  float cs[4], sn[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const double ang = (double)p * (double)a.inv_freq[4 * c + j];
+    double s, co;
+    sincos(ang, &s, &co);
+    cs[j] = (float)co * a.mscale;
+    sn[j] = (float)s * a.mscale;
+  }
+
+  const T* q = reinterpret_cast<const T*>(a.q) + row * a.Hq * kHeadDim;
+  T* qo = reinterpret_cast<T*>(a.q_out) + row * a.Hq * kHeadDim;
+  for (int h = hg; h < a.Hq; h += 8) rotate_head<T, PAIRING>(qo + h * kHeadDim, q + h * kHeadDim, c, cs, sn);
+
+  // destination row of this position in the cache (or none)
+  int64_t dst = -1;
+  if (p >= 0) {
+    if (a.cache_kind == 0) {
+      if (p < a.cache_len) dst = (int64_t)b * a.cache_len + p;
+    } else if (a.cache_kind == 1) {
+      const int nb = p >> a.log2_block;
+      if (nb < a.max_blocks) {
+        int blk = a.block_table[(int64_t)b * a.max_blocks + nb];
+        blk = min(max(blk, 0), a.num_blocks - 1);
+        dst = ((int64_t)blk << a.log2_block) + (p & ((1 << a.log2_block) - 1));
+      }
+    } else {
+      if (p >= L - a.cache_len) dst = (int64_t)b * a.cache_len + p % a.cache_len;
+    }
+  }
+  if (dst < 0) return;
+  const int64_t kv_row = (int64_t)a.Hkv * kHeadDim;
+  const T* k = reinterpret_cast<const T*>(a.k) + row * kv_row;
+  T* kc = reinterpret_cast<T*>(a.k_cache) + dst * kv_row;
+  for (int h = hg; h < a.Hkv; h += 8) rotate_head<T, PAIRING>(kc + h * kHeadDim, k + h * kHeadDim, c, cs, sn);
+  // values: copied as 16-byte words
+  typedef uint32_t w4 __attribute__((ext_vector_type(4)));
+  const w4* vs = reinterpret_cast<const w4*>(reinterpret_cast<const T*>(a.v) + row * kv_row);
+  w4* vd = reinterpret_cast<w4*>(reinterpret_cast<T*>(a.v_cache) + dst * kv_row);
+  const int words = (int)(kv_row * sizeof(T) / 16);
+  for (int i = lane; i < words; i += 64) vd[i] = vs[i];
+}
+
+}  // namespace
+
+hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  const int64_t blocks = (a.T + RP_THREADS / 64 - 1) / (RP_THREADS / 64);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+#define GQA_ROPE(TY, PR) hipLaunchKernelGGL((rope_append_kernel<TY, PR>), dim3((unsigned)blocks), dim3(RP_THREADS), 0, s, a)
+  if (a.fp32) {
+    if (a.pairing == 0) GQA_ROPE(float, 0);
+    else GQA_ROPE(float, 1);
+  } else {
+    if (a.pairing == 0) GQA_ROPE(__bf16, 0);
+    else GQA_ROPE(__bf16, 1);
+  }
+#undef GQA_ROPE
+  return hipGetLastError();
+}
+
+}  // namespace gqa

@@ -13,7 +13,9 @@ already resident in HBM:
   4. ring cache of a windowed layer (128 slots per sequence): append of one
      new token per sequence (B64), then decode from the rings at position 8191
      for B64 and for B4096 (the B4096 rings hold as many bytes as the dense
-     B64 x 8192 cache).
+     B64 x 8192 cache);
+  5. rotary encoding of new rows fused with their KV-cache append: the 4096
+     rows of the layer-shaped prefill, and a decode step of 64 sequences.
 `value` is the prefill throughput of the layer pair (1), in algorithmic
 TFLOP/s (4*D*Hq per visible query-key pair), timed with HIP events on the
 stream the kernels run on; every stage's own time, TFLOP/s, GB/s and roofline
@@ -339,6 +341,41 @@ def add_ring(stages, gq, up, i32, f32, dev):
                 flop=0, bytes=4 * B * row, bound="hbm")
 
 
+def add_rope(stages, gq, up, i32, dev):
+    import torch
+
+    import gqa_inputs as gi
+
+    # the layer-shaped prefill's 4096 new rows, rotated and appended to a contiguous cache
+    S, Hq, Hkv, D = 4096, 64, 8, 64
+    q = up(gi.make_tensor(7, gi.T_Q, (S, Hq, D), 1.0, "bf16"))
+    k = up(gi.make_tensor(7, gi.T_K, (S, Hkv, D), 1.0, "bf16"))
+    v = up(gi.make_tensor(7, gi.T_V, (S, Hkv, D), 1.0, "bf16"))
+    kc = torch.zeros((1, S, Hkv, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    qo = torch.empty_like(q)
+    sl = i32([S])
+    cu = i32([0, S])
+    inv = gq.rope_inv_freq(D, device=dev)
+    by = 2 * 2 * (S * Hq * D + 2 * S * Hkv * D)
+    stages["rope_append_s4096"] = dict(
+        fn=(lambda: gq.rope_append(q, k, v, sl, (kc, vc), inv_freq=inv, q_out=qo, cu_seqlens_q=cu)),
+        flop=0, bytes=by, bound="hbm")
+    # one decode step of 64 sequences
+    B = 64
+    qd = up(gi.make_tensor(8, gi.T_Q, (B, Hq, D), 1.0, "bf16"))
+    kd = up(gi.make_tensor(8, gi.T_K, (B, Hkv, D), 1.0, "bf16"))
+    vd = up(gi.make_tensor(8, gi.T_V, (B, Hkv, D), 1.0, "bf16"))
+    kcd = torch.zeros((B, 1024, Hkv, D), dtype=torch.bfloat16, device=dev)
+    vcd = torch.zeros_like(kcd)
+    qod = torch.empty_like(qd)
+    sld = i32([1000] * B)
+    byd = 2 * 2 * (B * Hq * D + 2 * B * Hkv * D)
+    stages["rope_append_decode_b64"] = dict(
+        fn=(lambda: gq.rope_append(qd, kd, vd, sld, (kcd, vcd), inv_freq=inv, q_out=qod)),
+        flop=0, bytes=byd, bound="hbm")
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -408,6 +445,9 @@ def main():
     # 4. ring cache of a windowed layer
     if wanted("ring"):
         add_ring(stages, gq, up, i32, f32, dev)
+    # 5. rotary encoding fused with the KV append
+    if wanted("rope"):
+        add_rope(stages, gq, up, i32, dev)
     if args.long:
         long_stages = {}
         add_prefill(long_stages, gq, gi.c4_prefill(), up, f32, dev)
@@ -484,7 +524,7 @@ def main():
             "workload": "layer-shaped prefill B1 S4096 Hq64 Hkv8 D64 bf16, dense layer then 128-token sliding-window "
                         "layer (value); each step also runs batched decode B64 cache 8192 (dense, window 128) and "
                         "ragged+paged 16 sequences (dense, window 128), and a windowed layer's 128-slot ring cache (append B64; "
-                        "decode B64 and B4096)",
+                        "decode B64 and B4096), and the rotary encoding + KV append of the prefill rows and of a decode step",
             "global_batch": 1,
             "seq_len": 4096,
             "parallelism": "single GPU",

@@ -208,6 +208,45 @@ int gqa_attn_decode_ring(const void* q, const void* k_ring, const void* v_ring,
                          float scale, int dtype,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Rotary position encoding of new tokens fused with their KV-cache append.
+ *
+ * «GPT-OSS-20B : Architecture MoE & Résumé du Model Card», §3.4 "Encodage de
+ * Position (RoPE)": a token at position m is turned with the frequencies
+ * θ_i = 10000^(-2i/d); «GPT-OSS vs Qwen3», "Adoption de RoPE": queries and keys
+ * are rotated by a position-dependent angle.  Pair i of every head, (a, b),
+ * becomes (a cos - b sin, a sin + b cos) at angle m * inv_freq[i], with cos and
+ * sin both multiplied by mscale (1 for plain RoPE).
+ *   pairing: GQA_ROPE_INTERLEAVED pairs coordinates (2i, 2i+1);
+ *            GQA_ROPE_HALVES pairs (i, i + D/2).
+ *   inv_freq [D/2] fp32 (device): θ_i for plain RoPE; a context-extension
+ *     scheme (e.g. YaRN, whose parameters the pages do not give in full)
+ *     passes its own table.
+ * Rows and positions as for gqa_kv_ring_append: q [T, Hq, D], k, v [T, Hkv, D];
+ * without cu_seqlens_q, T == B and row b is at position seqlens[b] - 1; with
+ * cu_seqlens_q [B+1], sequence b's rows are its newest q_len positions.
+ * Outputs: q_out [T, Hq, D] (may be q itself) holds the rotated queries; the
+ * rotated key row and the value row of position p are written to the cache:
+ *   GQA_CACHE_CONTIGUOUS: k_cache, v_cache [B, cache_len, Hkv, D], row p
+ *     (positions >= cache_len are not stored);
+ *   GQA_CACHE_PAGED: [num_blocks, block_size, Hkv, D], slot p % block_size of
+ *     block block_table[b * max_blocks + p / block_size] (power-of-two
+ *     block_size <= 1024; ids clamped to [0, num_blocks));
+ *   GQA_CACHE_RING: [B, cache_len, Hkv, D] rings, slot p % cache_len, only
+ *     the last cache_len positions.
+ * Angles are formed in fp64 (exact for integer positions and fp32
+ * frequencies); the rotation is fp32 and rounds to the dtype once.
+ */
+enum { GQA_ROPE_INTERLEAVED = 0, GQA_ROPE_HALVES = 1 };
+enum { GQA_CACHE_CONTIGUOUS = 0, GQA_CACHE_PAGED = 1, GQA_CACHE_RING = 2 };
+
+int gqa_rope_append(const void* q, const void* k, const void* v, void* q_out,
+                    const int32_t* cu_seqlens_q, const int32_t* seqlens,
+                    const float* inv_freq, float mscale, int pairing,
+                    void* k_cache, void* v_cache, int cache_kind, int cache_len,
+                    const int32_t* block_table, int max_blocks, int block_size, int num_blocks,
+                    int B, int T, int Hq, int Hkv, int D, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

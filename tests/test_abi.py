@@ -29,12 +29,12 @@ def L():
 
 
 def test_library_loads(L):
-    assert L.gqa_attn_version() == 300
+    assert L.gqa_attn_version() == 301
 
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -215,3 +215,37 @@ def test_ring_decode_workspace(L):
     big = L.gqa_attn_decode_ring_workspace_size(8, 65536, 64, 8, 64, 0)
     assert ring_decode(L, B=8, W=65536, ws=None, ws_bytes=0) == -3
     assert ring_decode(L, B=8, W=65536, ws=DUMMY, ws_bytes=big - 1) == -3
+
+
+def rope(L, B=4, T=4, Hq=64, Hkv=8, D=64, dt=0, cu=None, pairing=0, mscale=1.0, kind=0, cache_len=128,
+         table=None, maxblk=0, bs=0, nblk=0, seqlens=DUMMY, inv=DUMMY, q=DUMMY, kc=DUMMY):
+    return L.gqa_rope_append(q, DUMMY, DUMMY, DUMMY, cu, seqlens, inv, mscale, pairing, kc, DUMMY, kind, cache_len,
+                             table, maxblk, bs, nblk, B, T, Hq, Hkv, D, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=128), -2),
+    (dict(dt=5), -2),
+    (dict(pairing=2), -1),
+    (dict(mscale=float("nan")), -1),
+    (dict(mscale=float("inf")), -1),
+    (dict(T=3), -1),
+    (dict(kind=3), -1),
+    (dict(kind=0, cache_len=0), -1),
+    (dict(kind=2, cache_len=-1), -1),
+    (dict(kind=1, bs=12, maxblk=4, nblk=9, table=DUMMY), -2),
+    (dict(kind=1, bs=16, maxblk=0, nblk=9, table=DUMMY), -1),
+    (dict(kind=1, bs=16, maxblk=4, nblk=9, table=None), -1),
+    (dict(seqlens=None), -1),
+    (dict(inv=None), -1),
+    (dict(q=None), -1),
+    (dict(kc=None), -1),
+    (dict(Hq=0), -1),
+])
+def test_rope_append_rejects(L, kw, code):
+    assert rope(L, **kw) == code
+    assert L.gqa_attn_last_error() != b""
+
+
+def test_rope_append_empty_is_ok(L):
+    assert rope(L, B=0, T=0, seqlens=None, inv=None, q=None, kc=None) == 0
