@@ -12,8 +12,9 @@
 // be q itself), the keys are rotated and written with the values into the
 // cache slot of their position (contiguous, paged or ring cache).  The angle
 // m·inv_freq[i] is formed in fp64, where the product of an integer position
-// and an fp32 frequency is exact, so positions up to the 131 072-token context
-// keep full accuracy; the rotation itself is fp32.
+// and an fp32 frequency is exact, and reduced to a fraction of a turn there,
+// so positions up to the 131 072-token context keep full accuracy; sin, cos
+// (the hardware instructions) and the rotation itself are fp32.
 //
 // One wave per new row, 8 lanes per head: lane c = lane % 8 of a head owns the
 // pairs 4c .. 4c+3 and moves 16 contiguous bytes of them per load; cos and sin
@@ -65,33 +66,50 @@ __device__ __forceinline__ void store_n(T* dst, const T (&src)[N]) {
   }
 }
 
-// Rotate this lane's 4 pairs of one head in place (src -> dst may alias).
-template <typename T, int PAIRING>
-__device__ __forceinline__ void rotate_head(T* dst, const T* src, int c, const float (&cs)[4], const float (&sn)[4]) {
+// Rotate this lane's 4 pairs of NH heads (heads h0, h0 + 8, ...): all loads
+// are issued before any math, so one wave keeps NH loads in flight.  src and
+// dst may alias (every element is read before the same lane writes it).
+template <typename T, int PAIRING, int NH>
+__device__ __forceinline__ void rotate_heads(T* dst, const T* src, int h0, int nh, int c, const float (&cs)[4],
+                                             const float (&sn)[4]) {
   if (PAIRING == 0) {
     // pairs (2i, 2i+1), i = 4c .. 4c+3: elements 8c .. 8c+7
-    T x[8];
-    load_n<T, 8>(x, src + 8 * c);
+    T x[NH][8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float a = Elt<T>::get(x, 2 * j), b = Elt<T>::get(x, 2 * j + 1);
-      Elt<T>::put(x, 2 * j, __builtin_fmaf(a, cs[j], -b * sn[j]));
-      Elt<T>::put(x, 2 * j + 1, __builtin_fmaf(a, sn[j], b * cs[j]));
+    for (int u = 0; u < NH; ++u)
+      if (u < nh) load_n<T, 8>(x[u], src + (h0 + 8 * u) * kHeadDim + 8 * c);
+#pragma unroll
+    for (int u = 0; u < NH; ++u) {
+      if (u >= nh) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = Elt<T>::get(x[u], 2 * j), b = Elt<T>::get(x[u], 2 * j + 1);
+        Elt<T>::put(x[u], 2 * j, __builtin_fmaf(a, cs[j], -b * sn[j]));
+        Elt<T>::put(x[u], 2 * j + 1, __builtin_fmaf(a, sn[j], b * cs[j]));
+      }
+      store_n<T, 8>(dst + (h0 + 8 * u) * kHeadDim + 8 * c, x[u]);
     }
-    store_n<T, 8>(dst + 8 * c, x);
   } else {
     // pairs (i, i + 32), i = 4c .. 4c+3: elements 4c .. 4c+3 and 32+4c .. 32+4c+3
-    T x[4], y[4];
-    load_n<T, 4>(x, src + 4 * c);
-    load_n<T, 4>(y, src + 32 + 4 * c);
+    T x[NH][4], y[NH][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float a = Elt<T>::get(x, j), b = Elt<T>::get(y, j);
-      Elt<T>::put(x, j, __builtin_fmaf(a, cs[j], -b * sn[j]));
-      Elt<T>::put(y, j, __builtin_fmaf(a, sn[j], b * cs[j]));
+    for (int u = 0; u < NH; ++u)
+      if (u < nh) {
+        load_n<T, 4>(x[u], src + (h0 + 8 * u) * kHeadDim + 4 * c);
+        load_n<T, 4>(y[u], src + (h0 + 8 * u) * kHeadDim + 32 + 4 * c);
+      }
+#pragma unroll
+    for (int u = 0; u < NH; ++u) {
+      if (u >= nh) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = Elt<T>::get(x[u], j), b = Elt<T>::get(y[u], j);
+        Elt<T>::put(x[u], j, __builtin_fmaf(a, cs[j], -b * sn[j]));
+        Elt<T>::put(y[u], j, __builtin_fmaf(a, sn[j], b * cs[j]));
+      }
+      store_n<T, 4>(dst + (h0 + 8 * u) * kHeadDim + 4 * c, x[u]);
+      store_n<T, 4>(dst + (h0 + 8 * u) * kHeadDim + 32 + 4 * c, y[u]);
     }
-    store_n<T, 4>(dst + 4 * c, x);
-    store_n<T, 4>(dst + 32 + 4 * c, y);
   }
 }
 
@@ -125,19 +143,23 @@ __global__ __launch_bounds__(RP_THREADS) void rope_append_kernel(RopeAppendArgs 
   const int c = lane & 7;   // lane within its head group: pairs 4c .. 4c+3
   const int hg = lane >> 3; // head group: heads hg, hg + 8, ...
 
+  // angle in fp64 as a number of turns, reduced to [-1/2, 1/2] there (the
+  // product is exact and the reduction error is ~1e-16 of the angle); the
+  // hardware sine and cosine take turns
   float cs[4], sn[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const double ang = (double)p * (double)a.inv_freq[4 * c + j];
-    double s, co;
-    sincos(ang, &s, &co);
-    cs[j] = (float)co * a.mscale;
-    sn[j] = (float)s * a.mscale;
+    const double turns = (double)p * (double)a.inv_freq[4 * c + j] * 0.15915494309189535;  // 1 / (2 pi)
+    const float r = (float)(turns - __builtin_rint(turns));
+    cs[j] = __builtin_amdgcn_cosf(r) * a.mscale;
+    sn[j] = __builtin_amdgcn_sinf(r) * a.mscale;
   }
 
+  // heads hg, hg + 8, ... in batches of 8 per lane (64 heads: one batch)
   const T* q = reinterpret_cast<const T*>(a.q) + row * a.Hq * kHeadDim;
   T* qo = reinterpret_cast<T*>(a.q_out) + row * a.Hq * kHeadDim;
-  for (int h = hg; h < a.Hq; h += 8) rotate_head<T, PAIRING>(qo + h * kHeadDim, q + h * kHeadDim, c, cs, sn);
+  for (int h0 = hg; h0 < a.Hq; h0 += 64)
+    rotate_heads<T, PAIRING, 8>(qo, q, h0, (a.Hq - h0 + 7) / 8, c, cs, sn);
 
   // destination row of this position in the cache (or none)
   int64_t dst = -1;
@@ -159,7 +181,8 @@ __global__ __launch_bounds__(RP_THREADS) void rope_append_kernel(RopeAppendArgs 
   const int64_t kv_row = (int64_t)a.Hkv * kHeadDim;
   const T* k = reinterpret_cast<const T*>(a.k) + row * kv_row;
   T* kc = reinterpret_cast<T*>(a.k_cache) + dst * kv_row;
-  for (int h = hg; h < a.Hkv; h += 8) rotate_head<T, PAIRING>(kc + h * kHeadDim, k + h * kHeadDim, c, cs, sn);
+  for (int h0 = hg; h0 < a.Hkv; h0 += 64)
+    rotate_heads<T, PAIRING, 8>(kc, k, h0, (a.Hkv - h0 + 7) / 8, c, cs, sn);
   // values: copied as 16-byte words
   typedef uint32_t w4 __attribute__((ext_vector_type(4)));
   const w4* vs = reinterpret_cast<const w4*>(reinterpret_cast<const T*>(a.v) + row * kv_row);
