@@ -520,12 +520,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   }
 
   // ---- epilogue: normalise, round to bf16, store; log-sum-exp
+  // The row index is re-derived here behind an empty asm, so the compiler does
+  // not keep the prologue's 64-bit Q row offset alive across the tile loops
+  // (it would spill it).
+  int lr_e = lr;
+  asm volatile("" : "+v"(lr_e));
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     if (!nt_valid[i]) continue;
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[i]), __float_as_uint(l_run[i]), false, false);
     const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const int t = nt_t0[i] + lr;
+    const int t = nt_t0[i] + lr_e;
     if (t >= sv.q_len) continue;
     const float inv = lt > 0.f ? 1.f / lt : (lt == 0.f ? 0.f : lt);
     __bf16* op = a.out + ((sv.q_row0 + t) * a.Hq + nt_hq[i]) * (int64_t)kHeadDim;
