@@ -10,7 +10,9 @@ library and imports nothing from it.
 independent pure-Python scalar enumeration of the same definition;
 ``oracle.ring`` is the W-slot ring cache of windowed layers (append by position,
 decode through the windowed definition); ``oracle.rope`` is the rotary position
-encoding of new tokens and their KV-cache append.
+encoding of new tokens and their KV-cache append; ``oracle.backward`` is the
+gradient of the prefill (dq, dk, dv and the sink logits), the chain rule
+applied to the forward definition.
 
 Sources (the web pages this method is taken from):
 
@@ -38,7 +40,8 @@ the query's own position; queries of a chunk are the newest positions of their
 sequence (bottom-right causal alignment); scale defaults to 1/sqrt(D).
 
 Parity pins: every function here is pinned by tests in ``tests/test_oracle_pins.py``
-(brute force, closed forms, library routines, invariants).  No function is
+and the ``tests/test_oracle_*_pins.py`` files of the other modules (brute force,
+closed forms, library routines, finite differences, invariants).  No function is
 "parity unpinned".
 """
 from .attention import (  # noqa: F401
@@ -51,6 +54,11 @@ from .attention import (  # noqa: F401
     probabilities,
     varlen_ref,
     visible_mask,
+)
+from .backward import (  # noqa: F401
+    dout_dot_out,
+    prefill_grad_ref,
+    row_grads,
 )
 from .rope import (  # noqa: F401
     default_inv_freq,
