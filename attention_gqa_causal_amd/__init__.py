@@ -15,6 +15,8 @@ Functions (names follow the C ABI in ``include/gqa_attn.h``):
 * ``kv_ring_append(k_new, v_new, kv_ring, seqlens, cu_seqlens_q=None)`` and
   ``attn_decode_ring(q, kv_ring, seqlens, sinks, scale=None)``: the W-slot ring
   cache of sliding-window layers (position p in slot p % W)
+* ``attn_prefill_backward(q, k, v, sinks, out, lse, dout, ...)``: gradients of
+  the prefill with respect to q, k, v and the sink logits
 
 The computation is causal grouped-query attention with a learned per-head sink
 logit and an optional sliding window (0 = dense), as described on the pages
@@ -37,6 +39,8 @@ __all__ = [
     "rope_append",
     "rope_inv_freq",
     "attn_decode_ring",
+    "attn_prefill_backward",
+    "backward_workspace_size",
     "decode_workspace_size",
     "varlen_workspace_size",
     "lib",
@@ -87,6 +91,9 @@ _SIGNATURES = {
     "gqa_attn_decode_ring": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "gqa_rope_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _I, _I, _P, _I, _I, _I,
                              _I, _I, _I, _I, _I, _I, _P]),
+    "gqa_attn_prefill_backward_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "gqa_attn_prefill_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
 }
 
 
@@ -188,6 +195,55 @@ def attn_prefill(q, k, v, sinks=None, window: int = 0, scale=None, return_lse: b
     _check(lib().gqa_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(out), _ptr(lse),
                                   B, S, Hq, Hkv, D, int(window), int(sink_tokens), _scale(scale), dt, _stream(dev)))
     return (out, lse) if return_lse else out
+
+
+def backward_workspace_size(B, S, Hq, Hkv, D=64, dtype=GQA_BF16) -> int:
+    return int(lib().gqa_attn_prefill_backward_workspace_size(B, S, Hq, Hkv, D, dtype))
+
+
+def attn_prefill_backward(q, k, v, sinks, out, lse, dout, window: int = 0, scale=None, sink_tokens: int = 0,
+                          workspace=None, grads=None):
+    """Gradients of the prefill: returns (dq, dk, dv, dsinks).
+
+    q, out, dout [B, S, Hq, 64]; k, v [B, S, Hkv, 64] (one dtype, bf16 or fp32);
+    lse [B, Hq, S] fp32 as ``attn_prefill(..., return_lse=True)`` returned it;
+    sinks [Hq] fp32 or None (then dsinks is all zeros).  ``grads``: optional
+    preallocated (dq, dk, dv, dsinks).  ``workspace``: optional uint8 tensor of
+    at least ``backward_workspace_size`` bytes.
+    """
+    dev = q.device
+    _check_tensor(q, "q", q.dtype, dev, 4)
+    dt = _dtype_code(q)
+    B, S, Hq, D = q.shape
+    for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check_tensor(t, name, q.dtype, dev, 4)
+    _need(k.shape[:2] == (B, S) and k.shape[3] == D and v.shape == k.shape, "k/v must be [B, S, Hkv, D] matching q")
+    _need(out.shape == q.shape and dout.shape == q.shape, "out and dout must match q")
+    Hkv = k.shape[2]
+    _check_tensor(lse, "lse", torch.float32, dev, 3)
+    _need(tuple(lse.shape) == (B, Hq, S), "lse must be [B, Hq, S]")
+    sinks = _sinks_arg(sinks, Hq, dev)
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dsinks = torch.empty((Hq,), dtype=torch.float32, device=dev)
+    else:
+        dq, dk, dv, dsinks = grads
+        _check_tensor(dq, "dq", q.dtype, dev, 4)
+        _check_tensor(dk, "dk", q.dtype, dev, 4)
+        _check_tensor(dv, "dv", q.dtype, dev, 4)
+        _need(dq.shape == q.shape and dk.shape == k.shape and dv.shape == k.shape, "gradients must match q, k, v")
+        if dsinks is not None:
+            _check_tensor(dsinks, "dsinks", torch.float32, dev, 1)
+            _need(dsinks.shape[0] == Hq, f"dsinks must have Hq={Hq} entries")
+    need = backward_workspace_size(B, S, Hq, Hkv, D, dt)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _check_tensor(workspace, "workspace", torch.uint8, dev, 1)
+    _check(lib().gqa_attn_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(out), _ptr(lse), _ptr(dout),
+                                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks), B, S, Hq, Hkv, D, int(window),
+                                           int(sink_tokens), _scale(scale), dt, _ptr(workspace),
+                                           workspace.numel(), _stream(dev)))
+    return dq, dk, dv, dsinks
 
 
 def decode_workspace_size(B, Lmax, Hq, Hkv, D=64, window=0, dtype=GQA_BF16, sink_tokens=0) -> int:

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgqa_attn.so")
 
-SOURCES = ["api.cpp", "prefill_bf16.hip", "decode_bf16.hip", "generic_fp32.hip", "ring.hip", "rope.hip"]
+SOURCES = ["api.cpp", "prefill_bf16.hip", "decode_bf16.hip", "generic_fp32.hip", "ring.hip", "rope.hip", "backward.hip"]
 ARCH = "gfx950"
 
 

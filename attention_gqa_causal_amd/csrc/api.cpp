@@ -126,7 +126,7 @@ size_t decode_ws_bytes(const SplitPlan& p, int B, int Hq) {
 
 extern "C" {
 
-int gqa_attn_version(void) { return 301; }
+int gqa_attn_version(void) { return 400; }
 
 const char* gqa_attn_status_string(int status) {
   switch (status) {
@@ -413,6 +413,43 @@ int gqa_attn_decode_ring(const void* q, const void* k_ring, const void* v_ring, 
   // (the kernels clamp each length to W).
   return gqa_attn_decode(q, k_ring, v_ring, seqlens, sinks, out, lse, B, W, Hq, Hkv, D, 0, 0, scale, dtype,
                          workspace, workspace_bytes, stream);
+}
+
+size_t gqa_attn_prefill_backward_workspace_size(int B, int S, int Hq, int Hkv, int D, int dtype) {
+  if ((dtype != GQA_BF16 && dtype != GQA_FP32) || B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv ||
+      D != kHeadDim)
+    return 0;
+  const size_t bytes = (size_t)B * Hq * S * sizeof(float);  // <dO, o> per row and head
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int gqa_attn_prefill_backward(const void* q, const void* k, const void* v, const float* sinks, const void* out,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv, float* dsinks,
+                              int B, int S, int Hq, int Hkv, int D, int window, int sink_tokens, float scale,
+                              int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(Hq, Hkv, D, window, sink_tokens, scale, dtype);
+  if (rc) return rc;
+  if (B < 0 || S < 0) return fail(GQA_ERR_INVALID_ARG, "negative size (B=%d, S=%d)", B, S);
+  const size_t need = gqa_attn_prefill_backward_workspace_size(B, S, Hq, Hkv, D, dtype);
+  if (B > 0 && S > 0) {
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv)
+      return fail(GQA_ERR_INVALID_ARG, "q, k, v, out, lse, dout, dq, dk and dv must be non-NULL");
+    if (!workspace || workspace_bytes < need)
+      return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
+    if ((long long)B * S * Hq > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "problem too large");
+  } else if (!dsinks) {
+    return ok();
+  }
+  BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = out; a.dout = dout; a.lse = lse; a.sinks = sinks;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dsinks = dsinks; a.dlt = (float*)workspace;
+  a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+  a.window = window; a.sink_tokens = sink_tokens;
+  a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
+  a.scale_log2 = scale_log2_of(scale, D);
+  a.fp32 = dtype == GQA_FP32;
+  hipError_t e = launch_backward(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "prefill backward launch");
 }
 
 }  // extern "C"

@@ -106,11 +106,34 @@ struct RopeAppendArgs {
   int fp32;
 };
 
+// Backward of the prefill over whole sequences [B, S, H, D].
+struct BwdArgs {
+  const void* q;       // [B, S, Hq, D]
+  const void* k;       // [B, S, Hkv, D]
+  const void* v;
+  const void* o;       // forward output [B, S, Hq, D]
+  const void* dout;    // dL/do [B, S, Hq, D]
+  const float* lse;    // forward log-sum-exp [B, Hq, S], natural log, sink included
+  const float* sinks;  // [Hq] or NULL
+  void* dq;            // [B, S, Hq, D]
+  void* dk;            // [B, S, Hkv, D]
+  void* dv;
+  float* dsinks;       // [Hq] or NULL
+  float* dlt;          // workspace [B, Hq, S]: <dO, o>
+  int B, S, Hq, Hkv, G;
+  int window;
+  int sink_tokens;
+  float scale;         // softmax scale
+  float scale_log2;    // scale * log2(e)
+  int fp32;
+};
+
 int prefill_ntiles_per_wg();  // N-tiles (32 rows of one head) per prefill workgroup
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int kv_mode, bool varlen_q, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int kv_mode, hipStream_t s);
 hipError_t launch_fp32(const Fp32Args& a, int kv_mode, hipStream_t s);
 hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t s);
 hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s);
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
 
 }  // namespace gqa

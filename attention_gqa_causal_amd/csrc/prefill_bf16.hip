@@ -53,6 +53,7 @@
 #include <type_traits>
 
 #include "kernels.h"
+#include "tile_ops.h"
 
 namespace gqa {
 namespace {
@@ -61,37 +62,8 @@ constexpr int BK = 64;          // keys per tile
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int NT_WG = 2 * NWAVES;  // N-tiles per workgroup
-constexpr int RS = 64;          // LDS row (elements) of a K or V tile: one 128-byte key row, no padding
 constexpr int NBUF = 3;         // K/V tiles resident in LDS: current, next, and the one being filled
-constexpr unsigned kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), leaving the other counters alone
 constexpr float kRefit = 0x1p32f;  // a lane's per-tile weight sum past this moves the reference max
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x16 zero16() {
-  f32x16 z;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) z[r] = 0.f;
-  return z;
-}
-
-// LDS tiles hold K and V in their natural [key][d] layout, one 128-byte row
-// per key, with the eight 16-byte chunks of row r stored in the order
-// c ^ (r & 7).  The swizzle spreads the rows that one read instruction touches
-// over all banks, and it lets a wave fill 8 whole rows with one 16-byte
-// global-to-LDS load per lane (lane i lands at byte 16i of the wave's slice, so
-// it fetches logical chunk (i & 7) ^ (i >> 3) of row i >> 3).
-// Element offset of logical 16-byte chunk cc of a row whose index is r (mod 8).
-__device__ __forceinline__ int kchunk(int cc, int r) { return ((cc ^ r) & 7) * 8; }
 
 // S^T of key half h (keys 32h .. 32h+31 of the tile, one per MFMA row) for
 // both N-tiles; each K operand read from LDS feeds two MFMAs.
@@ -105,68 +77,17 @@ __device__ __forceinline__ void qk_half(f32x16& s0, f32x16& s1, const __bf16* ks
   }
 }
 
-// O^T += V^T P^T over key half h (k-steps u = 2h, 2h+1) for both N-tiles.  In
-// 16-lane group c of the wave, lane j reads 4 consecutive d of key row (j/4);
-// the transposing load hands lane i of the group the 4 keys at d = dbase + i.
-// The key order of k-step u matches the score registers:
-// 16u + {4lg..4lg+3, 8+4lg..8+4lg+3}.
-__device__ __forceinline__ bf16x8 v_operand(const __bf16* vs, int u, int dt, const int (&vofs)[2]) {
-  const __bf16* base = vs + vofs[dt] + 16 * u * RS;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * RS));
-  const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, w);
-}
-
+// O^T += V^T P^T over key half h (k-steps u = 2h, 2h+1) for both N-tiles; V^T
+// comes from the V tile through the transposing read.
 __device__ __forceinline__ void pv_half(f32x16 (&o)[2][2], const __bf16* vs, const bf16x8 (&p0)[2],
                                         const bf16x8 (&p1)[2], int h, const int (&vofs)[2]) {
 #pragma unroll
   for (int uu = 0; uu < 2; ++uu) {
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) {
-      const bf16x8 va = v_operand(vs, 2 * h + uu, dt, vofs);
+      const bf16x8 va = tr_operand(vs, 2 * h + uu, dt, vofs);
       o[0][dt] = mfma32(va, p0[uu], o[0][dt]);
       o[1][dt] = mfma32(va, p1[uu], o[1][dt]);
-    }
-  }
-}
-
-// Mask of one N-tile on key half h.  Lane holds keys
-// j0 + 32h + 8*(r/4) + 4*lg + r%4 of query row lr; with off = 32h + 8*(r/4) +
-// r%4 the key is visible iff off <= dh (causal) and, on a windowed layer,
-// off > dl (inside the window) or off < ds (one of the first st positions, the
-// start-of-sequence sink tokens).  dh, dl, ds are per-lane bounds, so the
-// per-register offsets stay compile-time constants.  The half is classified
-// with wave-uniform bounds first: wholly visible is left alone, wholly hidden
-// is cleared, and only a half that the causal diagonal or the window edge
-// crosses is compared element by element.
-template <bool STK>
-__device__ __forceinline__ void mask_half(f32x16& s, int h, int j0, int plo, int phi, int W, int st, int dh, int dl,
-                                          int ds) {
-  const int kb = j0 + 32 * h;  // first key of this half (uniform)
-  const bool any_sink = STK && kb < st;
-  const bool all_sink = STK && kb + 31 < st;
-  if (kb > phi || (W > 0 && !any_sink && kb + 31 <= plo - W)) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = -INFINITY;
-    return;
-  }
-  if (kb + 31 > plo) {  // causal diagonal crosses this half
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (32 * h + 8 * (r >> 2) + (r & 3) > dh) s[r] = -INFINITY;
-  }
-  if (W > 0 && !all_sink && kb <= phi - W) {  // window edge crosses this half
-    if (any_sink) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = 32 * h + 8 * (r >> 2) + (r & 3);
-        if (off <= dl && off >= ds) s[r] = -INFINITY;
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (32 * h + 8 * (r >> 2) + (r & 3) <= dl) s[r] = -INFINITY;
     }
   }
 }
@@ -210,8 +131,6 @@ __device__ __forceinline__ float exp_chunk(const f32x16& s, bf16x8& pb, int uu, 
   pb = __builtin_bit_cast(bf16x8, w);
   return ra + rb;
 }
-
-__device__ __forceinline__ void fence_schedule() { __builtin_amdgcn_sched_barrier(0); }
 
 // Rare path: some lane's weights on this key half summed past kRefit, i.e. a
 // score rose far above the reference max (always so on the first visible half
@@ -377,16 +296,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   };
 
 
-  // Per-lane element offsets of the transposing V reads (see pv_half): key
-  // row rk = 4*(lane/32) + (lane%16)/4 of each 8-row group, 4 consecutive d
-  // from d = 32*dt + 16*((lane/16)%2) + 4*(lane%4).
+  // Per-lane element offsets of the transposing V reads (see pv_half).
   int vofs[2];
-  {
-    const int rk = 4 * (lane >> 5) + ((lane & 15) >> 2);
-    const int c0 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt) vofs[dt] = rk * RS + kchunk(4 * dt + c0, rk) + 4 * (lane & 1);
-  }
+  tr_offsets(lane, vofs);
 
   // Tile t runs in three phases, each pairing vector work with independent
   // matrix work so that both units stay busy within the wave:
@@ -468,7 +380,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
       {
         bf16x8 va[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) va[i] = v_operand(Vs[cur], i >> 1, i & 1, vofs);
+        for (int i = 0; i < 4; ++i) va[i] = tr_operand(Vs[cur], i >> 1, i & 1, vofs);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int uu = i >> 1, dt = i & 1;

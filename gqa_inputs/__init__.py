@@ -18,7 +18,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-T_Q, T_K, T_V, T_SINK, T_LEN, T_PERM = range(6)
+T_Q, T_K, T_V, T_SINK, T_LEN, T_PERM, T_DOUT = range(7)
 
 
 def rng_for(cfg: int, tensor_id: int) -> np.random.Generator:

@@ -3,7 +3,8 @@
  *
  * Forward pass of causal grouped-query attention with a learned per-head sink
  * logit and an optional sliding window, over Q/K that already carry their
- * rotary position encoding.
+ * rotary position encoding; the rotary encoding and KV-cache append of new
+ * rows; and the backward pass of the prefill.
  *
  * What is computed (for query head h at sequence position p):
  *   G = Hq / Hkv, g = h / G            -- query heads share KV heads in
@@ -246,6 +247,39 @@ int gqa_rope_append(const void* q, const void* k, const void* v, void* q_out,
                     void* k_cache, void* v_cache, int cache_kind, int cache_len,
                     const int32_t* block_table, int max_blocks, int block_size, int num_blocks,
                     int B, int T, int Hq, int Hkv, int D, int dtype, void* stream);
+
+/*
+ * Backward of the prefill: the gradients of a loss L with respect to q, k, v
+ * and the sink logits, given dL/dout.  Training the model calls for them
+ * («GPT-OSS-20B : Architecture MoE & Résumé du Model Card», §5: pre-training
+ * by next-token prediction); the pages print no backward pass, so what is
+ * computed is the derivative of the forward definition above, with
+ * P_j = e^{x_j - lse} and D = <dL/dout, out> per row and head:
+ *   dx_j  = P_j (<dL/dout, v_j> - D)                    (gradient of logit x_j)
+ *   dq    = scale sum_j dx_j k_j[g]
+ *   dk_j[g] = scale sum over rows and query heads of g of dx_j q
+ *   dv_j[g] = sum over rows and query heads of g of P_j dL/dout
+ *   dsinks[h] = -sum over rows of e^{s_h - lse} D       (the sink has no value)
+ * Same layouts and arguments as gqa_attn_prefill (window, sink_tokens, scale):
+ *   q, out, dout, dq [B, S, Hq, D]     k, v, dk, dv [B, S, Hkv, D]
+ *   lse [B, Hq, S] fp32: the forward's, as gqa_attn_prefill wrote it (input)
+ *   sinks [Hq] fp32 or NULL (no sink)
+ *   dsinks [Hq] fp32 output, or NULL (not computed); zeros when sinks is NULL
+ * dq, dk, dv are written whole (no accumulation into them) in the dtype of
+ * the inputs.  workspace: at least gqa_attn_prefill_backward_workspace_size
+ * bytes of device memory, owned by the caller, clobbered by the call.  The
+ * result is deterministic (no atomics).  B == 0 or S == 0 writes only dsinks
+ * (zeros).  Errors as for every entry point; GQA_ERR_WORKSPACE when the
+ * workspace is missing or small.
+ */
+size_t gqa_attn_prefill_backward_workspace_size(int B, int S, int Hq, int Hkv, int D, int dtype);
+
+int gqa_attn_prefill_backward(const void* q, const void* k, const void* v, const float* sinks,
+                              const void* out, const float* lse, const void* dout,
+                              void* dq, void* dk, void* dv, float* dsinks,
+                              int B, int S, int Hq, int Hkv, int D,
+                              int window, int sink_tokens, float scale, int dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

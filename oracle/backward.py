@@ -57,12 +57,16 @@ def row_grads(q, k, v, q_pos, k_pos, sink: float, dout, window: int, scale: floa
     return dq, dk, dv, float(ds_rows.sum()), dx, ds_rows
 
 
-def prefill_grad_ref(q, k, v, sinks, dout, window: int = 0, scale=None, sink_tokens: int = 0):
+def prefill_grad_ref(q, k, v, sinks, dout, window: int = 0, scale=None, sink_tokens: int = 0, kv_heads=None,
+                     dsink_abs: bool = False):
     """Gradients of the prefill (self-attention of whole sequences).
 
     q, dout: [B, S, Hq, D]; k, v: [B, S, Hkv, D]; sinks: [Hq] or None (no sink).
     Returns dq [B, S, Hq, D], dk [B, S, Hkv, D], dv [B, S, Hkv, D], dsinks [Hq]
-    (zeros when sinks is None), all fp64.
+    (zeros when sinks is None), all fp64.  kv_heads (optional): compute only the
+    query heads of these KV heads (the rest of every output stays zero).
+    dsink_abs: also return, per head, the sum over rows of |ds| (the magnitude
+    of the terms that dsinks adds up, a scale for comparing it).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -77,18 +81,25 @@ def prefill_grad_ref(q, k, v, sinks, dout, window: int = 0, scale=None, sink_tok
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     dsinks = np.zeros((Hq,))
+    ds_abs = np.zeros((Hq,))
     pos = np.arange(S)
     for b in range(B):
         for h in range(Hq):
             g = kv_head(h, Hq, Hkv)
-            gq, gk, gv, gs, _, _ = row_grads(q[b, :, h], k[b, :, g], v[b, :, g], pos, pos, sinks[h], dout[b, :, h],
-                                             window, scale, sink_tokens)
+            if kv_heads is not None and g not in kv_heads:
+                continue
+            gq, gk, gv, gs, _, ds_rows = row_grads(q[b, :, h], k[b, :, g], v[b, :, g], pos, pos, sinks[h],
+                                                   dout[b, :, h], window, scale, sink_tokens)
             dq[b, :, h] = gq
             dk[b, :, g] += gk
             dv[b, :, g] += gv
             dsinks[h] += gs
+            ds_abs[h] += np.abs(ds_rows).sum()
     if not has_sink:
         dsinks[:] = 0.0
+        ds_abs[:] = 0.0
+    if dsink_abs:
+        return dq, dk, dv, dsinks, ds_abs
     return dq, dk, dv, dsinks
 
 

@@ -29,12 +29,12 @@ def L():
 
 
 def test_library_loads(L):
-    assert L.gqa_attn_version() == 301
+    assert L.gqa_attn_version() == 400
 
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -249,3 +249,45 @@ def test_rope_append_rejects(L, kw, code):
 
 def test_rope_append_empty_is_ok(L):
     assert rope(L, B=0, T=0, seqlens=None, inv=None, q=None, kc=None) == 0
+
+
+def backward(L, B=1, S=16, Hq=64, Hkv=8, D=64, window=0, sink_tokens=0, scale=0.0, dt=0, q=DUMMY, lse=DUMMY,
+             dout=DUMMY, dq=DUMMY, dsinks=None, ws=DUMMY, ws_bytes=1 << 20):
+    return L.gqa_attn_prefill_backward(q, DUMMY, DUMMY, None, DUMMY, lse, dout, dq, DUMMY, DUMMY, dsinks,
+                                       B, S, Hq, Hkv, D, window, sink_tokens, scale, dt, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=128), -2),
+    (dict(dt=3), -2),
+    (dict(Hq=12, Hkv=8), -2),
+    (dict(Hq=0), -1),
+    (dict(B=-1), -1),
+    (dict(window=-1), -1),
+    (dict(sink_tokens=-2), -1),
+    (dict(scale=-1.0), -1),
+    (dict(scale=float("nan")), -1),
+    (dict(q=None), -1),
+    (dict(lse=None), -1),
+    (dict(dout=None), -1),
+    (dict(dq=None), -1),
+    (dict(ws=None), -3),
+    (dict(ws_bytes=16 * 64 * 4 - 1), -3),
+])
+def test_backward_rejects(L, kw, code):
+    assert backward(L, **kw) == code
+    assert L.gqa_attn_last_error() != b""
+
+
+def test_backward_workspace_size(L):
+    # one fp32 per (sequence, head, position), rounded up to 256 bytes
+    assert L.gqa_attn_prefill_backward_workspace_size(1, 16, 64, 8, 64, 0) == 16 * 64 * 4
+    assert L.gqa_attn_prefill_backward_workspace_size(2, 4096, 64, 8, 64, 0) == 2 * 4096 * 64 * 4
+    assert L.gqa_attn_prefill_backward_workspace_size(1, 3, 1, 1, 64, 1) == 256
+    assert L.gqa_attn_prefill_backward_workspace_size(1, 16, 64, 8, 32, 0) == 0
+    assert L.gqa_attn_prefill_backward_workspace_size(1, 16, 12, 8, 64, 0) == 0
+
+
+def test_backward_empty_is_ok(L):
+    assert backward(L, B=0, q=None, lse=None, dout=None, dq=None, ws=None, ws_bytes=0) == 0
+    assert backward(L, S=0, q=None, lse=None, dout=None, dq=None, ws=None, ws_bytes=0) == 0

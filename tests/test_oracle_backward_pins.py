@@ -209,3 +209,31 @@ def test_planted_mistakes_are_caught(monkeypatch, kind):
     monkeypatch.setattr(BW, "row_grads", _planted(kind))
     grads = BW.prefill_grad_ref(q, k, v, sinks, dout, 0, 0.6, 0)
     assert fd_max_error(q, k, v, sinks, dout, 0, 0.6, 0, grads) > 1e-3
+
+
+def test_kv_head_subset_is_a_restriction():
+    B, S, Hq, Hkv, D = 1, 12, 8, 4, 4
+    q, k, v, dout = rnd(71, B, S, Hq, D), rnd(72, B, S, Hkv, D), rnd(73, B, S, Hkv, D), rnd(74, B, S, Hq, D)
+    sinks = rnd(75, Hq)
+    full = BW.prefill_grad_ref(q, k, v, sinks, dout, 5, None, 2)
+    part = BW.prefill_grad_ref(q, k, v, sinks, dout, 5, None, 2, kv_heads=[1, 3])
+    heads = [2, 3, 6, 7]
+    np.testing.assert_array_equal(part[0][:, :, heads], full[0][:, :, heads])
+    np.testing.assert_array_equal(part[1][:, :, [1, 3]], full[1][:, :, [1, 3]])
+    np.testing.assert_array_equal(part[2][:, :, [1, 3]], full[2][:, :, [1, 3]])
+    np.testing.assert_array_equal(part[3][heads], full[3][heads])
+    assert not part[0][:, :, [0, 1, 4, 5]].any() and not part[1][:, :, [0, 2]].any()
+
+
+def test_dsink_abs_is_the_sum_of_term_magnitudes():
+    B, S, Hq, Hkv, D = 1, 9, 4, 2, 4
+    q, k, v, dout = rnd(81, B, S, Hq, D), rnd(82, B, S, Hkv, D), rnd(83, B, S, Hkv, D), rnd(84, B, S, Hq, D)
+    sinks = rnd(85, Hq)
+    *_, ds, ds_abs = BW.prefill_grad_ref(q, k, v, sinks, dout, 0, None, 0, dsink_abs=True)
+    assert (ds_abs >= np.abs(ds) - 1e-15).all()
+    for h in range(Hq):
+        _, _, _, _, _, rows = BW.row_grads(q[0, :, h], k[0, :, h // 2], v[0, :, h // 2], np.arange(S), np.arange(S),
+                                           sinks[h], dout[0, :, h], 0, 1 / 2, 0)
+        np.testing.assert_allclose(ds_abs[h], np.abs(rows).sum(), rtol=1e-14)
+    *_, ds1, abs1 = BW.prefill_grad_ref(q[:, :1], k[:, :1], v[:, :1], sinks, dout[:, :1], 0, None, 0, dsink_abs=True)
+    np.testing.assert_allclose(abs1, np.abs(ds1), rtol=1e-14)   # one row: one term per head
