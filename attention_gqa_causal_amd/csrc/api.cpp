@@ -419,8 +419,16 @@ size_t gqa_attn_prefill_backward_workspace_size(int B, int S, int Hq, int Hkv, i
   if ((dtype != GQA_BF16 && dtype != GQA_FP32) || B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv ||
       D != kHeadDim)
     return 0;
-  const size_t bytes = (size_t)B * Hq * S * sizeof(float);  // <dO, o> per row and head
-  return (bytes + 255) & ~(size_t)255;
+  // <dO, o> and lse in log2 units per row and head, then (bf16, key ranges cut into slabs) the fp32
+  // dK/dV partial sums of every (sequence, KV head, 64-key block, slab)
+  // D and lse in log2 units, block sums of the sink gradient
+  size_t bytes = 2 * (((size_t)B * Hq * S * sizeof(float) + 255) & ~(size_t)255) +
+                 (((size_t)Hq * B * ((S + 1023) / 1024) * sizeof(float) + 255) & ~(size_t)255);
+  int n_slabs = 1, slab_len = 0;
+  backward_plan(B, S, Hkv, 0, 0, &n_slabs, &slab_len);  // the largest (dense) plan
+  if (dtype == GQA_BF16 && n_slabs > 1)
+    bytes += (size_t)B * Hkv * ((S + 63) / 64) * n_slabs * 2 * 64 * kHeadDim * sizeof(float);
+  return bytes;
 }
 
 int gqa_attn_prefill_backward(const void* q, const void* k, const void* v, const float* sinks, const void* out,
@@ -443,6 +451,13 @@ int gqa_attn_prefill_backward(const void* q, const void* k, const void* v, const
   BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = out; a.dout = dout; a.lse = lse; a.sinks = sinks;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dsinks = dsinks; a.dlt = (float*)workspace;
+  backward_plan(B, S, Hkv, window, sink_tokens, &a.n_slabs, &a.slab_len);
+  if (dtype != GQA_BF16) a.n_slabs = 1;
+  const size_t row_bytes = ((size_t)B * Hq * S * sizeof(float) + 255) & ~(size_t)255;
+  const size_t sink_bytes = ((size_t)Hq * B * ((S + 1023) / 1024) * sizeof(float) + 255) & ~(size_t)255;
+  a.lse2 = (float*)((char*)workspace + row_bytes);
+  a.dsink_part = (float*)((char*)workspace + 2 * row_bytes);
+  a.part = (float*)((char*)workspace + 2 * row_bytes + sink_bytes);
   a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
   a.window = window; a.sink_tokens = sink_tokens;
   a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);

@@ -15,9 +15,10 @@
 //   dk_j = scale sum_{p, h in g} dS_j q       dv_j = sum_{p, h in g} P_j dO
 //   dsink_h = -sum_p exp(s_h - lse) D         (the sink has no value vector)
 //
-// Four launches, all deterministic (no atomics):
-//   1. D per (row, head) from o and dO (bandwidth-bound, one wave per row);
-//   2. dsinks: one workgroup per head sums over the rows in a fixed order;
+// The launches, all deterministic (no atomics):
+//   1. D per (row, head) from o and dO (bandwidth-bound);
+//   2. lse in log2 units and block sums of the sink gradient, then dsinks
+//      as the sum of those in a fixed order;
 //   3. dK/dV: a workgroup owns 64 keys of one KV head; query tiles of 32
 //      positions x 2 heads of the group are staged in LDS (16-byte direct
 //      loads, three buffers, two units ahead) and every wave computes, for its
@@ -28,12 +29,19 @@
 //      operand (a lane holds one key and 16 queries, the row order of the
 //      contraction) and dO, Q read through the transposing LDS load.  The two
 //      waves that share keys but differ in head add their sums through LDS at
-//      the end; the result goes out as whole 128-byte rows.
+//      the end; the result goes out as whole 128-byte rows.  Under the causal
+//      mask the first key block sees every query and the last one only its
+//      own, so when there are few key blocks per slot of the chip, the query
+//      range is cut into up to 4 slabs, each its own workgroup: a key block
+//      with several slabs writes fp32 partial sums that a small kernel adds
+//      in slab order (deterministic), and one with a single slab writes bf16
+//      directly.
 //   4. dQ: the forward's decomposition (8 N-tiles of 32 positions x one head
 //      per workgroup, K/V tiles staged as in the forward): S^T = K Q^T and
 //      dP^T = V dO^T with Q and dO rows in registers, then dQ^T += K^T dS^T.
 // Recomputing S and dP in launch 4 costs 6 of its 12 matrix products per key
 // block; it buys freedom from atomics on dQ.
+#include <algorithm>
 #include <type_traits>
 
 #include "kernels.h"
@@ -51,7 +59,8 @@ constexpr int NBUF = 3;   // staged units / tiles resident in LDS
 
 // ---------------------------------------------------------------------------
 // 1. D = <dO, o> per (row, head): one wave per (sequence, position) row; the
-// lanes walk the row's 16-byte chunks and the lanes of one head add up.
+// lanes walk the row's 16-byte chunks (the heads of a position are
+// contiguous) and the lanes of one head add up.
 template <typename T>
 __global__ __launch_bounds__(BT) void bwd_dot_kernel(BwdArgs a) {
   const int lane = threadIdx.x & 63;
@@ -83,19 +92,28 @@ __global__ __launch_bounds__(BT) void bwd_dot_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 2. dsinks[h] = -sum over (sequence, position) of exp(s_h - lse) D, summed in
-// a fixed order (strided per thread, then a tree), so it is deterministic.
-__global__ __launch_bounds__(BT) void bwd_dsink_kernel(BwdArgs a) {
+// 2. Per (sequence, head, block of SB positions): the log-sum-exp copied in
+// log2 units (as the exponentials take it), and the block's share of the sink
+// gradient, -sum exp(s_h - lse) D, summed in a fixed order (strided per
+// thread, then a tree).
+constexpr int SB = 1024;
+__global__ __launch_bounds__(BT) void bwd_rowstat_kernel(BwdArgs a) {
   __shared__ float red[BT];
-  const int h = blockIdx.x;
+  const int nsb = (a.S + SB - 1) / SB;
+  const int x = blockIdx.x;
+  const int sb = x % nsb;
+  const int bh = x / nsb;  // b * Hq + h
+  const int h = bh % a.Hq;
   const float s2 = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;
-  const int64_t n = (int64_t)a.B * a.S;
+  const int p_end = min(a.S, (sb + 1) * SB);
   float acc = 0.f;
-  for (int64_t i = threadIdx.x; i < n; i += BT) {
-    const int b = (int)(i / a.S);
-    const int64_t idx = ((int64_t)b * a.Hq + h) * a.S + (i - (int64_t)b * a.S);
-    acc -= fast_exp2(s2 - a.lse[idx] * kLog2e) * a.dlt[idx];
+  for (int p = sb * SB + threadIdx.x; p < p_end; p += BT) {
+    const int64_t idx = (int64_t)bh * a.S + p;
+    const float l2 = a.lse[idx] * kLog2e;
+    a.lse2[idx] = l2;
+    acc -= fast_exp2(s2 - l2) * a.dlt[idx];
   }
+  if (!a.dsinks) return;
   red[threadIdx.x] = acc;
   __syncthreads();
 #pragma unroll
@@ -103,7 +121,25 @@ __global__ __launch_bounds__(BT) void bwd_dsink_kernel(BwdArgs a) {
     if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) a.dsinks[h] = red[0] + 0.f;
+  if (threadIdx.x == 0) a.dsink_part[(int64_t)h * a.B * nsb + (int64_t)(bh / a.Hq) * nsb + sb] = red[0];
+}
+
+// dsinks[h]: the partial sums of its (sequence, block) pairs in order.
+__global__ __launch_bounds__(64) void bwd_dsink_kernel(BwdArgs a) {
+  const int h = blockIdx.x * 64 + threadIdx.x;
+  if (h >= a.Hq) return;
+  const int n = a.B * ((a.S + SB - 1) / SB);
+  float acc = 0.f;
+  for (int i = 0; i < n; ++i) acc += a.dsink_part[(int64_t)h * n + i];
+  a.dsinks[h] = acc + 0.f;
+}
+
+// Last query position that can see a key of the 64-key block starting at j0:
+// the sequence end, or the window of the block's last key unless the block
+// holds sink tokens (st: the sink tokens of a windowed layer, else 0).
+__device__ __forceinline__ int block_p_hi(int j0, int S, int W, int st) {
+  const int kmax = min(j0 + KB - 1, S - 1);
+  return (W > 0 && j0 >= st) ? min(S - 1, kmax + W - 1) : S - 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -135,29 +171,34 @@ __global__ __launch_bounds__(BT, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // round-robin over the 8 XCDs), the longest first: they stream the same
   // Q / dO rows out of that XCD's L2.
   const int U = a.B * a.Hkv;
-  int unit, kb;
+  const int per_unit = nkb * a.n_slabs;  // (slab, key block) jobs of one (sequence, KV head)
+  int unit, r;
   {
     const int x = blockIdx.x;
     if ((U & 7) == 0) {
       const int sidx = x >> 3;
-      kb = sidx % nkb;
-      unit = (x & 7) + 8 * (sidx / nkb);
+      r = sidx % per_unit;
+      unit = (x & 7) + 8 * (sidx / per_unit);
     } else {
-      kb = x / U;
+      r = x / U;
       unit = x % U;
     }
   }
+  const int slab = r / nkb;
+  const int kb = r - slab * nkb;
   const int b = unit / a.Hkv;
   const int g = unit - b * a.Hkv;
   const int st = STK && W > 0 ? a.sink_tokens : 0;
   const int j0 = kb * KB;
   const int jw = j0 + 32 * kh;  // this wave's first key
-  // queries that can see a key of the block: p >= j0, and within the window
-  // of the block's last key unless the block holds sink tokens
-  const int kmax = min(j0 + KB - 1, S - 1);
-  const int p_hi = (W > 0 && j0 >= st) ? min(S - 1, kmax + W - 1) : S - 1;
-  const int t_lo = j0 / QT;
-  const int n_qt = p_hi / QT - t_lo + 1;
+  // queries that can see a key of the block: p >= j0 up to p_hi; this
+  // workgroup takes those of its slab
+  const int p_hi = block_p_hi(j0, S, W, st);
+  const int s_lo = j0 / a.slab_len, s_hi = p_hi / a.slab_len;
+  if (slab < s_lo || slab > s_hi) return;  // uniform: the slab holds no query of the block
+  const bool partial = s_hi > s_lo;
+  const int t_lo = max(j0, slab * a.slab_len) / QT;
+  const int n_qt = min(p_hi, (slab + 1) * a.slab_len - 1) / QT - t_lo + 1;
   const int np = (G + 1) >> 1;  // head pairs
   const int n_units = n_qt * np;
 
@@ -174,35 +215,51 @@ __global__ __launch_bounds__(BT, 2) void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  // staging of unit u: wave w fills rows 16w .. 16w+15 of the Q and dO tiles
-  // (row R = head (R / 32) of the pair, query R % 32), 8 rows per load; wave 0
-  // also loads lse and D (lane l: head l / 32, query l % 32).  Rows past the
-  // sequence, and the missing second head of an odd group, repeat valid rows
-  // (they are masked, and the loads stay in bounds).
+  // Staging of a unit (q-tile t, head pair i): wave w fills rows 16w .. 16w+15
+  // of the Q and dO tiles (row R = head R / 32 of the pair, query R % 32), 8
+  // rows per load; wave 0 also loads lse (log2 units) and D (lane l: head
+  // l / 32, query l % 32).  Addresses are a scalar base per unit plus a
+  // per-lane 32-bit offset; on the last tile, and for the missing second head
+  // of an odd group, rows repeat valid ones (masked, and in bounds).
   const int64_t q_stride = (int64_t)a.Hq * kHeadDim;
   const int dma_chunk = ((lane & 7) ^ (lane >> 3)) * 8;
-  auto dma_unit = [&](int u, int buf) {
-    const int i = u % np;
-    const int q0 = (t_lo + u / np) * QT;
+  uint32_t qoff[2];
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii) {
+    const int R = 16 * wave + 8 * ii + (lane >> 3);
+    qoff[ii] = (uint32_t)((((R & 31) * a.Hq + (R >> 5)) * kHeadDim + dma_chunk) * 2);
+  }
+  const uint32_t loff = (uint32_t)((lg * S + lr) * 4);
+  auto dma_unit = [&](int t, int i, int buf) {
+    const int q0 = (t_lo + t) * QT;
+    const bool fast = q0 + QT <= S && 2 * i + 1 < G;  // uniform
+    const int64_t ubase = ((int64_t)b * S + q0) * q_stride + (int64_t)(g * G + 2 * i) * kHeadDim;
+    const char* qb = reinterpret_cast<const char*>(q + ubase);
+    const char* gb = reinterpret_cast<const char*>(dout + ubase);
     __bf16* qs = smem_b + (2 * buf) * TILE;
     __bf16* gs = smem_b + (2 * buf + 1) * TILE;
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
-      const int R = 16 * wave + 8 * ii + (lane >> 3);
-      const int hd = g * G + min(2 * i + (R >> 5), G - 1);
-      const int p = min(q0 + (R & 31), S - 1);
-      const int64_t off = ((int64_t)b * S + p) * q_stride + hd * kHeadDim + dma_chunk;
+      uint32_t off = qoff[ii];
+      if (!fast) {
+        const int R = 16 * wave + 8 * ii + (lane >> 3);
+        const int pr = min(q0 + (R & 31), S - 1) - q0;
+        const int e = min(2 * i + (R >> 5), G - 1) - 2 * i;
+        off = (uint32_t)(((pr * a.Hq + e) * kHeadDim + dma_chunk) * 2);
+      }
       const int lofs = (16 * wave + 8 * ii) * RS;  // wave-uniform slice of 8 rows
-      __builtin_amdgcn_global_load_lds((const void*)(q + off), (lds_void*)(qs + lofs), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(dout + off), (lds_void*)(gs + lofs), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(qb + off), (lds_void*)(qs + lofs), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(gb + off), (lds_void*)(gs + lofs), 16, 0, 0);
     }
     if (wave == 0) {
-      const int hd = g * G + min(2 * i + lg, G - 1);
-      const int p = min(q0 + lr, S - 1);
-      const int64_t idx = ((int64_t)b * a.Hq + hd) * S + p;
+      const int64_t lbase = ((int64_t)b * a.Hq + g * G + 2 * i) * S + q0;
+      uint32_t off = loff;
+      if (!fast) off = (uint32_t)(((min(2 * i + lg, G - 1) - 2 * i) * S + min(q0 + lr, S - 1) - q0) * 4);
       float* ls = smem_f + buf * 4 * QT;
-      __builtin_amdgcn_global_load_lds((const void*)(a.lse + idx), (lds_void*)(ls), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(a.dlt + idx), (lds_void*)(ls + 2 * QT), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(a.lse2 + lbase) + off),
+                                       (lds_void*)(ls), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(a.dlt + lbase) + off),
+                                       (lds_void*)(ls + 2 * QT), 4, 0, 0);
     }
   };
 
@@ -216,25 +273,54 @@ __global__ __launch_bounds__(BT, 2) void bwd_dkdv_kernel(BwdArgs a) {
   tr_offsets(lane, vofs);
   const float c = a.scale_log2;
 
-  if (n_units > 0) dma_unit(0, 0);
-  if (n_units > 1) dma_unit(1, 1);
-  for (int u = 0; u < n_units; ++u) {
-    const int buf = u % NBUF;
-    // unit u (issued two units ago) has landed for every wave; the buffer of
-    // unit u-1 is free again
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-    if (u + 2 < n_units) dma_unit(u + 2, (u + 2) % NBUF);
-    const int i = u % np;
-    const int q0 = (t_lo + u / np) * QT;
-    if (2 * i + hh >= G) continue;
+  // unit u = (q-tile t, head pair i), i fastest; (t, i) of the unit being
+  // computed and (t2, i2) of the one being staged two ahead
+  int t = 0, i = 0, t2 = 0, i2 = 0;
+  auto advance = [&](int& tt, int& ip) {
+    if (++ip == np) {
+      ip = 0;
+      ++tt;
+    }
+  };
+  if (n_units > 0) {
+    dma_unit(t2, i2, 0);
+    advance(t2, i2);
+  }
+  if (n_units > 1) {
+    dma_unit(t2, i2, 1);
+    advance(t2, i2);
+  }
+  // One body per LDS buffer (unit u lives in buffer u % 3), so that the LDS
+  // addresses are compile-time offsets.
+  auto body = [&](auto bufc, int u) {
+    constexpr int BUF = decltype(bufc)::value;
+    // Unit u (staged two units ago) has landed for every wave; the buffer of
+    // unit u-1 is free again.  Vector memory loads complete in issue order, so
+    // waiting until only unit u+1's loads of this wave (4, and 2 more on wave
+    // 0) are outstanding leaves them a whole unit more to land.  The LDS reads
+    // of unit u-1 are complete too (lgkmcnt 0) before the barrier.
+    if (u + 1 < n_units) {
+      if (wave == 0) __builtin_amdgcn_s_waitcnt(0x0070 | 6);
+      else __builtin_amdgcn_s_waitcnt(0x0070 | 4);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0070);
+    }
+    asm volatile("s_barrier" ::: "memory");
+    if (u + 2 < n_units) {
+      dma_unit(t2, i2, (BUF + 2) % NBUF);
+      advance(t2, i2);
+    }
+    const int q0 = (t_lo + t) * QT;
+    const int ip = i;
+    advance(t, i);
+    if (2 * ip + hh >= G) return;
     // (queries q0 .. q0+31) x (keys jw .. jw+31): nothing visible, all
     // visible, or compared element by element
-    if (q0 + QT - 1 < jw || q0 >= S || (W > 0 && jw >= st && q0 - W >= jw + 31)) continue;
+    if (q0 + QT - 1 < jw || q0 >= S || (W > 0 && jw >= st && q0 - W >= jw + 31)) return;
     const bool full = q0 >= jw + 31 && q0 + QT - 1 < S && (W <= 0 || q0 + QT - 1 - W < jw || jw + 31 < st);
 
-    const __bf16* qs = smem_b + (2 * buf) * TILE + hh * QT * RS;
-    const __bf16* gs = smem_b + (2 * buf + 1) * TILE + hh * QT * RS;
+    const __bf16* qs = smem_b + (2 * BUF) * TILE + hh * QT * RS;
+    const __bf16* gs = smem_b + (2 * BUF + 1) * TILE + hh * QT * RS;
     f32x16 s, dp;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -244,11 +330,11 @@ __global__ __launch_bounds__(BT, 2) void bwd_dkdv_kernel(BwdArgs a) {
       dp = mfma32(ga, vop[kk], kk == 0 ? zero16() : dp);
     }
     // register r: query q0 + 8(r/4) + 4lg + r%4, key jw + lr
-    const float* ls = smem_f + buf * 4 * QT + hh * QT + 4 * lg;
+    const float* ls = smem_f + BUF * 4 * QT + hh * QT + 4 * lg;
     f32x4 l4[4], d4[4];
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
-      l4[a4] = *reinterpret_cast<const f32x4*>(ls + 8 * a4) * kLog2e;
+      l4[a4] = *reinterpret_cast<const f32x4*>(ls + 8 * a4);
       d4[a4] = *reinterpret_cast<const f32x4*>(ls + 2 * QT + 8 * a4);
     }
     if (!full) {
@@ -288,9 +374,21 @@ __global__ __launch_bounds__(BT, 2) void bwd_dkdv_kernel(BwdArgs a) {
         dv[dt] = mfma32(pa[uu], gt, dv[dt]);
         dk[dt] = mfma32(da[uu], qt, dk[dt]);
       }
+  };
+  std::integral_constant<int, 0> B0;
+  std::integral_constant<int, 1> B1;
+  std::integral_constant<int, 2> B2;
+  int u = 0;
+  for (; u + NBUF <= n_units; u += NBUF) {
+    body(B0, u);
+    body(B1, u + 1);
+    body(B2, u + 2);
   }
+  if (u < n_units) body(B0, u);
+  if (u + 1 < n_units) body(B1, u + 1);
 
   // ---- the two head halves add up through LDS; rows leave as 16-byte chunks
+  // (bf16), or as fp32 partial sums of this slab
   __syncthreads();  // every wave is done with the staging buffers (no loads in flight)
   float* red = reinterpret_cast<float*>(smem_b);  // [kh][dK, dV][32 keys][64] fp32: 32 KB
   __bf16* outt = smem_b + 2 * 2 * 32 * 64 * 2;     // [dK, dV][64 keys][64] bf16: 16 KB
@@ -298,21 +396,37 @@ __global__ __launch_bounds__(BT, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 8 * (r >> 2) + 4 * lg + (r & 3);
-        red[((kh * 2 + 0) * 32 + key) * 64 + 32 * dt + lr] = dk[dt][r];
-        red[((kh * 2 + 1) * 32 + key) * 64 + 32 * dt + lr] = dv[dt][r];
+      for (int rr = 0; rr < 16; ++rr) {
+        const int key = 8 * (rr >> 2) + 4 * lg + (rr & 3);
+        red[((kh * 2 + 0) * 32 + key) * 64 + 32 * dt + lr] = dk[dt][rr];
+        red[((kh * 2 + 1) * 32 + key) * 64 + 32 * dt + lr] = dv[dt][rr];
       }
   }
   __syncthreads();
+  if (partial) {
+    if (hh == 0) {
+      // [dK, dV][64 keys][64] fp32 of (sequence, KV head, key block, slab)
+      float* pp = a.part + ((((int64_t)unit * nkb + kb) * a.n_slabs + slab) * 2) * (KB * kHeadDim);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int key = 8 * (rr >> 2) + 4 * lg + (rr & 3);
+          const int e = (32 * kh + key) * 64 + 32 * dt + lr;
+          pp[e] = (dk[dt][rr] + red[((kh * 2 + 0) * 32 + key) * 64 + 32 * dt + lr]) * a.scale;
+          pp[KB * kHeadDim + e] = dv[dt][rr] + red[((kh * 2 + 1) * 32 + key) * 64 + 32 * dt + lr];
+        }
+    }
+    return;
+  }
   if (hh == 0) {
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 8 * (r >> 2) + 4 * lg + (r & 3);
-        const float xk = (dk[dt][r] + red[((kh * 2 + 0) * 32 + key) * 64 + 32 * dt + lr]) * a.scale;
-        const float xv = dv[dt][r] + red[((kh * 2 + 1) * 32 + key) * 64 + 32 * dt + lr];
+      for (int rr = 0; rr < 16; ++rr) {
+        const int key = 8 * (rr >> 2) + 4 * lg + (rr & 3);
+        const float xk = (dk[dt][rr] + red[((kh * 2 + 0) * 32 + key) * 64 + 32 * dt + lr]) * a.scale;
+        const float xv = dv[dt][rr] + red[((kh * 2 + 1) * 32 + key) * 64 + 32 * dt + lr];
         outt[(32 * kh + key) * 64 + 32 * dt + lr] = (__bf16)xk;
         outt[(64 + 32 * kh + key) * 64 + 32 * dt + lr] = (__bf16)xv;
       }
@@ -327,6 +441,45 @@ __global__ __launch_bounds__(BT, 2) void bwd_dkdv_kernel(BwdArgs a) {
       __bf16* dst = (tsr ? dvp : dkp) + ((int64_t)b * S + j) * kv_stride + g * kHeadDim + 8 * ch;
       *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(outt + (tsr * 64 + row) * 64 + 8 * ch);
     }
+  }
+}
+
+// 3b. dK, dV of the key blocks split into several slabs: the fp32 partials
+// added in slab order and rounded to bf16.  One workgroup per (sequence, KV
+// head, key block); blocks with a single slab were written directly.
+template <bool STK>
+__global__ __launch_bounds__(BT) void bwd_dkdv_reduce_kernel(BwdArgs a) {
+  const int S = a.S, W = a.window;
+  const int nkb = (S + KB - 1) / KB;
+  const int x = blockIdx.x;
+  const int unit = x / nkb;
+  const int kb = x - unit * nkb;
+  const int st = STK && W > 0 ? a.sink_tokens : 0;
+  const int j0 = kb * KB;
+  const int s_lo = j0 / a.slab_len, s_hi = block_p_hi(j0, S, W, st) / a.slab_len;
+  if (s_hi == s_lo) return;
+  const int b = unit / a.Hkv;
+  const int g = unit - b * a.Hkv;
+  const float* base = a.part + (((int64_t)unit * nkb + kb) * a.n_slabs) * 2 * (KB * kHeadDim);
+  const int64_t kv_stride = (int64_t)a.Hkv * kHeadDim;
+  // chunk c: tensor c / 512, key (c / 8) % 64, d 8 * (c % 8) .. +7
+  for (int c = threadIdx.x; c < 2 * KB * 8; c += BT) {
+    const int tsr = c >> 9, row = (c >> 3) & 63, ch = c & 7;
+    const int j = j0 + row;
+    if (j >= S) continue;
+    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+    for (int sl = s_lo; sl <= s_hi; ++sl) {
+      const float* src = base + ((int64_t)sl * 2 + tsr) * (KB * kHeadDim) + row * kHeadDim + 8 * ch;
+      lo += *reinterpret_cast<const f32x4*>(src);
+      hi += *reinterpret_cast<const f32x4*>(src + 4);
+    }
+    u32x4 w;
+    w[0] = pack_bf16x2(lo[0], lo[1]);
+    w[1] = pack_bf16x2(lo[2], lo[3]);
+    w[2] = pack_bf16x2(hi[0], hi[1]);
+    w[3] = pack_bf16x2(hi[2], hi[3]);
+    __bf16* dst = reinterpret_cast<__bf16*>(tsr ? a.dv : a.dk) + ((int64_t)b * S + j) * kv_stride + g * kHeadDim + 8 * ch;
+    *reinterpret_cast<u32x4*>(dst) = w;
   }
 }
 
@@ -406,7 +559,7 @@ __global__ __launch_bounds__(BT, 2) void bwd_dq_kernel(BwdArgs a) {
       gb[i][kk] = __builtin_bit_cast(bf16x8, y);
     }
     const int64_t li = ((int64_t)b * a.Hq + nt_hq[i]) * S + t;
-    l2[i] = ok ? a.lse[li] * kLog2e : 0.f;
+    l2[i] = ok ? a.lse2[li] : 0.f;
     dl[i] = ok ? a.dlt[li] : 0.f;
   }
   f32x16 acc[2][2];
@@ -591,14 +744,31 @@ __global__ __launch_bounds__(BT) void bwd_dkdv_fp32_kernel(BwdArgs a) {
 
 }  // namespace
 
+// Slabs per key block: enough (slab, key block) jobs for about 4096 workgroups
+// (8 per slot of a 256-CU chip at 2 workgroups per CU), at most 4 slabs.
+// Windowed layers without sink tokens give every key block the same short
+// query range, so they are never cut.
+void backward_plan(int B, int S, int Hkv, int window, int sink_tokens, int* n_slabs, int* slab_len) {
+  const int64_t jobs = (int64_t)B * Hkv * ((S + KB - 1) / KB);
+  int n = 1;
+  if (jobs > 0 && jobs < 4096 && !(window > 0 && sink_tokens == 0))
+    n = (int)std::min<int64_t>(4, (4096 + jobs - 1) / jobs);
+  int len = ((S + n - 1) / n + QT - 1) / QT * QT;
+  if (len < QT) len = QT;
+  *slab_len = len;
+  *n_slabs = (S + len - 1) / len > 1 ? (S + len - 1) / len : 1;
+}
+
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.S;
   if (rows > 0) {
     const int64_t blocks = (rows + BT / 64 - 1) / (BT / 64);
     if (a.fp32) hipLaunchKernelGGL(bwd_dot_kernel<float>, dim3((unsigned)blocks), dim3(BT), 0, s, a);
     else hipLaunchKernelGGL(bwd_dot_kernel<__bf16>, dim3((unsigned)blocks), dim3(BT), 0, s, a);
+    const int64_t nrs = (int64_t)a.B * a.Hq * ((a.S + SB - 1) / SB);
+    hipLaunchKernelGGL(bwd_rowstat_kernel, dim3((unsigned)nrs), dim3(BT), 0, s, a);
   }
-  if (a.dsinks) hipLaunchKernelGGL(bwd_dsink_kernel, dim3(a.Hq), dim3(BT), 0, s, a);
+  if (a.dsinks) hipLaunchKernelGGL(bwd_dsink_kernel, dim3((a.Hq + 63) / 64), dim3(64), 0, s, a);
   if (rows == 0) return hipGetLastError();
   if (a.fp32) {
     const int64_t nq = (rows * a.Hq + 3) / 4, nk = (rows * a.Hkv + 3) / 4;
@@ -608,14 +778,17 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   }
   const bool stk = a.window > 0 && a.sink_tokens > 0;
   const int nkb = (a.S + KB - 1) / KB;
-  const unsigned g1 = (unsigned)((int64_t)a.B * a.Hkv * nkb);
+  const unsigned g1 = (unsigned)((int64_t)a.B * a.Hkv * nkb * a.n_slabs);
+  const unsigned g1r = (unsigned)((int64_t)a.B * a.Hkv * nkb);
   const int n_ntiles = ((a.S + 31) / 32) * a.G;
   const unsigned g2 = (unsigned)((int64_t)a.B * a.Hkv * ((n_ntiles + NT_WG - 1) / NT_WG));
   if (stk) {
     hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3(g1), dim3(BT), 0, s, a);
+    if (a.n_slabs > 1) hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<true>, dim3(g1r), dim3(BT), 0, s, a);
     hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3(g2), dim3(BT), 0, s, a);
   } else {
     hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3(g1), dim3(BT), 0, s, a);
+    if (a.n_slabs > 1) hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<false>, dim3(g1r), dim3(BT), 0, s, a);
     hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3(g2), dim3(BT), 0, s, a);
   }
   return hipGetLastError();

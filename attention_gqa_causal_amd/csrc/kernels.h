@@ -120,6 +120,11 @@ struct BwdArgs {
   void* dv;
   float* dsinks;       // [Hq] or NULL
   float* dlt;          // workspace [B, Hq, S]: <dO, o>
+  float* lse2;         // workspace [B, Hq, S]: lse * log2(e)
+  float* dsink_part;   // workspace [Hq, B, ceil(S / 1024)]: block sums of the sink gradient
+  float* part;         // workspace [B*Hkv, key blocks of 64, n_slabs, 2, 64, 64] fp32 (n_slabs > 1)
+  int n_slabs;         // the query range of a key block is cut at multiples of slab_len
+  int slab_len;        // a multiple of 32
   int B, S, Hq, Hkv, G;
   int window;
   int sink_tokens;
@@ -135,5 +140,6 @@ hipError_t launch_fp32(const Fp32Args& a, int kv_mode, hipStream_t s);
 hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t s);
 hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s);
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
+void backward_plan(int B, int S, int Hkv, int window, int sink_tokens, int* n_slabs, int* slab_len);  // split of the dK/dV query ranges
 
 }  // namespace gqa

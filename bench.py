@@ -15,7 +15,10 @@ already resident in HBM:
      for B64 and for B4096 (the B4096 rings hold as many bytes as the dense
      B64 x 8192 cache);
   5. rotary encoding of new rows fused with their KV-cache append: the 4096
-     rows of the layer-shaped prefill, and a decode step of 64 sequences.
+     rows of the layer-shaped prefill, and a decode step of 64 sequences;
+  6. backward of the layer-shaped prefill (dq, dk, dv, dsinks from dL/dout,
+     the forward's output and log-sum-exp), dense and window 128: algorithmic
+     work 10*D*Hq per visible pair (the five matrix products S, dP, dV, dK, dQ).
 `value` is the prefill throughput of the layer pair (1), in algorithmic
 TFLOP/s (4*D*Hq per visible query-key pair), timed with HIP events on the
 stream the kernels run on; every stage's own time, TFLOP/s, GB/s and roofline
@@ -341,6 +344,30 @@ def add_ring(stages, gq, up, i32, f32, dev):
                 flop=0, bytes=4 * B * row, bound="hbm")
 
 
+def add_backward(stages, gq, p, up, f32, dev):
+    import torch
+
+    import gqa_inputs as gi
+
+    B, S, Hq, D = p.q.shape
+    Hkv = p.k.shape[2]
+    q, k, v = up(p.q), up(p.k), up(p.v)
+    sinks = f32(p.sinks)
+    dout = up(gi.make_tensor(2, gi.T_DOUT, p.q.shape, 1.0, "bf16"))
+    ws = torch.empty((gq.backward_workspace_size(B, S, Hq, Hkv, D),), dtype=torch.uint8, device=dev)
+    for name, W in (("backward_dense", 0), ("backward_swa128", 128)):
+        out, lse = gq.attn_prefill(q, k, v, sinks, window=W, return_lse=True)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                 torch.empty((Hq,), dtype=torch.float32, device=dev))
+        flop, _ = prefill_work(B, S, Hq, Hkv, D, W)
+        # reads q, k, v, out, dout, lse; writes dq, dk, dv
+        byts = 2 * (3 * B * S * Hq * D + 4 * B * S * Hkv * D) + 4 * B * Hq * S
+        stages[name] = dict(
+            fn=(lambda out=out, lse=lse, grads=grads, W=W: gq.attn_prefill_backward(
+                q, k, v, sinks, out, lse, dout, window=W, workspace=ws, grads=grads)),
+            flop=flop * 10 // 4, bytes=byts, bound="mfma" if W == 0 else "hbm")
+
+
 def add_rope(stages, gq, up, i32, dev):
     import torch
 
@@ -448,6 +475,9 @@ def main():
     # 5. rotary encoding fused with the KV append
     if wanted("rope"):
         add_rope(stages, gq, up, i32, dev)
+    # 6. backward of the layer-shaped prefill
+    if wanted("backward"):
+        add_backward(stages, gq, gi.c2_layer(), up, f32, dev)
     if args.long:
         long_stages = {}
         add_prefill(long_stages, gq, gi.c4_prefill(), up, f32, dev)
@@ -524,7 +554,8 @@ def main():
             "workload": "layer-shaped prefill B1 S4096 Hq64 Hkv8 D64 bf16, dense layer then 128-token sliding-window "
                         "layer (value); each step also runs batched decode B64 cache 8192 (dense, window 128) and "
                         "ragged+paged 16 sequences (dense, window 128), and a windowed layer's 128-slot ring cache (append B64; "
-                        "decode B64 and B4096), and the rotary encoding + KV append of the prefill rows and of a decode step",
+                        "decode B64 and B4096), the rotary encoding + KV append of the prefill rows and of a decode step, "
+                        "and the backward of the layer-shaped prefill (dense, window 128)",
             "global_batch": 1,
             "seq_len": 4096,
             "parallelism": "single GPU",

@@ -267,7 +267,10 @@ int gqa_rope_append(const void* q, const void* k, const void* v, void* q_out,
  *   dsinks [Hq] fp32 output, or NULL (not computed); zeros when sinks is NULL
  * dq, dk, dv are written whole (no accumulation into them) in the dtype of
  * the inputs.  workspace: at least gqa_attn_prefill_backward_workspace_size
- * bytes of device memory, owned by the caller, clobbered by the call.  The
+ * bytes of device memory, owned by the caller, clobbered by the call (it
+ * holds <dL/dout, out> per row and head, and, when there are few key blocks
+ * to spread over the chip, fp32 partial sums of dk and dv: 64 MB for
+ * B1 S4096 with 8 KV heads).  The
  * result is deterministic (no atomics).  B == 0 or S == 0 writes only dsinks
  * (zeros).  Errors as for every entry point; GQA_ERR_WORKSPACE when the
  * workspace is missing or small.

@@ -272,7 +272,7 @@ def backward(L, B=1, S=16, Hq=64, Hkv=8, D=64, window=0, sink_tokens=0, scale=0.
     (dict(dout=None), -1),
     (dict(dq=None), -1),
     (dict(ws=None), -3),
-    (dict(ws_bytes=16 * 64 * 4 - 1), -3),
+    (dict(ws_bytes=1024), -3),
 ])
 def test_backward_rejects(L, kw, code):
     assert backward(L, **kw) == code
@@ -280,10 +280,17 @@ def test_backward_rejects(L, kw, code):
 
 
 def test_backward_workspace_size(L):
-    # one fp32 per (sequence, head, position), rounded up to 256 bytes
-    assert L.gqa_attn_prefill_backward_workspace_size(1, 16, 64, 8, 64, 0) == 16 * 64 * 4
-    assert L.gqa_attn_prefill_backward_workspace_size(2, 4096, 64, 8, 64, 0) == 2 * 4096 * 64 * 4
-    assert L.gqa_attn_prefill_backward_workspace_size(1, 3, 1, 1, 64, 1) == 256
+    # two fp32 per (sequence, head, position) and one per (head, sequence, 1024
+    # positions), each array rounded up to 256 bytes; with few
+    # 64-key blocks (under 4096 per call) bf16 adds fp32 dK/dV partials for up
+    # to 4 query slabs of every block
+    part = 2 * 64 * 64 * 4
+    ws = L.gqa_attn_prefill_backward_workspace_size
+    assert ws(1, 16, 64, 8, 64, 1) == 2 * 16 * 64 * 4 + 256
+    assert ws(1, 4096, 64, 8, 64, 0) == 2 * 4096 * 64 * 4 + 4 * 64 * 4 + 8 * 64 * 4 * part
+    assert ws(8, 4096, 64, 8, 64, 0) == 2 * 8 * 4096 * 64 * 4 + 8 * 4 * 64 * 4  # 4096 key blocks: no slabs
+    assert ws(1, 100, 64, 8, 64, 0) == 2 * 100 * 64 * 4 + 256 + 8 * 2 * 4 * part
+    assert ws(1, 3, 1, 1, 64, 1) == 3 * 256
     assert L.gqa_attn_prefill_backward_workspace_size(1, 16, 64, 8, 32, 0) == 0
     assert L.gqa_attn_prefill_backward_workspace_size(1, 16, 12, 8, 64, 0) == 0
 
