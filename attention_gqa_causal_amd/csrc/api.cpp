@@ -179,6 +179,14 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, const float* s
   a.skip_single = 0;
   a.lse_sb = (int64_t)Hq * S; a.lse_sh = S; a.lse_row0 = 0;
   if ((long long)B * Hkv * a.wg_per_seq > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
+  // Causal layers with two to four tile groups per slot (2 workgroups per CU)
+  // pair a heavy and a light group per workgroup; with more groups the
+  // dispatch order balances by itself, and windowed layers give every group
+  // about the same work.
+  const bool dense_like = window == 0 || window >= S;
+  const long long groups = (long long)B * Hkv * a.wg_per_seq;
+  a.paired = dense_like && sink_tokens == 0 && groups >= 4LL * num_cus() && groups < 8LL * num_cus() &&
+             env_int("GQA_PREFILL_PAIRED", 1);
   hipError_t e = launch_prefill_bf16(a, KV_BATCHED, false, st);
   return e == hipSuccess ? ok() : hip_fail(e, "prefill bf16 launch");
 }

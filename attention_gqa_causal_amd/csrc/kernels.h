@@ -24,6 +24,7 @@ struct PrefillArgs {
   int64_t lse_sb;    // lse index = b*lse_sb + h*lse_sh + t (+ q_row0 when lse_row0)
   int64_t lse_sh;
   int lse_row0;
+  int paired;        // each workgroup runs a heavy and a light tile group in turn (batched causal prefill)
 };
 
 // Decode-style attention: one query token per sequence, KV split over

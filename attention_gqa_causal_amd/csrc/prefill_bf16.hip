@@ -160,12 +160,13 @@ __device__ __forceinline__ float refit_half(f32x16& s, bf16x8 (&pb)[2], float& m
   return exp_half(s, pb, m, c);
 }
 
-// STK: the layer keeps start-of-sequence sink tokens visible past its window
-// (a separate instantiation, so that other layers carry none of its code).
+// One job: the tile group x of the dispatch order (see below) of one
+// (sequence, KV head).  STK: the layer keeps start-of-sequence sink tokens
+// visible past its window (a separate instantiation, so that other layers
+// carry none of its code).
 template <int MODE, bool VARLEN, bool STK>
-__global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[NBUF][BK * RS];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[NBUF][BK * RS];
+__device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, __bf16 (*Ks)[BK * RS],
+                                            __bf16 (*Vs)[BK * RS]) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -180,7 +181,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   const int U = a.B * a.Hkv;
   int unit, rank;
   {
-    const int x = blockIdx.x;
     if ((U & 7) == 0) {
       const int sidx = x >> 3;
       rank = sidx % a.wg_per_seq;
@@ -464,13 +464,55 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   }
 }
 
+template <int MODE, bool VARLEN, bool STK>
+__global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[NBUF][BK * RS];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[NBUF][BK * RS];
+  prefill_job<MODE, VARLEN, STK>(a, blockIdx.x, Ks, Vs);
+}
+
+// Under the causal mask the tile groups of a sequence carry work in
+// proportion to their position.  When there are between two and four of them
+// per slot of the chip (2 workgroups per CU), the last ones to start run
+// alone at the end; then a workgroup takes two jobs in turn, the k-th heaviest
+// and the k-th lightest of its XCD's list, so every workgroup carries the same
+// work.  A kernel of its own, so that the one-job kernel keeps its registers.
+__global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_paired_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[NBUF][BK * RS];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[NBUF][BK * RS];
+  const int total = a.B * a.Hkv * a.wg_per_seq;
+  int x = blockIdx.x, j2;
+  if (((a.B * a.Hkv) & 7) == 0) {  // jobs of XCD c are c + 8m, m = 0 .. M-1, heaviest first
+    const int c = blockIdx.x & 7, m = blockIdx.x >> 3, M = total >> 3;
+    x = c + 8 * m;
+    j2 = c + 8 * (M - 1 - m);
+  } else {
+    j2 = total - 1 - blockIdx.x;
+  }
+  int x2 = j2 != x ? j2 : -1;  // the middle job of an odd list runs once
+  // one call site, so that the job is inlined once
+  for (;;) {
+    prefill_job<KV_BATCHED, false, false>(a, x, Ks, Vs);
+    if (x2 < 0) break;
+    __syncthreads();  // every wave is done with the LDS buffers
+    x = x2;
+    x2 = -1;
+  }
+}
+
 }  // namespace
 
 int prefill_ntiles_per_wg() { return NT_WG; }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int kv_mode, bool varlen_q, hipStream_t s) {
-  const int grid = a.B * a.Hkv * a.wg_per_seq;
+  int grid = a.B * a.Hkv * a.wg_per_seq;
   if (grid <= 0) return hipSuccess;
+  if (a.paired) {
+    if (kv_mode != KV_BATCHED || varlen_q || (a.window > 0 && a.sink_tokens > 0)) return hipErrorInvalidValue;
+    grid = ((a.B * a.Hkv) & 7) == 0 ? 8 * ((grid / 8 + 1) / 2) : (grid + 1) / 2;
+    hipLaunchKernelGGL(prefill_bf16_paired_kernel, dim3(grid), dim3(NTHREADS), 0, s, a);
+    return hipGetLastError();
+  }
   const bool stk = a.window > 0 && a.sink_tokens > 0;
 #define GQA_LAUNCH(M, V)                                                                               \
   do {                                                                                                 \
