@@ -81,6 +81,22 @@ def test_prefill_bf16_deterministic(device):
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2]) and torch.equal(outs[3], outs[4])
 
 
+@pytest.mark.parametrize("B,S,Hkv", [(1, 4096, 8), (1, 12000, 3)])
+def test_prefill_paired_equals_one_job_per_workgroup(device, monkeypatch, B, S, Hkv):
+    # the paired kernel (a heavy and a light tile group per workgroup) runs the
+    # same jobs in another order: results are bit-identical; the second shape
+    # has an odd job list (3 KV heads: no XCD grouping) with a middle job
+    p = gi.prefill_problem(2003, B, S, 8 * Hkv, Hkv, 64, "bf16", std=SQRT_HALF)
+    args = (dev_tensor(p.q, device), dev_tensor(p.k, device), dev_tensor(p.v, device), dev_f32(p.sinks, device))
+    say(f"prefill paired vs one job per workgroup B{B} S{S} Hkv{Hkv}")
+    monkeypatch.setenv("GQA_PREFILL_PAIRED", "0")
+    o0, l0 = gq.attn_prefill(*args, return_lse=True)
+    monkeypatch.setenv("GQA_PREFILL_PAIRED", "1")
+    o1, l1 = gq.attn_prefill(*args, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
 def test_prefill_empty(device):
     q = torch.empty((0, 16, 64, 64), dtype=torch.bfloat16, device=device)
     k = torch.empty((0, 16, 8, 64), dtype=torch.bfloat16, device=device)
