@@ -164,11 +164,15 @@ __device__ __forceinline__ float refit_half(f32x16& s, bf16x8 (&pb)[2], float& m
 // (sequence, KV head).  STK: the layer keeps start-of-sequence sink tokens
 // visible past its window (a separate instantiation, so that other layers
 // carry none of its code).
-template <int MODE, bool VARLEN, bool STK>
+template <int MODE, bool VARLEN, bool STK, bool IN_LOOP = false>
 __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, __bf16 (*Ks)[BK * RS],
                                             __bf16 (*Vs)[BK * RS]) {
 
-  const int tid = threadIdx.x;
+  // In the paired kernel the thread index passes through an empty asm so that
+  // lane-derived values are formed inside each job: hoisted out of its job
+  // loop they would stay live across it (and be spilled).
+  int tid = threadIdx.x;
+  if (IN_LOOP) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (lets per-wave values live in SGPRs)
   const int lr = lane & 31;  // row of the 32-wide MFMA tile this lane serves
@@ -492,7 +496,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_paired_kernel(Prefil
   int x2 = j2 != x ? j2 : -1;  // the middle job of an odd list runs once
   // one call site, so that the job is inlined once
   for (;;) {
-    prefill_job<KV_BATCHED, false, false>(a, x, Ks, Vs);
+    prefill_job<KV_BATCHED, false, false, true>(a, x, Ks, Vs);
     if (x2 < 0) break;
     __syncthreads();  // every wave is done with the LDS buffers
     x = x2;

@@ -169,7 +169,8 @@ def summarize_counters(fetch_dir, write_dir):
     f_scale = (f_copy * 1024.0) / COPY_BYTES  # counter bytes per true byte read
     w_scale = (w_copy * 1024.0) / COPY_BYTES
     res = {}
-    for kind, key, work in (("prefill", "prefill_bf16_kernel", prefill_work(1, 4096, 64, 8, 64, 0)),
+    # the dense B1 S4096 prefill runs the paired kernel (a heavy and a light tile group per workgroup)
+    for kind, key, work in (("prefill", "prefill_bf16_paired_kernel", prefill_work(1, 4096, 64, 8, 64, 0)),
                             ("decode", "decode_split_kernel", decode_work([8192] * 64, 64, 8, 64, 0))):
         fk, wk = pick(fetch, key), pick(write, key)
         rd = fk * 1024.0 / f_scale
@@ -575,7 +576,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(pd["tflops"] / PEAK_BF16_TFLOPS, 4),
             "traffic": load_traffic("prefill"),
-            "kernel": "prefill_bf16_kernel<KV_BATCHED> (dense, S4096)",
+            "kernel": "prefill_bf16_paired_kernel (dense, B1 S4096)",
         }
     if "decode_dense" in parts:
         dd = parts["decode_dense"]
