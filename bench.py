@@ -214,6 +214,73 @@ def summarize_counters(fetch_dir, write_dir):
     print("\n".join(lines))
 
 
+def _short_kernel_name(n):
+    """Kernel name without namespaces and argument lists."""
+    import re
+
+    if n.startswith("_Z"):  # mangled: keep the identifier and a rough template hint
+        m = re.search(r"N_1\d+(\w+?)(I|E)", n)
+        base = m.group(1) if m else n
+        base = re.sub(r"^\d+", "", base)
+        tmpl = re.search(r"I(.*)EEvNS", n)
+        return base + (f"<{tmpl.group(1)}>" if tmpl else "")
+    n = n.replace("void ", "").replace("gqa::(anonymous namespace)::", "")
+    return n.split("(")[0]
+
+
+def summarize_trace(trace_dir, out_md=None):
+    """Kernel-trace summary of one bench run: rocprofv3's per-kernel statistics, and
+    per-dispatch medians grouped by (kernel, grid size), which tells the stages of
+    one kernel apart."""
+    import csv
+    import glob
+    import statistics
+
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    trace = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not stats or not trace:
+        raise SystemExit(f"no kernel_stats.csv / kernel_trace.csv under {trace_dir}")
+    lines = ["# Kernel trace: one bench step (all stages)", "",
+             "Command (repository root, one MI355X):", "",
+             "    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o run -- "
+             "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline",
+             "    python3 bench.py --summarize-trace gpurun_out/prof_trace", "",
+             "Every stage runs 13 times (3 warm-up + 10 timed). rocprofv3 `--stats` summary (all stages of one kernel "
+             "pooled):", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    with open(stats[0]) as f:
+        for r in csv.DictReader(f):
+            lines.append(f"| `{_short_kernel_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                         f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                         f"{float(r['Percentage']):.1f} |")
+    groups = {}
+    with open(trace[0]) as f:
+        for r in csv.DictReader(f):
+            key = (_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])))
+            groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    # stages that launch one kernel on the same grid (dense and windowed layers)
+    # differ in duration: split such a group at its largest gap
+    rows = []
+    for (name, wgs), v in groups.items():
+        v = sorted(v)
+        parts = [v]
+        if len(v) >= 4 and v[-1] > 2 * v[0]:
+            gaps = [(v[i + 1] / max(v[i], 1e-9), i) for i in range(len(v) - 1)]
+            _, cut = max(gaps)
+            parts = [v[:cut + 1], v[cut + 1:]]
+        for part in parts:
+            rows.append((name, wgs, len(part), statistics.median(part)))
+    lines += ["", "Per-dispatch durations by (kernel, workgroups), median over the run (a group whose durations "
+              "fall into two clusters, e.g. the dense and the windowed layer on one grid, is shown as two rows):", "",
+              "| kernel | workgroups | dispatches | median us |", "|---|---|---|---|"]
+    for name, wgs, n, med in sorted(rows, key=lambda r: -r[3] * r[2]):
+        lines.append(f"| `{name}` | {wgs} | {n} | {med:.1f} |")
+    text = "\n".join(lines) + "\n"
+    with open(out_md or os.path.join(PROFILES, "kernel_trace_bench_step.md"), "w") as f:
+        f.write(text)
+    print(text)
+
+
 # ----------------------------------------------------------------------------- CPU oracle baseline
 
 def cpu_baseline(seconds: float):
@@ -419,10 +486,15 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="run only the dense prefill, the dense decode and a plain 256 MiB device copy "
                          "(3 dispatches each) for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="turn a rocprofv3 --kernel-trace --stats run into profiles/kernel_trace_bench_step.md")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn the two counter runs into profiles/traffic_*.json and profiles/hbm_traffic.md")
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
         return
