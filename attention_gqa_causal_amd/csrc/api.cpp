@@ -328,6 +328,7 @@ int gqa_attn_varlen_paged(const void* q, const void* k_cache, const void* v_cach
     a.wg_per_seq = (int)((ntiles + prefill_ntiles_per_wg() - 1) / prefill_ntiles_per_wg());
     a.skip_single = 1;
     a.lse_sb = 0; a.lse_sh = Tq; a.lse_row0 = 1;
+    a.sort_seq = B <= 256 && env_int("GQA_VARLEN_SORT", 1) != 0;
     if ((long long)B * Hkv * a.wg_per_seq > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
     hipError_t e = launch_prefill_bf16(a, mode, true, st);
     if (e != hipSuccess) return hip_fail(e, "varlen prefill launch");

@@ -25,6 +25,7 @@ struct PrefillArgs {
   int64_t lse_sh;
   int lse_row0;
   int paired;        // each workgroup runs a heavy and a light tile group in turn (batched causal prefill)
+  int sort_seq;      // ragged batches (B <= 256): dispatch the sequences with the most work first
 };
 
 // Decode-style attention: one query token per sequence, KV split over

@@ -64,6 +64,7 @@ constexpr int NTHREADS = 64 * NWAVES;
 constexpr int NT_WG = 2 * NWAVES;  // N-tiles per workgroup
 constexpr int NBUF = 3;         // K/V tiles resident in LDS: current, next, and the one being filled
 constexpr float kRefit = 0x1p32f;  // a lane's per-tile weight sum past this moves the reference max
+constexpr int kSortMax = NTHREADS;  // ragged batches up to this many sequences are dispatched longest first
 
 // S^T of key half h (keys 32h .. 32h+31 of the tile, one per MFMA row) for
 // both N-tiles; each K operand read from LDS feeds two MFMAs.
@@ -166,7 +167,7 @@ __device__ __forceinline__ float refit_half(f32x16& s, bf16x8 (&pb)[2], float& m
 // carry none of its code).
 template <int MODE, bool VARLEN, bool STK, bool IN_LOOP = false>
 __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, __bf16 (*Ks)[BK * RS],
-                                            __bf16 (*Vs)[BK * RS]) {
+                                            __bf16 (*Vs)[BK * RS], const int* order = nullptr) {
 
   // In the paired kernel the thread index passes through an empty asm so that
   // lane-derived values are formed inside each job: hoisted out of its job
@@ -195,8 +196,8 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
     }
   }
   const int tg = a.wg_per_seq - 1 - rank;
-  const int b = unit / a.Hkv;
-  const int g = unit - b * a.Hkv;
+  const int g = unit % a.Hkv;
+  const int b = order ? order[unit / a.Hkv] : unit / a.Hkv;  // ragged batches: longest sequences first
   const SeqView sv = seq_view<MODE>(a.seq, b, VARLEN);
   const int G = a.G;
   const int n_ntiles = ((sv.q_len + 31) >> 5) * G;
@@ -472,7 +473,38 @@ template <int MODE, bool VARLEN, bool STK>
 __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 Ks[NBUF][BK * RS];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[NBUF][BK * RS];
-  prefill_job<MODE, VARLEN, STK>(a, blockIdx.x, Ks, Vs);
+  const int* order = nullptr;
+  if constexpr (VARLEN) {
+    // Ragged batches: the sequences' tile groups carry work in proportion to
+    // their query and key counts, so the workgroups take the sequences from
+    // the most work to the least (as far as the dispatch order goes), instead
+    // of in batch order where a long sequence dispatched last runs alone at
+    // the end.  Every workgroup ranks the (at most kSortMax) sequences itself.
+    __shared__ float seq_w[kSortMax];
+    __shared__ int seq_order[kSortMax];
+    if (a.sort_seq) {
+      const int t = threadIdx.x;
+      const int B = a.B;
+      if (t < B) {
+        const SeqView sv = seq_view<MODE>(a.seq, t, true);
+        const int kl = a.window > 0 ? min(sv.kv_len, sv.q_len + a.window) : sv.kv_len;
+        seq_w[t] = (a.skip_single && sv.q_len <= 1) ? 0.f : (float)sv.q_len * (float)kl;
+      }
+      __syncthreads();
+      if (t < B) {
+        const float w = seq_w[t];
+        int r = 0;
+        for (int j = 0; j < B; ++j) {
+          const float wj = seq_w[j];
+          r += (wj > w) || (wj == w && j < t);
+        }
+        seq_order[r] = t;
+      }
+      __syncthreads();
+      order = seq_order;
+    }
+  }
+  prefill_job<MODE, VARLEN, STK>(a, blockIdx.x, Ks, Vs, order);  // one call site: inlined once
 }
 
 // Under the causal mask the tile groups of a sequence carry work in

@@ -323,6 +323,20 @@ def test_varlen_packed_and_permutation(device):
 
 
 @pytest.mark.parametrize("W", [0, 128])
+def test_varlen_longest_first_equals_batch_order(device, monkeypatch, W):
+    # ragged batches are dispatched longest sequence first; the batch order
+    # computes the same jobs, so the bits agree
+    p = gi.c5_ragged()
+    say(f"varlen longest-first vs batch order W={W}")
+    monkeypatch.setenv("GQA_VARLEN_SORT", "0")
+    o0, l0 = run_varlen(p, device, W)
+    monkeypatch.setenv("GQA_VARLEN_SORT", "1")
+    o1, l1 = run_varlen(p, device, W)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
+@pytest.mark.parametrize("W", [0, 128])
 def test_varlen_ragged_paged_sampled(device, W):
     """16 sequences, lengths U{128..8192}, 512-token chunks and decode steps, 16-token
     blocks under a permuted table (the ragged + paged workload)."""
