@@ -1,5 +1,6 @@
-"""GPU parity on the long-context workloads: prefill at S32768 and decode at
-B8 x 131072, both 64/8 heads bf16 N(0,1), dense and window 128.
+"""GPU parity on the long-context workloads: prefill (and its backward) at
+S32768 and decode at B8 x 131072, all 64/8 heads bf16 N(0,1), dense and window
+128.
 
 The oracle computes sampled outputs one by one (every head of the sampled
 query rows; every head of two whole decode sequences); properties that hold at
@@ -70,3 +71,50 @@ def test_decode_long_context(device, long_decode, W):
                                          gi.bf16_to_f64(d.v.store[sl]), d.seqlens[sl], d.sinks, W, d.scale)
         assert_bf16_close(got[sl], o_ref, f"sequence {b}")
         assert_lse_close(got_l[sl], l_ref, "lse")
+
+
+@pytest.mark.parametrize("W", [0, 128])
+def test_backward_long_context_sampled(device, long_prefill, W):
+    """Backward at S32768 (one slab per key block at this size).  The oracle's
+    single-head gradient routine on a subset of query rows is exact for dq of
+    those rows, and for dk, dv of the keys that only those rows see: the last
+    64 positions (every query that sees key j sits at j or later).  Other
+    sampled query rows check dq on their own."""
+    import oracle.backward as BW
+    from gpu_helpers import assert_grad_close
+
+    p = long_prefill
+    S = p.q.shape[1]
+    say(f"backward long context S{S} W={W}")
+    q, k, v = dev_tensor(p.q, device), dev_tensor(p.k, device), dev_tensor(p.v, device)
+    sinks = dev_f32(p.sinks, device)
+    dout = gi.make_tensor(4, gi.T_DOUT, p.q.shape, 1.0, "bf16")
+    out, lse = gq.attn_prefill(q, k, v, sinks, window=W, return_lse=True)
+    dq, dk, dv, _ = gq.attn_prefill_backward(q, k, v, sinks, out, lse, dev_tensor(dout, device), window=W)
+    torch.cuda.synchronize()
+    dq, dk, dv = to_f64(dq)[0], to_f64(dk)[0], to_f64(dv)[0]
+    for t in (dq, dk, dv):
+        assert np.isfinite(t).all()
+    tail = np.arange(S - 64, S)
+    rng = np.random.default_rng(200 + W)
+    early = sorted(set([0, 1, 127, 128, 4095] + [int(r) for r in rng.integers(0, S - 64, size=6)]))
+    qf, kf, vf, gf = p.q.f64[0], p.k.f64[0], p.v.f64[0], dout.f64[0]
+    k_pos = np.arange(S)
+    dq_ref_tail = np.zeros((64, 64, 64))
+    dq_ref_early = np.zeros((len(early), 64, 64))
+    dk_ref = np.zeros((64, 8, 64))
+    dv_ref = np.zeros((64, 8, 64))
+    for h in range(64):
+        g = oracle.kv_head(h, 64, 8)
+        gq_t, gk_t, gv_t, _, _, _ = BW.row_grads(qf[tail, h], kf[:, g], vf[:, g], tail, k_pos, p.sinks[h],
+                                                 gf[tail, h], W, p.scale)
+        dq_ref_tail[:, h] = gq_t
+        dk_ref[:, g] += gk_t[tail]
+        dv_ref[:, g] += gv_t[tail]
+        gq_e, _, _, _, _, _ = BW.row_grads(qf[early, h], kf[:, g], vf[:, g], early, k_pos, p.sinks[h],
+                                           gf[early, h], W, p.scale)
+        dq_ref_early[:, h] = gq_e
+    assert_grad_close(dq[tail], dq_ref_tail, "dq last 64 rows")
+    assert_grad_close(dq[early], dq_ref_early, "dq sampled rows")
+    assert_grad_close(dk[tail], dk_ref, "dk last 64 keys")
+    assert_grad_close(dv[tail], dv_ref, "dv last 64 keys")
