@@ -436,36 +436,49 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
     for (int t = pe; t < n_tiles; ++t) body(MSK, t);
   }
 
-  // ---- epilogue: normalise, round to bf16, store; log-sum-exp
+  // ---- epilogue: normalise, round to bf16, log-sum-exp.  A lane's registers
+  // hold 4-element pieces of 32 different rows, so the output tile goes
+  // through LDS and leaves as whole 128-byte rows (8 lanes per row, 16 bytes
+  // each) instead of 16 partial writes per row.
   // The row index is re-derived here behind an empty asm, so the compiler does
   // not keep the prologue's 64-bit Q row offset alive across the tile loops
   // (it would spill it).
   int lr_e = lr;
   asm volatile("" : "+v"(lr_e));
+  __syncthreads();  // every wave is done with the K/V tiles
+  __bf16* stg = wave < NBUF ? Ks[wave] : Vs[0];  // this wave's 64 rows: [N-tile][row][64]
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    if (!nt_valid[i]) continue;
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[i]), __float_as_uint(l_run[i]), false, false);
     const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const int t = nt_t0[i] + lr_e;
-    if (t >= sv.q_len) continue;
     const float inv = lt > 0.f ? 1.f / lt : (lt == 0.f ? 0.f : lt);
-    __bf16* op = a.out + ((sv.q_row0 + t) * a.Hq + nt_hq[i]) * (int64_t)kHeadDim;
+    const int row = 32 * i + lr_e;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int cq = 0; cq < 4; ++cq) {
-        const int d0 = 32 * dt + 8 * cq + 4 * lg;
         u32x2 v;
         v[0] = pack_bf16x2(o[i][dt][4 * cq + 0] * inv, o[i][dt][4 * cq + 1] * inv);
         v[1] = pack_bf16x2(o[i][dt][4 * cq + 2] * inv, o[i][dt][4 * cq + 3] * inv);
-        *reinterpret_cast<u32x2*>(op + d0) = v;
+        *reinterpret_cast<u32x2*>(stg + row * RS + kchunk(4 * dt + cq, row) + 4 * lg) = v;  // d = 32dt + 8cq + 4lg
       }
-    if (a.lse && lg == 0) {
+    const int t = nt_t0[i] + lr_e;
+    if (nt_valid[i] && t < sv.q_len && a.lse && lg == 0) {
       const float v = (lt == 0.f) ? -INFINITY : (m_run[i] + __log2f(lt)) * kLn2;
       const int64_t idx = (int64_t)b * a.lse_sb + (int64_t)nt_hq[i] * a.lse_sh + t + (a.lse_row0 ? sv.q_row0 : 0);
       a.lse[idx] = v;
     }
+  }
+  wave_lds_sync();  // the wave reads back only its own rows
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = j >> 2;                        // N-tile of rows 8j .. 8j+7
+    const int r = (lane >> 3) + 8 * (j & 3);     // row within the N-tile
+    const int cc = lane & 7;                     // 16-byte chunk of the row
+    const int t = nt_t0[i] + r;
+    if (!nt_valid[i] || t >= sv.q_len) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + (32 * i + r) * RS + kchunk(cc, r));
+    *reinterpret_cast<u32x4*>(a.out + ((sv.q_row0 + t) * a.Hq + nt_hq[i]) * (int64_t)kHeadDim + 8 * cc) = v;
   }
 }
 
