@@ -642,26 +642,36 @@ __global__ __launch_bounds__(BT, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   }
 
-  // ---- epilogue: dq = scale * acc, rounded to bf16
+  // ---- epilogue: dq = scale * acc, rounded to bf16; through LDS so that it
+  // leaves as whole 128-byte rows (a lane holds pieces of 32 rows)
   int lr_e = lr;
   asm volatile("" : "+v"(lr_e));
-  __bf16* dq = reinterpret_cast<__bf16*>(a.dq);
+  __syncthreads();  // every wave is done with the K/V tiles
+  __bf16* stg = wave < NBUF ? Ks[wave] : Vs[0];  // this wave's 64 rows: [N-tile][row][64]
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    if (!nt_valid[i]) continue;
-    const int t = nt_t0[i] + lr_e;
-    if (t >= S) continue;
-    __bf16* op = dq + (((int64_t)b * S + t) * a.Hq + nt_hq[i]) * kHeadDim;
+    const int row = 32 * i + lr_e;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int cq = 0; cq < 4; ++cq) {
-        const int d0 = 32 * dt + 8 * cq + 4 * lg;
         u32x2 w;
         w[0] = pack_bf16x2(acc[i][dt][4 * cq + 0] * a.scale, acc[i][dt][4 * cq + 1] * a.scale);
         w[1] = pack_bf16x2(acc[i][dt][4 * cq + 2] * a.scale, acc[i][dt][4 * cq + 3] * a.scale);
-        *reinterpret_cast<u32x2*>(op + d0) = w;
+        *reinterpret_cast<u32x2*>(stg + row * RS + kchunk(4 * dt + cq, row) + 4 * lg) = w;  // d = 32dt + 8cq + 4lg
       }
+  }
+  wave_lds_sync();  // the wave reads back only its own rows
+  __bf16* dq = reinterpret_cast<__bf16*>(a.dq);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = j >> 2;                     // N-tile of rows 8j .. 8j+7
+    const int r = (lane >> 3) + 8 * (j & 3);  // row within the N-tile
+    const int cc = lane & 7;                  // 16-byte chunk of the row
+    const int t = nt_t0[i] + r;
+    if (!nt_valid[i] || t >= S) continue;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(stg + (32 * i + r) * RS + kchunk(cc, r));
+    *reinterpret_cast<u32x4*>(dq + (((int64_t)b * S + t) * a.Hq + nt_hq[i]) * kHeadDim + 8 * cc) = w;
   }
 }
 
