@@ -590,11 +590,18 @@ __global__ __launch_bounds__(BT, 2) void bwd_dq_kernel(BwdArgs a) {
 
   if (n_tiles > 0) dma_tile(0, 0);
   if (n_tiles > 1) dma_tile(1, 1);
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t % NBUF;
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-    if (t + 2 < n_tiles) dma_tile(t + 2, (t + 2) % NBUF);
+  // One body per LDS buffer (tile t lives in buffer t % 3): compile-time LDS
+  // offsets.
+  auto body = [&](auto bufc, int t) {
+    constexpr int BUF = decltype(bufc)::value;
+    // Tile t (staged two tiles ago) has landed for every wave once only tile
+    // t+1's loads of this wave (4) are in flight (vector loads complete in
+    // issue order); the LDS reads of tile t-1 are done before its buffer takes
+    // tile t+2.
+    if (t + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0070 | 4);
+    else __builtin_amdgcn_s_waitcnt(0x0070);
+    asm volatile("s_barrier" ::: "memory");
+    if (t + 2 < n_tiles) dma_tile(t + 2, (BUF + 2) % NBUF);
     const int j0 = tile_j0(t);
     const int ds = STK ? st - j0 - 4 * lg : 0;
 #pragma unroll
@@ -602,21 +609,21 @@ __global__ __launch_bounds__(BT, 2) void bwd_dq_kernel(BwdArgs a) {
       bf16x8 ka[4], va[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        ka[kk] = *reinterpret_cast<const bf16x8*>(Ks[buf] + (32 * h + lr) * RS + kchunk(2 * kk + lg, lr));
-        va[kk] = *reinterpret_cast<const bf16x8*>(Vs[buf] + (32 * h + lr) * RS + kchunk(2 * kk + lg, lr));
+        ka[kk] = *reinterpret_cast<const bf16x8*>(Ks[BUF] + (32 * h + lr) * RS + kchunk(2 * kk + lg, lr));
+        va[kk] = *reinterpret_cast<const bf16x8*>(Vs[BUF] + (32 * h + lr) * RS + kchunk(2 * kk + lg, lr));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         if (!nt_valid[i]) continue;
-        f32x16 s, dp;
+        f32x16 sc, dp;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          s = mfma32(ka[kk], qb[i][kk], kk == 0 ? zero16() : s);
+          sc = mfma32(ka[kk], qb[i][kk], kk == 0 ? zero16() : sc);
           dp = mfma32(va[kk], gb[i][kk], kk == 0 ? zero16() : dp);
         }
         const int dh = pos0[i] + lr - j0 - 4 * lg;
         const int dlw = W > 0 ? dh - W : -0x40000000;
-        mask_half<STK>(s, h, j0, pos0[i], phi[i], W, st, dh, dlw, ds);
+        mask_half<STK>(sc, h, j0, pos0[i], phi[i], W, st, dh, dlw, ds);
         bf16x8 db[2];
 #pragma unroll
         for (int uu = 0; uu < 2; ++uu) {
@@ -624,8 +631,8 @@ __global__ __launch_bounds__(BT, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r0 = 8 * uu + 2 * e, r1 = r0 + 1;
-            const float p0 = fast_exp2(__builtin_fmaf(s[r0], c, -l2[i]));
-            const float p1 = fast_exp2(__builtin_fmaf(s[r1], c, -l2[i]));
+            const float p0 = fast_exp2(__builtin_fmaf(sc[r0], c, -l2[i]));
+            const float p1 = fast_exp2(__builtin_fmaf(sc[r1], c, -l2[i]));
             const f32x2 gg = {p0 * (dp[r0] - dl[i]), p1 * (dp[r1] - dl[i])};
             w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(gg, bf16x2));
           }
@@ -637,9 +644,22 @@ __global__ __launch_bounds__(BT, 2) void bwd_dq_kernel(BwdArgs a) {
         for (int uu = 0; uu < 2; ++uu)
 #pragma unroll
           for (int dt = 0; dt < 2; ++dt)
-            acc[i][dt] = mfma32(tr_operand(Ks[buf], 2 * h + uu, dt, vofs), db[uu], acc[i][dt]);
+            acc[i][dt] = mfma32(tr_operand(Ks[BUF], 2 * h + uu, dt, vofs), db[uu], acc[i][dt]);
       }
     }
+  };
+  {
+    std::integral_constant<int, 0> B0;
+    std::integral_constant<int, 1> B1;
+    std::integral_constant<int, 2> B2;
+    int t = 0;
+    for (; t + NBUF <= n_tiles; t += NBUF) {
+      body(B0, t);
+      body(B1, t + 1);
+      body(B2, t + 2);
+    }
+    if (t < n_tiles) body(B0, t);
+    if (t + 1 < n_tiles) body(B1, t + 1);
   }
 
   // ---- epilogue: dq = scale * acc, rounded to bf16; through LDS so that it
