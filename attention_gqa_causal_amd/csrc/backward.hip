@@ -222,7 +222,7 @@ __global__ __launch_bounds__(BT, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // per-lane 32-bit offset; on the last tile, and for the missing second head
   // of an odd group, rows repeat valid ones (masked, and in bounds).
   const int64_t q_stride = (int64_t)a.Hq * kHeadDim;
-  const int dma_chunk = ((lane & 7) ^ (lane >> 3)) * 8;
+  const int dma_chunk = ((lane & 7) ^ kswz(lane >> 3)) * 8;
   uint32_t qoff[2];
 #pragma unroll
   for (int ii = 0; ii < 2; ++ii) {
@@ -571,7 +571,7 @@ __global__ __launch_bounds__(BT, 2) void bwd_dq_kernel(BwdArgs a) {
   const int64_t kv_stride = (int64_t)a.Hkv * kHeadDim;
   const __bf16* kbase = reinterpret_cast<const __bf16*>(a.k) + (int64_t)b * S * kv_stride + g * kHeadDim;
   const __bf16* vbase = reinterpret_cast<const __bf16*>(a.v) + (int64_t)b * S * kv_stride + g * kHeadDim;
-  const int dma_chunk = ((lane & 7) ^ (lane >> 3)) * 8;
+  const int dma_chunk = ((lane & 7) ^ kswz(lane >> 3)) * 8;
   // wave w fills rows 16w .. 16w+15 of a tile; rows past the key range repeat
   // row hi (masked, in bounds)
   auto dma_tile = [&](int t, int buf) {

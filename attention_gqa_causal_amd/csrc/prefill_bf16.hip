@@ -271,7 +271,7 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
   const int64_t kv_stride = (int64_t)a.Hkv * kHeadDim;
   const __bf16* kbase = a.k + g * kHeadDim;
   const __bf16* vbase = a.v + g * kHeadDim;
-  const int dma_chunk = ((lane & 7) ^ (lane >> 3)) * 8;  // logical chunk this lane's LDS slot holds
+  const int dma_chunk = ((lane & 7) ^ kswz(lane >> 3)) * 8;  // logical chunk this lane's LDS slot holds
   auto fetch_blk = [&](int t, int (&blk)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {

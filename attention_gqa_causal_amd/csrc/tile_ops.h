@@ -39,14 +39,19 @@ __device__ __forceinline__ f32x16 zero16() {
 }
 
 // LDS tiles hold rows of 64 bf16 (a key, or a query, with its 64 d) in their
-// natural [row][d] layout, one 128-byte row each, with the eight 16-byte
-// chunks of row r stored in the order c ^ (r & 7).  The swizzle spreads the
-// rows that one read instruction touches over all banks, and it lets a wave
-// fill 8 whole rows with one 16-byte global-to-LDS load per lane (lane i lands
-// at byte 16i of the wave's slice, so it fetches logical chunk (i & 7) ^ (i >> 3)
-// of row i >> 3).
+// natural [row][d] layout, one 128-byte row each, with logical 16-byte chunk c
+// of row r stored at chunk position c ^ kswz(r), kswz(r) = 2 (r % 4) +
+// (r / 4) % 2.  The swizzle spreads the rows that one read instruction touches
+// over all banks: the 8 rows of a row read (one chunk each; kswz is a
+// permutation of 0..7) and the 4 rows of a transposing read (a pair of
+// adjacent chunks each; kswz(r) / 2 differs between any 4 consecutive rows
+// that start at a multiple of 4, so the 4 pairs land on different banks).
+// It also lets a wave fill 8 whole rows with one 16-byte global-to-LDS load per
+// lane: lane i lands at byte 16i of the wave's 8-row slice, so it fetches
+// logical chunk (i & 7) ^ kswz(i >> 3) of row i >> 3.
+__device__ __forceinline__ int kswz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 // Element offset of logical 16-byte chunk cc of a row whose index is r (mod 8).
-__device__ __forceinline__ int kchunk(int cc, int r) { return ((cc ^ r) & 7) * 8; }
+__device__ __forceinline__ int kchunk(int cc, int r) { return ((cc ^ kswz(r)) & 7) * 8; }
 
 // Operand of a product that contracts over the rows of an LDS tile: for
 // k-step u (tile rows 16u .. 16u+15) and d-block dt, lane l gets column
