@@ -130,6 +130,7 @@ def load_traffic(kind, launches_per_call=1):
 # ----------------------------------------------------------------------------- HBM traffic from counters
 
 COPY_BYTES = 256 << 20
+FLUSH_BYTES = 512 << 20  # twice the MI355X last-level cache (256 MiB MALL)
 
 
 def _read_counter_csv(d, counter):
@@ -281,6 +282,140 @@ def summarize_trace(trace_dir, out_md=None):
     print(text)
 
 
+UNIT_COUNTERS = ("GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU "
+                 "SQ_INSTS_VALU_TRANS_F32 SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_ACTIVE_INST_LDS")
+
+
+def _read_dispatches(d):
+    """Dispatches of one rocprofv3 --pmc run in order: dicts with name, workgroups, duration (ns) and the counter
+    values (rocprofv3's csv sums each counter over all its hardware instances: SEs, XCDs)."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    disp = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            i = int(r["Dispatch_Id"])
+            e = disp.setdefault(i, {"name": r["Kernel_Name"],
+                                    "wgs": int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])),
+                                    "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), "c": {}})
+            e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    agent = {"xcc": 8, "simd": 1024, "cu": 256, "clk_mhz": 2400}
+    info = glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True)
+    if info:
+        with open(info[0]) as f:
+            for r in csv.DictReader(f):
+                if r.get("Agent_Type") == "GPU":
+                    agent = {"xcc": int(r["Num_Xcc"]), "simd": int(r["Simd_Count"]), "cu": int(r["Cu_Count"]),
+                             "clk_mhz": int(r["Max_Engine_Clk_Fcompute"])}
+    return [disp[i] for i in sorted(disp)], agent
+
+
+def summarize_units(dirs):
+    """Execution-unit counters of single stages (one rocprofv3 --pmc run per stage, `bench.py --counters --parts
+    STAGE --manifest DIR/stage.json`): executed matrix-core FLOP and exp instructions against the algorithmic
+    counts, matrix-unit and vector-unit busy fractions, LDS bank conflicts.  The busy fractions follow rocprofv3's
+    own derived metrics (MfmaUtil, VALUBusy, LdsBankConflict) with GRBM_GUI_ACTIVE per XCD as the time base."""
+    import statistics
+
+    rows, krows, agent = [], [], None
+    for d in dirs:
+        with open(os.path.join(d, "stage.json")) as f:
+            st = json.load(f)["stages"][0]
+        disp, agent = _read_dispatches(d)
+        last_copy = max(i for i, e in enumerate(disp) if "copyBuffer" in e["name"] or "copy_kernel" in e["name"])
+        mine = [e for e in disp[last_copy + 1:] if "gqa::" in e["name"]]
+        if not mine or len(mine) % st["calls"]:
+            raise SystemExit(f"{d}: {len(mine)} library dispatches for {st['calls']} calls")
+        nx, ns, nc = agent["xcc"], agent["simd"], agent["cu"]
+        calls = st["calls"]
+        # per (kernel, grid): the median dispatch of each counter (the first dispatch of a run can carry
+        # collection set-up in its GUI-active count), times the group's dispatches per call
+        groups = {}
+        for e in mine:
+            groups.setdefault((_short_kernel_name(e["name"]), e["wgs"]), []).append(e)
+        names_c = sorted({c for e in mine for c in e["c"]})
+        med = {}
+        for key, es in groups.items():
+            m = {c: statistics.median(e["c"].get(c, 0.0) for e in es) for c in names_c}
+            m["ns"] = statistics.median(e["ns"] for e in es)
+            med[key] = (m, len(es) / calls)
+
+        def per_call(c):
+            return sum(m[c] * k for m, k in med.values())
+
+        g = per_call("GRBM_GUI_ACTIVE") / nx  # GUI-active cycles of one XCD per call
+        conf, idx = per_call("SQ_LDS_BANK_CONFLICT"), per_call("SQ_LDS_IDX_ACTIVE")
+        rows.append({
+            "stage": st["name"], "us": per_call("ns") / 1e3,
+            "clk": g / (per_call("ns") * 1e-9) / 1e9,
+            "mfma_ratio": per_call("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512 / st["flop"] if st["flop"] else None,
+            "exp_ratio": per_call("SQ_INSTS_VALU_TRANS_F32") * 64 / st["exp"] if st.get("exp") else None,
+            "mfma_busy": per_call("SQ_VALU_MFMA_BUSY_CYCLES") / (g * ns),
+            "valu_busy": per_call("SQ_ACTIVE_INST_VALU") / (g * nc),
+            "lds_busy": per_call("SQ_ACTIVE_INST_LDS") / (g * nc),
+            "lds_conf": conf / (idx - conf) if idx > conf else 0.0,
+        })
+        for (kn, wgs), (m, _) in med.items():
+            gk = m["GRBM_GUI_ACTIVE"] / nx
+            ck, ik = m["SQ_LDS_BANK_CONFLICT"], m["SQ_LDS_IDX_ACTIVE"]
+            krows.append((st["name"], kn, wgs, m["ns"] / 1e3, m["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e9,
+                          m["SQ_INSTS_VALU_TRANS_F32"] * 64 / 1e6, m["SQ_VALU_MFMA_BUSY_CYCLES"] / (gk * ns),
+                          m["SQ_ACTIVE_INST_VALU"] / (gk * nc), ck / (ik - ck) if ik > ck else 0.0))
+
+    def pct(x):
+        return "–" if x is None else f"{100 * x:.1f} %"
+
+    def rat(x):
+        return "–" if x is None else f"{x:.2f}"
+
+    lines = ["# Execution-unit counters per stage", "",
+             "Commands (repository root, one MI355X; one rocprofv3 run per stage, 3 calls each after a 256 MiB "
+             "calibration copy):", "",
+             "    cd /tmp && export TMPDIR=/tmp",
+             "    for s in " + " ".join(r["stage"] for r in rows) + "; do",
+             f"      rocprofv3 --pmc {UNIT_COUNTERS} --output-format csv -d $R/gpurun_out/units_$s -o run -- \\",
+             "        python3 $R/bench.py --counters --parts $s --manifest $R/gpurun_out/units_$s/stage.json",
+             "    done",
+             "    python3 bench.py --summarize-units " + " ".join(f"gpurun_out/units_{r['stage']}" for r in rows), "",
+             f"Device: {agent['xcc']} XCDs, {agent['cu']} CUs, {agent['simd']} SIMDs, rated engine clock "
+             f"{agent['clk_mhz']} MHz.", "",
+             "Definitions (per call: for each kernel of the call, the median over its dispatches of each counter, "
+             "summed over the call's kernels):", "",
+             "* MFMA FLOP ratio = 512 · `SQ_INSTS_VALU_MFMA_MOPS_BF16` ÷ algorithmic FLOP (visible pairs only); above 1 "
+             "means masked or padded matrix work.",
+             "* exp ratio = 64 · `SQ_INSTS_VALU_TRANS_F32` ÷ algorithmic exponentials (one per visible pair and query "
+             "head; for the backward, one pass over the probabilities). Counts every transcendental instruction of "
+             "a wave, all 64 lanes, so it is an upper bound on exponentials evaluated.",
+             "* matrix busy = `SQ_VALU_MFMA_BUSY_CYCLES` ÷ (GRBM cycles per XCD × SIMDs) (rocprofv3's MfmaUtil).",
+             "* vector busy = `SQ_ACTIVE_INST_VALU` ÷ (GRBM cycles per XCD × CUs) (rocprofv3's VALUBusy); LDS busy "
+             "likewise with `SQ_ACTIVE_INST_LDS`.",
+             "* LDS conflicts = `SQ_LDS_BANK_CONFLICT` ÷ (`SQ_LDS_IDX_ACTIVE` − `SQ_LDS_BANK_CONFLICT`), conflict "
+             "cycles per access cycle (rocprofv3's LdsBankConflict).",
+             "* GRBM clock = `GRBM_GUI_ACTIVE` per XCD ÷ kernel time. The counter window is a little longer than "
+             "the kernel (start and stop of collection), so this overstates the clock most for short kernels.", "",
+             "| stage | us / call (profiled) | MFMA FLOP ratio | exp ratio | matrix busy | vector busy | LDS busy | "
+             "LDS conflicts | GRBM clock GHz |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['stage']} | {r['us']:.1f} | {rat(r['mfma_ratio'])} | {rat(r['exp_ratio'])} | "
+                     f"{pct(r['mfma_busy'])} | {pct(r['valu_busy'])} | {pct(r['lds_busy'])} | "
+                     f"{rat(r['lds_conf'])} | {r['clk']:.2f} |")
+    lines += ["", "Per kernel (median dispatch):", "",
+              "| stage | kernel | workgroups | us | MFMA GFLOP | exp lanes (M) | matrix busy | vector busy | "
+              "LDS conflicts |", "|---|---|---|---|---|---|---|---|---|"]
+    for s_, kn, wgs, us, gf, ex, mb, vb, lc in krows:
+        lines.append(f"| {s_} | `{kn}` | {wgs} | {us:.1f} | {gf:.2f} | {ex:.1f} | {pct(mb)} | {pct(vb)} | "
+                     f"{lc:.2f} |")
+    text = "\n".join(lines) + "\n"
+    with open(os.path.join(PROFILES, "units_counters.md"), "w") as f:
+        f.write(text)
+    print(text)
+
+
 # ----------------------------------------------------------------------------- CPU oracle baseline
 
 def cpu_baseline(seconds: float):
@@ -342,12 +477,12 @@ def add_prefill(stages, gq, p, up, f32, dev):
     for name, W in (("prefill_dense", 0), ("prefill_swa128", 128)):
         fl, by = prefill_work(B, S, Hq, Hkv, D, W)
         stages[name] = dict(fn=(lambda W=W: gq.attn_prefill(pq, pk, pv, ps, window=W, out=pout)), flop=fl, bytes=by,
-                            bound="mfma" if W == 0 else "hbm")
+                            exp=fl // (4 * D), bound="mfma" if W == 0 else "hbm")
     # windowed layer with 4 start-of-sequence sink tokens kept visible
     fl, by = prefill_work_sink_tokens(B, S, Hq, Hkv, D, 128, 4)
     stages["prefill_swa128_sink4"] = dict(
         fn=(lambda: gq.attn_prefill(pq, pk, pv, ps, window=128, sink_tokens=4, out=pout)), flop=fl, bytes=by,
-        bound="hbm")
+        exp=fl // (4 * D), bound="hbm")
 
 
 def add_decode(stages, gq, d, up, i32, f32, dev):
@@ -361,13 +496,13 @@ def add_decode(stages, gq, d, up, i32, f32, dev):
         nbytes = gq.decode_workspace_size(Bd, Ld, Hq, Hkv, D, W)
         ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
         stages[name] = dict(fn=(lambda W=W, ws=ws: gq.attn_decode(dq, (dk, dv), dsl, ds, window=W, workspace=ws)),
-                            flop=fl, bytes=by, bound="hbm")
+                            flop=fl, bytes=by, exp=fl // (4 * D), bound="hbm")
     fl, by = decode_work([int(x) for x in d.seqlens], Hq, Hkv, D, 128, n_sink=4)
     nbytes = gq.decode_workspace_size(Bd, Ld, Hq, Hkv, D, 128, sink_tokens=4)
     ws4 = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
     stages["decode_swa128_sink4"] = dict(
         fn=(lambda: gq.attn_decode(dq, (dk, dv), dsl, ds, window=128, sink_tokens=4, workspace=ws4)),
-        flop=fl, bytes=by, bound="hbm")
+        flop=fl, bytes=by, exp=fl // (4 * D), bound="hbm")
 
 
 def add_varlen(stages, gq, r, up, i32, f32, dev):
@@ -383,7 +518,7 @@ def add_varlen(stages, gq, r, up, i32, f32, dev):
         ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
         stages[name] = dict(fn=(lambda W=W, ws=ws: gq.attn_varlen_paged(
             rq, (rk, rv), rbt, rcu, rsl, rs, window=W, max_q_len=r.max_q_len, max_kv_len=r.max_kv_len,
-            workspace=ws)), flop=fl, bytes=by, bound="mfma" if W == 0 else "hbm")
+            workspace=ws)), flop=fl, bytes=by, exp=fl // (4 * D), bound="mfma" if W == 0 else "hbm")
 
 
 def add_ring(stages, gq, up, i32, f32, dev):
@@ -402,7 +537,7 @@ def add_ring(stages, gq, up, i32, f32, dev):
         stages[f"ring_decode_w128_b{B}"] = dict(
             fn=(lambda rq=rq, rk=rk, rv=rv, rsl=rsl, rs=rs, ws=ws: gq.attn_decode_ring(rq, (rk, rv), rsl, rs,
                                                                                       workspace=ws)),
-            flop=fl, bytes=by, bound="hbm")
+            flop=fl, bytes=by, exp=fl // (4 * D), bound="hbm")
         if B == 64:
             kn = up(gi.make_tensor(68, gi.T_K, (B, Hkv, D), 1.0, "bf16"))
             vn = up(gi.make_tensor(68, gi.T_V, (B, Hkv, D), 1.0, "bf16"))
@@ -433,7 +568,7 @@ def add_backward(stages, gq, p, up, f32, dev):
         stages[name] = dict(
             fn=(lambda out=out, lse=lse, grads=grads, W=W: gq.attn_prefill_backward(
                 q, k, v, sinks, out, lse, dout, window=W, workspace=ws, grads=grads)),
-            flop=flop * 10 // 4, bytes=byts, bound="mfma" if W == 0 else "hbm")
+            flop=flop * 10 // 4, bytes=byts, exp=flop // (4 * D), bound="mfma" if W == 0 else "hbm")
 
 
 def add_rope(stages, gq, up, i32, dev):
@@ -484,8 +619,13 @@ def main():
     ap.add_argument("--long", action="store_true",
                     help="also time the long-context workloads (prefill S32768, decode B8 x 131072)")
     ap.add_argument("--counters", action="store_true",
-                    help="run only the dense prefill, the dense decode and a plain 256 MiB device copy "
-                         "(3 dispatches each) for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
+                    help="run only a plain 256 MiB device copy, then each selected stage (--parts; default the "
+                         "dense prefill and the dense decode) 3 times, for rocprofv3 --pmc runs")
+    ap.add_argument("--manifest", metavar="PATH",
+                    help="with --counters: write the selected stages and their algorithmic work as JSON to PATH")
+    ap.add_argument("--summarize-units", nargs="+", metavar="DIR",
+                    help="turn per-stage rocprofv3 --pmc runs of the execution-unit counters (each DIR holds one "
+                         "run and its --manifest stage.json) into profiles/units_counters.md")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="turn a rocprofv3 --kernel-trace --stats run into profiles/kernel_trace_bench_step.md")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -498,7 +638,10 @@ def main():
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
         return
-    if args.counters:
+    if args.summarize_units:
+        summarize_units(args.summarize_units)
+        return
+    if args.counters and args.parts == "all":
         args.parts = "prefill_dense,decode_dense"
 
     if args.gpus != 1:
@@ -566,10 +709,17 @@ def main():
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
-        for n in ("prefill_dense", "decode_dense"):
+        torch.cuda.synchronize()
+        # every library dispatch after the last calibration copy belongs to these calls, in this order
+        for n in names:
             for _ in range(3):
                 stages[n]["fn"]()
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
+        if args.manifest:
+            os.makedirs(os.path.dirname(os.path.abspath(args.manifest)), exist_ok=True)
+            with open(args.manifest, "w") as f:
+                json.dump({"stages": [{"name": n, "calls": 3, "flop": stages[n]["flop"], "bytes": stages[n]["bytes"],
+                                       "exp": stages[n].get("exp")} for n in names]}, f, indent=1)
         print("counter workload done", flush=True)
         return
 
@@ -592,12 +742,28 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # cold cache: before each call a 512 MiB write evicts the 256 MiB last-level cache (and the L2s),
+    # so the call's inputs come from HBM; reported beside the warm numbers, never as `value`
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    cold = {n: [] for n in names}
+    for i in range(args.steps):
+        for n in names:
+            flush.fill_(i)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            stages[n]["fn"]()
+            b.record()
+            cold[n].append((a, b))
+    torch.cuda.synchronize()
+    del flush
+
     parts = {}
     for n in names:
         ms = sorted(a.elapsed_time(b) for a, b in ev[n])
         avg = sum(ms) / len(ms)
         st = stages[n]
         t = avg / 1e3
+        ms_cold = sorted(a.elapsed_time(b) for a, b in cold[n])[len(cold[n]) // 2]
         t_roof = max(st["flop"] / (PEAK_BF16_TFLOPS * 1e12), st["bytes"] / (PEAK_HBM_GBPS * 1e9))
         parts[n] = {
             "ms": round(avg, 5),
@@ -606,6 +772,8 @@ def main():
             "gbps": round(st["bytes"] / t / 1e9, 2),
             "bound": st["bound"],
             "roofline_frac": round(t_roof / t, 4),
+            "ms_cold_median": round(ms_cold, 5),
+            "roofline_frac_cold": round(t_roof / (ms_cold / 1e3), 4),
             "alg_flop": st["flop"],
             "alg_bytes": st["bytes"],
         }
