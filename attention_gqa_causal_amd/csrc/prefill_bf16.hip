@@ -119,14 +119,21 @@ __device__ __forceinline__ float exp_half(const f32x16& s, bf16x8 (&pb)[2], floa
 // One eighth of a tile's exponentials for one N-tile: the 8 scores of
 // k-step group uu of a key half (one bf16 P^T operand) and their partial sum.
 __device__ __forceinline__ float exp_chunk(const f32x16& s, bf16x8& pb, int uu, float m, float c) {
-  float ra = 0.f, rb = 0.f;
+  // the sums start from the first weights, not from 0: 0 + x would cost an add
+  // each (the compiler keeps it, as it cannot rule out x = -0)
+  float ra, rb;
   u32x4 w;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const f32x2 x = {fast_exp2(__builtin_fmaf(s[8 * uu + 2 * e], c, -m)),
                      fast_exp2(__builtin_fmaf(s[8 * uu + 2 * e + 1], c, -m))};
-    ra += x[0];
-    rb += x[1];
+    if (e == 0) {
+      ra = x[0];
+      rb = x[1];
+    } else {
+      ra += x[0];
+      rb += x[1];
+    }
     w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
   }
   pb = __builtin_bit_cast(bf16x8, w);
@@ -346,7 +353,7 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
         mask_half<STK>(sA[0], 0, j0, pos0[0], phi[0], W, st, dh0, dl0, ds);
         mask_half<STK>(sA[1], 0, j0, pos0[1], phi[1], W, st, dh1, dl1, ds);
       }
-      float r0 = 0.f, r1 = 0.f;
+      float r0, r1;  // set by the first exponential chunk of each N-tile
       {
         bf16x8 ka[4];
 #pragma unroll
@@ -358,7 +365,9 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
           sB[0] = mfma32(ka[k], qb[0][k], k == 0 ? zero16() : sB[0]);
           sB[1] = mfma32(ka[k], qb[1][k], k == 0 ? zero16() : sB[1]);
           fence_schedule();
-          if (k < 2) r0 += exp_chunk(sA[0], pA0[k], k, m_run[0], c);
+          if (k == 0) r0 = exp_chunk(sA[0], pA0[k], k, m_run[0], c);
+          else if (k == 1) r0 += exp_chunk(sA[0], pA0[k], k, m_run[0], c);
+          else if (k == 2) r1 = exp_chunk(sA[1], pA1[k - 2], k - 2, m_run[1], c);
           else r1 += exp_chunk(sA[1], pA1[k - 2], k - 2, m_run[1], c);
         }
         fence_schedule();
@@ -380,8 +389,6 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
         mask_half<STK>(sB[0], 1, j0, pos0[0], phi[0], W, st, dh0, dl0, ds);
         mask_half<STK>(sB[1], 1, j0, pos0[1], phi[1], W, st, dh1, dl1, ds);
       }
-      r0 = 0.f;
-      r1 = 0.f;
       {
         bf16x8 va[4];
 #pragma unroll
@@ -393,7 +400,9 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
           o[0][dt] = mfma32(va[i], pA0[uu], o[0][dt]);
           o[1][dt] = mfma32(va[i], pA1[uu], o[1][dt]);
           fence_schedule();
-          if (i < 2) r0 += exp_chunk(sB[0], pB0[i], i, m_run[0], c);
+          if (i == 0) r0 = exp_chunk(sB[0], pB0[i], i, m_run[0], c);
+          else if (i == 1) r0 += exp_chunk(sB[0], pB0[i], i, m_run[0], c);
+          else if (i == 2) r1 = exp_chunk(sB[1], pB1[i - 2], i - 2, m_run[1], c);
           else r1 += exp_chunk(sB[1], pB1[i - 2], i - 2, m_run[1], c);
         }
         fence_schedule();
