@@ -248,18 +248,16 @@ __global__ __launch_bounds__(BT, 2) void bwd_dkdv_kernel(BwdArgs a) {
         off = (uint32_t)(((pr * a.Hq + e) * kHeadDim + dma_chunk) * 2);
       }
       const int lofs = (16 * wave + 8 * ii) * RS;  // wave-uniform slice of 8 rows
-      __builtin_amdgcn_global_load_lds((const void*)(qb + off), (lds_void*)(qs + lofs), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(gb + off), (lds_void*)(gs + lofs), 16, 0, 0);
+      dma16(qb, off, (lds_void*)(qs + lofs));
+      dma16(gb, off, (lds_void*)(gs + lofs));
     }
     if (wave == 0) {
       const int64_t lbase = ((int64_t)b * a.Hq + g * G + 2 * i) * S + q0;
       uint32_t off = loff;
       if (!fast) off = (uint32_t)(((min(2 * i + lg, G - 1) - 2 * i) * S + min(q0 + lr, S - 1) - q0) * 4);
       float* ls = smem_f + buf * 4 * QT;
-      __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(a.lse2 + lbase) + off),
-                                       (lds_void*)(ls), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(a.dlt + lbase) + off),
-                                       (lds_void*)(ls + 2 * QT), 4, 0, 0);
+      dma4(reinterpret_cast<const char*>(a.lse2 + lbase), off, (lds_void*)(ls));
+      dma4(reinterpret_cast<const char*>(a.dlt + lbase), off, (lds_void*)(ls + 2 * QT));
     }
   };
 
@@ -574,14 +572,18 @@ __global__ __launch_bounds__(BT, 2) void bwd_dq_kernel(BwdArgs a) {
   const int dma_chunk = ((lane & 7) ^ kswz(lane >> 3)) * 8;
   // wave w fills rows 16w .. 16w+15 of a tile; rows past the key range repeat
   // row hi (masked, in bounds)
+  // (a scalar base per tile and a 32-bit offset per lane)
   auto dma_tile = [&](int t, int buf) {
+    const int j0 = tile_j0(t);
+    const char* kt = reinterpret_cast<const char*>(kbase + (int64_t)j0 * kv_stride);
+    const char* vt = reinterpret_cast<const char*>(vbase + (int64_t)j0 * kv_stride);
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
-      const int j = min(tile_j0(t) + 16 * wave + 8 * ii + (lane >> 3), hi);
-      const int64_t off = (int64_t)j * kv_stride + dma_chunk;
+      const int r = min(16 * wave + 8 * ii + (lane >> 3), hi - j0);
+      const uint32_t off = (uint32_t)(r * (int)kv_stride + dma_chunk) * 2u;
       const int lofs = (16 * wave + 8 * ii) * RS;
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + off), (lds_void*)(&Ks[buf][lofs]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vbase + off), (lds_void*)(&Vs[buf][lofs]), 16, 0, 0);
+      dma16(kt, off, (lds_void*)(&Ks[buf][lofs]));
+      dma16(vt, off, (lds_void*)(&Vs[buf][lofs]));
     }
   };
   int vofs[2];

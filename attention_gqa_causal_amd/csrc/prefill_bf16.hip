@@ -290,6 +290,23 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
     }
   };
   auto dma_tile = [&](int t, const int (&blk)[2], int buf) {
+    if constexpr (MODE == KV_BATCHED) {
+      // a scalar base per tile and a 32-bit offset per lane (the tile's rows
+      // are consecutive cache rows); rows past hi repeat row hi
+      const int j0 = tile_j0(t);
+      const int64_t tb = ((int64_t)sv.b * a.seq.lmax + j0) * kv_stride;
+      const char* kt = reinterpret_cast<const char*>(kbase + tb);
+      const char* vt = reinterpret_cast<const char*>(vbase + tb);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = min(16 * wave + 8 * i + (lane >> 3), hi - j0);
+        const uint32_t off = (uint32_t)(r * (int)kv_stride + dma_chunk) * 2u;
+        const int lofs = (16 * wave + 8 * i) * RS;  // wave-uniform slice of 8 rows
+        dma16(kt, off, (lds_void*)(&Ks[buf][lofs]));
+        dma16(vt, off, (lds_void*)(&Vs[buf][lofs]));
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int j = min(tile_j0(t) + 16 * wave + 8 * i + (lane >> 3), hi);
@@ -302,8 +319,8 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
       }
       const int64_t off = row * kv_stride + dma_chunk;
       const int lofs = (16 * wave + 8 * i) * RS;  // wave-uniform slice of 8 rows
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + off), (lds_void*)(&Ks[buf][lofs]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vbase + off), (lds_void*)(&Vs[buf][lofs]), 16, 0, 0);
+      dma16((const void*)(kbase + off), (lds_void*)(&Ks[buf][lofs]));
+      dma16((const void*)(vbase + off), (lds_void*)(&Vs[buf][lofs]));
     }
   };
 

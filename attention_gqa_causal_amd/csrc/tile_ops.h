@@ -121,6 +121,37 @@ __device__ __forceinline__ void mask_half(f32x16& s, int h, int j0, int plo, int
   }
 }
 
+// 16-byte global-to-LDS load (lane i lands at byte 16 i past lds_dst, which
+// must be wave-uniform), issued from inline asm.  The compiler, seeing an LDS
+// write in flight, would make every later LDS read wait for it, even reads of
+// another buffer; the tile loops instead wait for these loads themselves
+// (s_waitcnt vmcnt, then a barrier) before any wave reads the buffer they fill.
+// M0 takes the LDS address and needs one wait state before the load; the
+// leading s_nop covers a base address just written to SGPRs by a vector
+// instruction (five wait states).
+__device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, lds_void* lds_dst) {
+  const uint32_t m0v = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_dst));
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(m0v)
+               : "memory", "m0");
+}
+// 4-byte form (lane i lands at byte 4 i past lds_dst), same contract.
+__device__ __forceinline__ void dma4(const char* gbase, uint32_t voff, lds_void* lds_dst) {
+  const uint32_t m0v = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_dst));
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(m0v)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma16(const void* gaddr, lds_void* lds_dst) {
+  const uint32_t m0v = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_dst));
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gaddr), "s"(m0v)
+               : "memory", "m0");
+}
+
 // Pin the instruction order: nothing is scheduled across this point.
 __device__ __forceinline__ void fence_schedule() { __builtin_amdgcn_sched_barrier(0); }
 
