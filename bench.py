@@ -24,6 +24,12 @@ TFLOP/s (4*D*Hq per visible query-key pair), timed with HIP events on the
 stream the kernels run on; every stage's own time, TFLOP/s, GB/s and roofline
 fraction is reported under "parts".  "roofline" describes the dominant kernel
 (dense prefill, MFMA-bound); "roofline_decode" the HBM-bound dense decode.
+Each part also carries two other timings of the same stage, never used for
+`value`: cold (each call after a 512 MiB write that evicts the last-level
+cache; median) and back to back (the stage alone, called `steps` times in a
+row, median; a dense MFMA kernel then runs at the lower clock its own power
+draw settles at, where inside the step it starts from the clock the HBM-bound
+stages left).
 """
 from __future__ import annotations
 
@@ -757,6 +763,25 @@ def main():
     torch.cuda.synchronize()
     del flush
 
+    # back to back: the same stage called `steps` times in a row.  In the step loop above each stage runs between
+    # other stages, and a compute-bound kernel then finds the clock that the HBM-bound stages left it; called back
+    # to back it runs at the clock its own power draw settles at (lower for dense MFMA work)
+    # (events around each call, median: a stage shorter than its host-side launch cost would otherwise be timed
+    # at the launch rate)
+    b2b = {}
+    for n in names:
+        for _ in range(2):
+            stages[n]["fn"]()
+        evs = []
+        for _ in range(args.steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            stages[n]["fn"]()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        b2b[n] = sorted(a.elapsed_time(b) for a, b in evs)[len(evs) // 2]
+
     parts = {}
     for n in names:
         ms = sorted(a.elapsed_time(b) for a, b in ev[n])
@@ -774,6 +799,8 @@ def main():
             "roofline_frac": round(t_roof / t, 4),
             "ms_cold_median": round(ms_cold, 5),
             "roofline_frac_cold": round(t_roof / (ms_cold / 1e3), 4),
+            "ms_back_to_back_median": round(b2b[n], 5),
+            "roofline_frac_back_to_back": round(t_roof / (b2b[n] / 1e3), 4),
             "alg_flop": st["flop"],
             "alg_bytes": st["bytes"],
         }
