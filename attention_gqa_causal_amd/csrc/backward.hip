@@ -214,6 +214,10 @@ __global__ __launch_bounds__(BT, 2) void bwd_dkdv_kernel(BwdArgs a) {
       vop[kk] = *reinterpret_cast<const bf16x8*>(v + off + 16 * kk);
     }
   }
+  // Let these loads land here: a wait for them left to the compiler would sit
+  // inside the unit loop, where it would also wait for the staging loads in
+  // flight (issued from asm, so not counted by the compiler).
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
   // Staging of a unit (q-tile t, head pair i): wave w fills rows 16w .. 16w+15
   // of the Q and dO tiles (row R = head R / 32 of the pair, query R % 32), 8
@@ -560,6 +564,7 @@ __global__ __launch_bounds__(BT, 2) void bwd_dq_kernel(BwdArgs a) {
     l2[i] = ok ? a.lse2[li] : 0.f;
     dl[i] = ok ? a.dlt[li] : 0.f;
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // as in the dK/dV kernel: no compiler wait on these inside the tile loop
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
