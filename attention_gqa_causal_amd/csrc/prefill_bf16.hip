@@ -245,16 +245,18 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
   auto tile_j0 = [&](int t) { return t < n_st ? BK * t : j_begin + BK * (t - n_st); };
 
   // ---- Q^T operands (B of S^T = K Q^T): lane holds row lr, d = 16*k + 8*lg .. +7
+  // (addresses: the N-tile's first row as a scalar base, a 32-bit lane offset)
   bf16x8 qb[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int t = nt_t0[i] + lr;
     const bool ok = nt_valid[i] && t < sv.q_len;
-    const __bf16* qp = a.q + ((sv.q_row0 + t) * a.Hq + nt_hq[i]) * (int64_t)kHeadDim + 8 * lg;
+    const char* qt = reinterpret_cast<const char*>(a.q + ((sv.q_row0 + nt_t0[i]) * a.Hq + nt_hq[i]) * (int64_t)kHeadDim);
+    const uint32_t qo = (uint32_t)(lr * a.Hq * kHeadDim + 8 * lg) * 2u;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok) v = *reinterpret_cast<const u32x4*>(qp + 16 * k);
+      if (ok) v = *reinterpret_cast<const u32x4*>(qt + qo + 32 * k);
       qb[i][k] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -504,7 +506,8 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
     const int t = nt_t0[i] + r;
     if (!nt_valid[i] || t >= sv.q_len) continue;
     const u32x4 v = *reinterpret_cast<const u32x4*>(stg + (32 * i + r) * RS + kchunk(cc, r));
-    *reinterpret_cast<u32x4*>(a.out + ((sv.q_row0 + t) * a.Hq + nt_hq[i]) * (int64_t)kHeadDim + 8 * cc) = v;
+    char* ot = reinterpret_cast<char*>(a.out + ((sv.q_row0 + nt_t0[i]) * a.Hq + nt_hq[i]) * (int64_t)kHeadDim);
+    *reinterpret_cast<u32x4*>(ot + (uint32_t)(r * a.Hq * kHeadDim + 8 * cc) * 2u) = v;
   }
 }
 
