@@ -585,7 +585,7 @@ __global__ __launch_bounds__(BT, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
       const int r = min(16 * wave + 8 * ii + (lane >> 3), hi - j0);
-      const uint32_t off = (uint32_t)(r * (int)kv_stride + dma_chunk) * 2u;
+      const uint32_t off = (__umul24(r, (uint32_t)kv_stride) + dma_chunk) * 2u;  // r < 64: 24-bit product
       const int lofs = (16 * wave + 8 * ii) * RS;
       dma16(kt, off, (lds_void*)(&Ks[buf][lofs]));
       dma16(vt, off, (lds_void*)(&Vs[buf][lofs]));

@@ -302,7 +302,7 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int r = min(16 * wave + 8 * i + (lane >> 3), hi - j0);
-        const uint32_t off = (uint32_t)(r * (int)kv_stride + dma_chunk) * 2u;
+        const uint32_t off = (__umul24(r, (uint32_t)kv_stride) + dma_chunk) * 2u;  // r < 64: 24-bit product
         const int lofs = (16 * wave + 8 * i) * RS;  // wave-uniform slice of 8 rows
         dma16(kt, off, (lds_void*)(&Ks[buf][lofs]));
         dma16(vt, off, (lds_void*)(&Vs[buf][lofs]));
