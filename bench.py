@@ -252,7 +252,8 @@ def summarize_trace(trace_dir, out_md=None):
              "    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o run -- "
              "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline",
              "    python3 bench.py --summarize-trace gpurun_out/prof_trace", "",
-             "Every stage runs 13 times (3 warm-up + 10 timed). rocprofv3 `--stats` summary (all stages of one kernel "
+             "Every stage runs 35 times: 3 warm-up, 10 in the step loop, 10 cold (each after a 512 MiB fill, the "
+             "`FillFunctor<int>` rows), 2 + 10 back to back. rocprofv3 `--stats` summary (all stages of one kernel "
              "pooled):", "",
              "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
     with open(stats[0]) as f:
