@@ -48,11 +48,16 @@ __all__ = [
     "GQA_BF16",
     "GQA_FP32",
     "GqaError",
+    "debug_flags",
 ]
 
 GQA_BF16 = 0
 GQA_FP32 = 1
 GQA_OK = 0
+GQA_ERR_INVALID_ARG = -1
+GQA_ERR_UNSUPPORTED = -2
+GQA_ERR_WORKSPACE = -3
+GQA_ERR_HIP = -4
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libgqa_attn.so"
@@ -80,6 +85,7 @@ _SIGNATURES = {
     "gqa_attn_version": (_I, []),
     "gqa_attn_status_string": (ctypes.c_char_p, [_I]),
     "gqa_attn_last_error": (ctypes.c_char_p, []),
+    "gqa_attn_debug_flags": (_I, [ctypes.POINTER(ctypes.c_uint), _I]),
     "gqa_attn_prefill": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "gqa_attn_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "gqa_attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
@@ -114,6 +120,25 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
+# device-side metadata clamp records (gqa_attn_debug_flags, libraries built with GQA_DEBUG)
+GQA_DBG_SEQLENS_K = 1
+GQA_DBG_BLOCK_TABLE = 2
+GQA_DBG_CU_SEQLENS_Q = 4
+GQA_DBG_PACKED_ROW = 8
+GQA_DBG_Q_LEN = 16
+
+
+def debug_flags(reset: bool = True) -> int:
+    """OR of the GQA_DBG_* kinds of device-side metadata the kernels had to clamp
+    since the last reset (synchronises the device).  Needs the library built with
+    GQA_DEBUG (``python -m attention_gqa_causal_amd.build --debug``, then
+    GQA_ATTN_LIB pointing at libgqa_attn_debug.so); a release library raises
+    GqaError (GQA_ERR_UNSUPPORTED)."""
+    flags = ctypes.c_uint(0)
+    _check(lib().gqa_attn_debug_flags(ctypes.byref(flags), 1 if reset else 0))
+    return int(flags.value)
+
+
 def _check(status: int):
     if status != GQA_OK:
         L = lib()
@@ -122,6 +147,15 @@ def _check(status: int):
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _out_arg(out, q):
+    """A caller's output tensor (checked against q), or a new one."""
+    if out is None:
+        return torch.empty_like(q)
+    _check_tensor(out, "out", q.dtype, q.device, q.dim())
+    _need(out.shape == q.shape, "out must match q")
+    return out
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -251,12 +285,13 @@ def decode_workspace_size(B, Lmax, Hq, Hkv, D=64, window=0, dtype=GQA_BF16, sink
 
 
 def attn_decode(q, kv_cache, seqlens, sinks=None, window: int = 0, scale=None, return_lse: bool = False,
-                workspace=None, sink_tokens: int = 0):
+                workspace=None, sink_tokens: int = 0, out=None):
     """One new query token per sequence against a contiguous KV cache.
 
     q [B, Hq, 64]; kv_cache = (k_cache, v_cache) each [B, Lmax, Hkv, 64], or one
     [2, B, Lmax, Hkv, 64] tensor; seqlens [B] int32 on the GPU (cached positions
-    including the new token).  Returns out [B, Hq, 64] (and lse [B, Hq]).
+    including the new token).  Returns out [B, Hq, 64] (and lse [B, Hq]); out
+    may be given (a contiguous tensor like q).
     """
     dev = q.device
     _check_tensor(q, "q", q.dtype, dev, 3)
@@ -270,7 +305,7 @@ def attn_decode(q, kv_cache, seqlens, sinks=None, window: int = 0, scale=None, r
     _check_tensor(seqlens, "seqlens", torch.int32, dev, 1)
     _need(seqlens.shape[0] == B, "seqlens must have B entries")
     sinks = _sinks_arg(sinks, Hq, dev)
-    out = torch.empty_like(q)
+    out = _out_arg(out, q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None
     ws_bytes = int(lib().gqa_attn_decode_workspace_size(B, Lmax, Hq, Hkv, D, int(window), int(sink_tokens), dt))
     if ws_bytes and workspace is None:
@@ -289,7 +324,7 @@ def varlen_workspace_size(B, max_q_len, max_kv_len, Hq, Hkv, D=64, window=0, dty
 
 def attn_varlen_paged(q, kv_cache, block_table, cu_seqlens_q, seqlens_k, sinks=None, window: int = 0, scale=None,
                       max_q_len: int | None = None, max_kv_len: int | None = None, cu_seqlens_k=None,
-                      return_lse: bool = False, workspace=None, sink_tokens: int = 0):
+                      return_lse: bool = False, workspace=None, sink_tokens: int = 0, out=None):
     """Packed variable-length queries over a paged KV cache (mixed prefill chunks and decode steps).
 
     q [Tq, Hq, 64]; kv_cache = (k_cache, v_cache) each [num_blocks, block_size, Hkv, 64]
@@ -297,7 +332,8 @@ def attn_varlen_paged(q, kv_cache, block_table, cu_seqlens_q, seqlens_k, sinks=N
     [num_rows, Hkv, 64] caches addressed by cu_seqlens_k [B+1].  cu_seqlens_q [B+1]
     and seqlens_k [B] are int32 on the GPU.  max_q_len / max_kv_len are host-side
     bounds; when omitted they are read back from the GPU (a synchronising copy).
-    Returns out [Tq, Hq, 64] (and lse [Hq, Tq]).
+    Returns out [Tq, Hq, 64] (and lse [Hq, Tq]); out may be given (a contiguous
+    tensor like q).
     """
     dev = q.device
     _check_tensor(q, "q", q.dtype, dev, 3)
@@ -332,7 +368,7 @@ def attn_varlen_paged(q, kv_cache, block_table, cu_seqlens_q, seqlens_k, sinks=N
     if max_kv_len is None:
         max_kv_len = cap if cap is not None else (int(seqlens_k.max().item()) if B else 0)
     sinks = _sinks_arg(sinks, Hq, dev)
-    out = torch.empty_like(q)
+    out = _out_arg(out, q)
     lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev) if return_lse else None
     ws_bytes = int(lib().gqa_attn_varlen_workspace_size(B, max_q_len, max_kv_len, Hq, Hkv, D, int(window),
                                                         int(sink_tokens), dt))

@@ -126,7 +126,27 @@ size_t decode_ws_bytes(const SplitPlan& p, int B, int Hq) {
 
 extern "C" {
 
-int gqa_attn_version(void) { return 400; }
+int gqa_attn_version(void) { return 500; }
+
+int gqa_attn_debug_flags(unsigned int* flags, int reset) {
+  if (!flags) return fail(GQA_ERR_INVALID_ARG, "flags is NULL");
+  *flags = 0;
+#ifndef GQA_DEBUG
+  (void)reset;
+  return fail(GQA_ERR_UNSUPPORTED, "release build: device-side metadata is clamped but not recorded");
+#else
+  hipError_t (*const fns[])(unsigned int*, bool) = {gqa::debug_flags_prefill, gqa::debug_flags_decode,
+                                                    gqa::debug_flags_fp32,    gqa::debug_flags_ring,
+                                                    gqa::debug_flags_rope,    gqa::debug_flags_backward};
+  for (auto fn : fns) {
+    unsigned int v = 0;
+    const hipError_t e = fn(&v, reset != 0);
+    if (e != hipSuccess) return hip_fail(e, "debug flag copy");
+    *flags |= v;
+  }
+  return ok();
+#endif
+}
 
 const char* gqa_attn_status_string(int status) {
   switch (status) {
@@ -300,6 +320,7 @@ int gqa_attn_varlen_paged(const void* q, const void* k_cache, const void* v_cach
   seq.log2_block = log2b;
   seq.num_blocks = num_blocks;
   seq.lmax = max_kv_len;
+  seq.q_rows = Tq;
   const float sl2 = scale_log2_of(scale, D);
 
   if (dtype == GQA_FP32) {

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gqa_attn.h"
+
 namespace gqa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -19,6 +21,48 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -3.0e38f;  // finite floor for running maxima (avoids inf - inf)
 
 constexpr int kHeadDim = 64;
+
+// ---------------------------------------------------------------------------
+// device-side metadata checks
+//
+// Metadata the kernels read from device memory (sequence lengths, query
+// offsets, block tables) is clamped so that no access leaves the caller's
+// buffers, whatever it holds.  Built with GQA_DEBUG the kernels also record
+// every kind of value they had to clamp, as bits of a flag word that
+// gqa_attn_debug_flags() reads back; release builds only clamp.
+// (the GQA_DBG_* bits of gqa_attn.h)
+constexpr unsigned kDbgSeqlensK = GQA_DBG_SEQLENS_K;
+constexpr unsigned kDbgBlockTable = GQA_DBG_BLOCK_TABLE;
+constexpr unsigned kDbgCuSeqlensQ = GQA_DBG_CU_SEQLENS_Q;
+constexpr unsigned kDbgPackedRow = GQA_DBG_PACKED_ROW;
+constexpr unsigned kDbgQLen = GQA_DBG_Q_LEN;
+
+#ifdef GQA_DEBUG
+static __device__ unsigned int g_debug_flags;  // one per translation unit
+#define GQA_FLAG(cond, bit)                                      \
+  do {                                                           \
+    if (cond) atomicOr(&::gqa::g_debug_flags, (unsigned)(bit));  \
+  } while (0)
+// Host accessor of this translation unit's flag word (synchronising copy).
+#define GQA_DEBUG_FLAGS_ACCESSOR(fn)                                                        \
+  hipError_t fn(unsigned int* flags, bool reset) {                                          \
+    hipError_t e = hipMemcpyFromSymbol(flags, HIP_SYMBOL(g_debug_flags), sizeof(unsigned)); \
+    if (e == hipSuccess && reset) {                                                         \
+      const unsigned zero = 0;                                                              \
+      e = hipMemcpyToSymbol(HIP_SYMBOL(g_debug_flags), &zero, sizeof(unsigned));            \
+    }                                                                                       \
+    return e;                                                                               \
+  }
+#else
+#define GQA_FLAG(cond, bit) \
+  do {                      \
+  } while (0)
+#define GQA_DEBUG_FLAGS_ACCESSOR(fn)                       \
+  hipError_t fn(unsigned int* flags, bool /*reset*/) {     \
+    *flags = 0;                                            \
+    return hipSuccess;                                     \
+  }
+#endif
 
 // ---------------------------------------------------------------------------
 // addressing of sequences
@@ -48,6 +92,7 @@ struct SeqArgs {
   int log2_block;
   int num_blocks;  // paged: number of physical blocks; packed: number of rows
   int lmax;        // batched: Lmax (row stride per sequence)
+  int q_rows;      // varlen: packed query rows (Tq), the bound of cu_seqlens_q
 };
 
 struct SeqView {
@@ -57,28 +102,41 @@ struct SeqView {
   int b;
 };
 
+// Packed query rows [r0, r1) of sequence b, clamped to [0, q_rows].
+__device__ __forceinline__ void q_range(const SeqArgs& a, int b, int& r0, int& r1) {
+  const int c0 = a.cu_seqlens_q[b];
+  const int c1 = a.cu_seqlens_q[b + 1];
+  r0 = min(max(c0, 0), a.q_rows);
+  r1 = min(max(c1, r0), a.q_rows);
+  GQA_FLAG(r0 != c0 || r1 != c1, kDbgCuSeqlensQ);
+}
+
 template <int MODE>
 __device__ __forceinline__ SeqView seq_view(const SeqArgs& a, int b, bool varlen_q) {
   SeqView s;
   s.b = b;
   if (varlen_q) {
-    int r0 = a.cu_seqlens_q[b];
-    int r1 = a.cu_seqlens_q[b + 1];
+    int r0, r1;
+    q_range(a, b, r0, r1);
     s.q_row0 = r0;
-    s.q_len = max(r1 - r0, 0);
+    s.q_len = r1 - r0;
   } else {
     s.q_row0 = (int64_t)b * a.q_len_fixed;
     s.q_len = a.q_len_fixed;
   }
   if (a.seqlens_k) {
-    int L = a.seqlens_k[b];
+    const int L0 = a.seqlens_k[b];
+    int L = L0;
     if (MODE == KV_BATCHED) L = min(L, a.lmax);
     if (MODE == KV_PAGED) L = min(L, a.max_blocks << a.log2_block);
-    s.kv_len = max(L, 0);
+    L = max(L, 0);
+    GQA_FLAG(L != L0, kDbgSeqlensK);
+    s.kv_len = L;
   } else {
     s.kv_len = a.kv_len_fixed;
   }
   // queries are the newest positions; never more queries than positions
+  GQA_FLAG(s.q_len > s.kv_len, kDbgQLen);
   if (s.q_len > s.kv_len) s.q_len = s.kv_len;
   return s;
 }
@@ -88,13 +146,16 @@ __device__ __forceinline__ int64_t kv_row(const SeqArgs& a, const SeqView& s, in
   if (MODE == KV_BATCHED) {
     return (int64_t)s.b * a.lmax + j;
   } else if (MODE == KV_PAGED) {
-    int blk = a.block_table[(int64_t)s.b * a.max_blocks + (j >> a.log2_block)];
-    blk = min(max(blk, 0), a.num_blocks - 1);
+    const int blk0 = a.block_table[(int64_t)s.b * a.max_blocks + (j >> a.log2_block)];
+    const int blk = min(max(blk0, 0), a.num_blocks - 1);
+    GQA_FLAG(blk != blk0, kDbgBlockTable);
     return ((int64_t)blk << a.log2_block) + (j & ((1 << a.log2_block) - 1));
   } else {
-    int64_t r = (int64_t)a.cu_seqlens_k[s.b] + j;
-    r = r < 0 ? 0 : r;
-    return r < a.num_blocks ? r : (int64_t)a.num_blocks - 1;
+    const int64_t r0 = (int64_t)a.cu_seqlens_k[s.b] + j;
+    int64_t r = r0 < 0 ? 0 : r0;
+    r = r < a.num_blocks ? r : (int64_t)a.num_blocks - 1;
+    GQA_FLAG(r != r0, kDbgPackedRow);
+    return r;
   }
 }
 

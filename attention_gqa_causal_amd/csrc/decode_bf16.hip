@@ -133,6 +133,7 @@ __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a)
       int64_t row;
       if (MODE == KV_PAGED) {
         const int bb = min(max(blk[i], 0), a.seq.num_blocks - 1);
+        GQA_FLAG(bb != blk[i], kDbgBlockTable);
         row = ((int64_t)bb << a.seq.log2_block) + (j & ((1 << a.seq.log2_block) - 1));
       } else {
         row = kv_row<MODE>(a.seq, sv, j);
@@ -338,8 +339,9 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   int64_t q_row = b;
   int64_t row0 = 0;
   if (a.varlen_q) {
-    const int r0 = a.seq.cu_seqlens_q[b];
-    if (a.seq.cu_seqlens_q[b + 1] - r0 != 1) return;
+    int r0, r1;
+    q_range(a.seq, b, r0, r1);
+    if (r1 - r0 != 1) return;
     q_row = r0;
     row0 = r0;
   }
@@ -389,5 +391,8 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int kv_mode, hipStream_t s) {
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.Hq), dim3(64), 0, s, a);
   return hipGetLastError();
 }
+
+// Metadata-check flags of this file's kernels (recorded only when built with GQA_DEBUG).
+GQA_DEBUG_FLAGS_ACCESSOR(debug_flags_decode)
 
 }  // namespace gqa

@@ -95,4 +95,7 @@ hipError_t launch_fp32(const Fp32Args& a, int kv_mode, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Metadata-check flags of this file's kernels (recorded only when built with GQA_DEBUG).
+GQA_DEBUG_FLAGS_ACCESSOR(debug_flags_fp32)
+
 }  // namespace gqa

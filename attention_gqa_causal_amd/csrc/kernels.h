@@ -144,4 +144,13 @@ hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s);
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
 void backward_plan(int B, int S, int Hkv, int window, int sink_tokens, int* n_slabs, int* slab_len);  // split of the dK/dV query ranges
 
+// Metadata-check flag words, one per kernel file (common.h); zero unless built
+// with GQA_DEBUG.  Each call copies synchronously and optionally clears.
+hipError_t debug_flags_backward(unsigned int* flags, bool reset);
+hipError_t debug_flags_decode(unsigned int* flags, bool reset);
+hipError_t debug_flags_fp32(unsigned int* flags, bool reset);
+hipError_t debug_flags_prefill(unsigned int* flags, bool reset);
+hipError_t debug_flags_ring(unsigned int* flags, bool reset);
+hipError_t debug_flags_rope(unsigned int* flags, bool reset);
+
 }  // namespace gqa

@@ -315,6 +315,7 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
       int64_t row;
       if (MODE == KV_PAGED) {
         const int bb = min(max(blk[i], 0), a.seq.num_blocks - 1);
+        GQA_FLAG(bb != blk[i], kDbgBlockTable);
         row = ((int64_t)bb << a.seq.log2_block) + (j & ((1 << a.seq.log2_block) - 1));
       } else {
         row = kv_row<MODE>(a.seq, sv, j);
@@ -608,5 +609,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int kv_mode, bool varlen_q,
 #undef GQA_LAUNCH
   return hipGetLastError();
 }
+
+// Metadata-check flags of this file's kernels (recorded only when built with GQA_DEBUG).
+GQA_DEBUG_FLAGS_ACCESSOR(debug_flags_prefill)
 
 }  // namespace gqa

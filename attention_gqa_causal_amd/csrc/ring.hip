@@ -70,4 +70,7 @@ hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Metadata-check flags of this file's kernels (recorded only when built with GQA_DEBUG).
+GQA_DEBUG_FLAGS_ACCESSOR(debug_flags_ring)
+
 }  // namespace gqa

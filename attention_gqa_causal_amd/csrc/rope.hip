@@ -170,6 +170,7 @@ __global__ __launch_bounds__(RP_THREADS) void rope_append_kernel(RopeAppendArgs 
       const int nb = p >> a.log2_block;
       if (nb < a.max_blocks) {
         int blk = a.block_table[(int64_t)b * a.max_blocks + nb];
+        GQA_FLAG(blk < 0 || blk >= a.num_blocks, kDbgBlockTable);
         blk = min(max(blk, 0), a.num_blocks - 1);
         dst = ((int64_t)blk << a.log2_block) + (p & ((1 << a.log2_block) - 1));
       }
@@ -208,5 +209,8 @@ hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s) {
 #undef GQA_ROPE
   return hipGetLastError();
 }
+
+// Metadata-check flags of this file's kernels (recorded only when built with GQA_DEBUG).
+GQA_DEBUG_FLAGS_ACCESSOR(debug_flags_rope)
 
 }  // namespace gqa

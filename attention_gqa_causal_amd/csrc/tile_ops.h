@@ -126,30 +126,48 @@ __device__ __forceinline__ void mask_half(f32x16& s, int h, int j0, int plo, int
 // write in flight, would make every later LDS read wait for it, even reads of
 // another buffer; the tile loops instead wait for these loads themselves
 // (s_waitcnt vmcnt, then a barrier) before any wave reads the buffer they fill.
-// M0 takes the LDS address and needs one wait state before the load; the
+// M0 takes the LDS address (one wait state before the load) and gets its old
+// value back afterwards, since the compiler does not track M0 across asm; the
 // leading s_nop covers a base address just written to SGPRs by a vector
-// instruction (five wait states).
+// instruction (five wait states).  Base and LDS address go through
+// readfirstlane, so they are scalar operands whatever the compiler proved.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ uint32_t lds_addr(lds_void* p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
+}
 __device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, lds_void* lds_dst) {
-  const uint32_t m0v = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_dst));
-  asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(gbase), "s"(m0v)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_nop 4\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(uniform_ptr(gbase)), "s"(lds_addr(lds_dst))
+      : "memory");
 }
 // 4-byte form (lane i lands at byte 4 i past lds_dst), same contract.
 __device__ __forceinline__ void dma4(const char* gbase, uint32_t voff, lds_void* lds_dst) {
-  const uint32_t m0v = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_dst));
-  asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :
-               : "v"(voff), "s"(gbase), "s"(m0v)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_nop 4\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(uniform_ptr(gbase)), "s"(lds_addr(lds_dst))
+      : "memory");
 }
+// 16-byte form with a 64-bit per-lane address (no scalar base).
 __device__ __forceinline__ void dma16(const void* gaddr, lds_void* lds_dst) {
-  const uint32_t m0v = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_dst));
-  asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gaddr), "s"(m0v)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gaddr), "s"(lds_addr(lds_dst))
+      : "memory");
 }
 
 // Pin the instruction order: nothing is scheduled across this point.

@@ -97,6 +97,36 @@ const char* gqa_attn_status_string(int status);
 const char* gqa_attn_last_error(void);
 
 /*
+ * Device-side metadata checks.
+ *
+ * Metadata the kernels read from device memory (seqlens_k / seqlens,
+ * cu_seqlens_q, cu_seqlens_k, block tables) cannot be validated before the
+ * launch without a synchronisation, so the kernels clamp it: a sequence length
+ * to the cache capacity, a query range to [0, Tq], a block id to
+ * [0, num_blocks), a packed row to [0, num_rows).  No access then leaves the
+ * caller's buffers, and results for metadata that needed clamping are
+ * unspecified.  A library built with GQA_DEBUG (`python -m
+ * attention_gqa_causal_amd.build --debug` writes libgqa_attn_debug.so) also
+ * records each kind of value it had to clamp:
+ */
+enum gqa_debug_flag {
+  GQA_DBG_SEQLENS_K = 1,     /* a sequence length < 0 or above the cache capacity */
+  GQA_DBG_BLOCK_TABLE = 2,   /* a block table entry outside [0, num_blocks) */
+  GQA_DBG_CU_SEQLENS_Q = 4,  /* cu_seqlens_q outside [0, Tq] or decreasing */
+  GQA_DBG_PACKED_ROW = 8,    /* a packed KV row outside [0, num_rows) */
+  GQA_DBG_Q_LEN = 16         /* more new query tokens than KV positions */
+};
+
+/*
+ * ORs the records of every kernel into *flags (GQA_DBG_* bits) and, when
+ * reset != 0, clears them.  Synchronises the device (blocking copies), so it
+ * is a debugging call, not one for a serving loop.  Release builds set
+ * *flags = 0 and return GQA_ERR_UNSUPPORTED without touching the device.
+ * Errors: flags == NULL -> GQA_ERR_INVALID_ARG; a failed copy -> GQA_ERR_HIP.
+ */
+int gqa_attn_debug_flags(unsigned int* flags, int reset);
+
+/*
  * Prefill: causal self-attention over whole sequences of equal length.
  *   q   [B, S, Hq, D]     k, v [B, S, Hkv, D]     out [B, S, Hq, D]
  *   lse [B, Hq, S] fp32 (optional)

@@ -29,12 +29,12 @@ def L():
 
 
 def test_library_loads(L):
-    assert L.gqa_attn_version() == 400
+    assert L.gqa_attn_version() == 500
 
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -298,3 +298,26 @@ def test_backward_workspace_size(L):
 def test_backward_empty_is_ok(L):
     assert backward(L, B=0, q=None, lse=None, dout=None, dq=None, ws=None, ws_bytes=0) == 0
     assert backward(L, S=0, q=None, lse=None, dout=None, dq=None, ws=None, ws_bytes=0) == 0
+
+
+def test_release_library_reports_no_debug_records(L):
+    # release builds clamp device-side metadata without recording it: the call
+    # says so and touches no device
+    flags = ctypes.c_uint(123)
+    assert L.gqa_attn_debug_flags(ctypes.byref(flags), 1) == gq.GQA_ERR_UNSUPPORTED
+    assert flags.value == 0
+    assert L.gqa_attn_debug_flags(None, 0) == gq.GQA_ERR_INVALID_ARG
+
+
+def test_debug_library_exports_the_same_symbols():
+    path = os.path.join(ROOT, "attention_gqa_causal_amd", "libgqa_attn_debug.so")
+    if not os.path.exists(path):
+        pytest.skip("debug library not built (python -m attention_gqa_causal_amd.build --debug)")
+    D = ctypes.CDLL(path)
+    for n in declared_functions():
+        assert hasattr(D, n), n
+    D.gqa_attn_version.restype = ctypes.c_int
+    assert D.gqa_attn_version() == 500
+    # a NULL flags pointer is rejected before any device access
+    D.gqa_attn_debug_flags.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    assert D.gqa_attn_debug_flags(None, 0) == gq.GQA_ERR_INVALID_ARG

@@ -1,0 +1,224 @@
+"""The metadata-checking build (GQA_DEBUG, libgqa_attn_debug.so) on the GPU.
+
+Metadata the kernels read from device memory cannot be validated on the host
+without a synchronisation, so the kernels clamp it; the debug build also
+records each kind of value it clamped.  Checked here: on valid metadata the
+debug build records nothing and returns the release build's results bit for
+bit; block ids, sequence lengths, query offsets and query counts out of range
+are recorded by kind; every write stays inside the output (guard rows behind
+it are untouched), results stay finite, and sequences whose own metadata is
+valid get the same rows as in a call with all metadata valid.  The release
+build, given the same metadata, stays inside its buffers too.
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import attention_gqa_causal_amd as gq
+import gqa_inputs as gi
+from gpu_helpers import dev_f32, dev_i32, dev_tensor, say
+
+pytestmark = pytest.mark.gpu
+
+DEBUG_LIB = os.path.join(os.path.dirname(gq.__file__), "libgqa_attn_debug.so")
+GUARD = 3  # guard rows behind each output
+SENTINEL = 12288.0  # exact in bf16
+
+
+@pytest.fixture(scope="module")
+def libs():
+    if not os.path.exists(DEBUG_LIB):
+        pytest.fail(f"{DEBUG_LIB} missing: python -m attention_gqa_causal_amd.build --debug")
+    rel = gq.lib()
+    dbg = ctypes.CDLL(DEBUG_LIB)
+    for name, (res, args) in gq._SIGNATURES.items():
+        fn = getattr(dbg, name)
+        fn.restype = res
+        fn.argtypes = args
+    return rel, dbg
+
+
+@pytest.fixture
+def use(monkeypatch, libs):
+    """use("release") / use("debug"): route the binding's calls to that library."""
+    def _use(which):
+        monkeypatch.setattr(gq, "_lib", libs[0] if which == "release" else libs[1])
+    return _use
+
+
+def guarded(rows, Hq, D, dtype=torch.bfloat16):
+    """An output of `rows` rows with GUARD rows of a sentinel pattern behind it."""
+    big = torch.full((rows + GUARD, Hq, D), SENTINEL, dtype=dtype, device="cuda")
+    return big, big[:rows]
+
+
+def assert_guard_intact(big, rows, what):
+    tail = big[rows:].float()
+    assert torch.all(tail == SENTINEL), f"{what}: write past the output"
+
+
+def varlen_case(cfg=41):
+    return gi.varlen_problem(cfg, [300, 40, 129, 77], [30, 1, 129, 5], 16, 4, 64, block_size=16, maxblk=24)
+
+
+def run_varlen(p, W=0, table=None, cu=None, seqlens=None, max_q_len=None, max_kv_len=None):
+    Tq = p.q.shape[0]
+    big, out = guarded(Tq, p.q.shape[1], p.q.shape[2])
+    o, lse = gq.attn_varlen_paged(
+        dev_tensor(p.q, "cuda"), (dev_tensor(p.k, "cuda"), dev_tensor(p.v, "cuda")),
+        dev_i32(p.block_table if table is None else table, "cuda"),
+        dev_i32(p.cu_seqlens_q if cu is None else cu, "cuda"),
+        dev_i32(p.seqlens_k if seqlens is None else seqlens, "cuda"),
+        dev_f32(p.sinks, "cuda"), window=W,
+        max_q_len=int(p.q_lens.max()) if max_q_len is None else max_q_len,
+        max_kv_len=int(p.seqlens_k.max()) if max_kv_len is None else max_kv_len,
+        out=out, return_lse=True)
+    torch.cuda.synchronize()
+    assert_guard_intact(big, Tq, "varlen")
+    return o.clone(), lse.clone()
+
+
+def seq_rows(p, b):
+    return slice(int(p.cu_seqlens_q[b]), int(p.cu_seqlens_q[b + 1]))
+
+
+@pytest.mark.parametrize("W", [0, 16])
+def test_valid_metadata_records_nothing_and_matches_release(use, W):
+    p = varlen_case()
+    use("release")
+    o_r, l_r = run_varlen(p, W)
+    use("debug")
+    gq.debug_flags(reset=True)
+    o_d, l_d = run_varlen(p, W)
+    flags = gq.debug_flags()
+    say(f"valid varlen W={W}: flags {flags}")
+    assert flags == 0
+    assert torch.equal(o_r, o_d) and torch.equal(l_r, l_d)
+    # batched prefill and decode too
+    pp = gi.prefill_problem(42, 2, 200, 8, 2, 64)
+    q, k, v, s = (dev_tensor(pp.q, "cuda"), dev_tensor(pp.k, "cuda"), dev_tensor(pp.v, "cuda"),
+                  dev_f32(pp.sinks, "cuda"))
+    a = gq.attn_prefill(q, k, v, s, window=W).clone()
+    use("release")
+    b = gq.attn_prefill(q, k, v, s, window=W).clone()
+    assert torch.equal(a, b)
+    use("debug")
+    assert gq.debug_flags() == 0
+
+
+def test_block_ids_out_of_range(use):
+    p = varlen_case()
+    use("release")
+    o_ok, _ = run_varlen(p)
+    bad = p.block_table.copy()
+    n_blocks = p.k.shape[0]
+    bad[0, 2] = n_blocks + 1000
+    bad[2, 0] = -7
+    use("debug")
+    gq.debug_flags(reset=True)
+    o, lse = run_varlen(p, table=bad)
+    flags = gq.debug_flags()
+    say(f"block ids out of range: flags {flags}")
+    assert flags & gq.GQA_DBG_BLOCK_TABLE
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    for b in (1, 3):  # their own tables are valid
+        assert torch.equal(o[seq_rows(p, b)], o_ok[seq_rows(p, b)])
+
+
+def test_sequence_length_out_of_range(use):
+    p = varlen_case()
+    use("release")
+    o_ok, _ = run_varlen(p)
+    bad = p.seqlens_k.copy()
+    bad[1] = p.block_table.shape[1] * p.block_size + 50  # past the table's capacity
+    use("debug")
+    gq.debug_flags(reset=True)
+    o, _ = run_varlen(p, seqlens=bad)
+    flags = gq.debug_flags()
+    say(f"sequence length past capacity: flags {flags}")
+    assert flags & gq.GQA_DBG_SEQLENS_K
+    assert torch.isfinite(o.float()).all()
+    for b in (0, 2, 3):
+        assert torch.equal(o[seq_rows(p, b)], o_ok[seq_rows(p, b)])
+    # a negative length: the sequence has no positions, so no query of it is computed
+    bad = p.seqlens_k.copy()
+    bad[3] = -5
+    gq.debug_flags(reset=True)
+    run_varlen(p, seqlens=bad)
+    assert gq.debug_flags() & gq.GQA_DBG_SEQLENS_K
+
+
+def test_query_offsets_out_of_range(use):
+    p = varlen_case()
+    use("release")
+    o_ok, _ = run_varlen(p)
+    Tq = p.q.shape[0]
+    cu = p.cu_seqlens_q.copy()
+    cu[-1] = Tq + 100      # the last sequence would run past the packed rows
+    use("debug")
+    gq.debug_flags(reset=True)
+    o, _ = run_varlen(p, cu=cu, max_q_len=int(p.q_lens.max()) + 100)
+    flags = gq.debug_flags()
+    say(f"cu_seqlens_q past Tq: flags {flags}")
+    assert flags & gq.GQA_DBG_CU_SEQLENS_Q
+    assert torch.isfinite(o.float()).all()
+    for b in (0, 1, 2):
+        assert torch.equal(o[seq_rows(p, b)], o_ok[seq_rows(p, b)])
+    # decreasing offsets
+    cu = p.cu_seqlens_q.copy()
+    cu[2] = cu[1] - 1
+    gq.debug_flags(reset=True)
+    run_varlen(p, cu=cu)
+    assert gq.debug_flags() & gq.GQA_DBG_CU_SEQLENS_Q
+
+
+def test_more_queries_than_positions(use):
+    p = varlen_case()
+    bad = p.seqlens_k.copy()
+    bad[0] = 10  # sequence 0 brings 30 new queries
+    use("debug")
+    gq.debug_flags(reset=True)
+    o, _ = run_varlen(p, seqlens=bad)
+    flags = gq.debug_flags()
+    say(f"q_len > seqlens_k: flags {flags}")
+    assert flags & gq.GQA_DBG_Q_LEN
+    assert torch.isfinite(o[seq_rows(p, 1)].float()).all()
+
+
+def test_decode_lengths_out_of_range_and_reset(use):
+    d = gi.decode_problem(43, 4, 256, 8, 2, 64, seqlens=[256, 100, 1, 37])
+    q, k, v, s = (dev_tensor(d.q, "cuda"), dev_tensor(d.k, "cuda"), dev_tensor(d.v, "cuda"),
+                  dev_f32(d.sinks, "cuda"))
+    bad = np.array([300, 100, -2, 37], dtype=np.int32)  # past Lmax, valid, negative, valid
+    use("debug")
+    gq.debug_flags(reset=True)
+    big, out = guarded(4, 8, 64)
+    o = gq.attn_decode(q, (k, v), dev_i32(bad, "cuda"), s, out=out)
+    torch.cuda.synchronize()
+    assert_guard_intact(big, 4, "decode")
+    first = gq.debug_flags(reset=True)
+    second = gq.debug_flags()
+    say(f"decode lengths out of range: flags {first}, after reset {second}")
+    assert first & gq.GQA_DBG_SEQLENS_K and second == 0
+    assert torch.isfinite(o.float()).all()
+    ok = gq.attn_decode(q, (k, v), dev_i32(d.seqlens, "cuda"), s)
+    assert torch.equal(o[1], ok[1]) and torch.equal(o[3], ok[3])
+
+
+def test_release_build_stays_in_bounds(use):
+    p = varlen_case()
+    use("release")
+    bad_t = p.block_table.copy()
+    bad_t[0, 1] = 10 ** 6
+    bad_l = p.seqlens_k.copy()
+    bad_l[1] = 10 ** 6
+    cu = p.cu_seqlens_q.copy()
+    cu[-1] = p.q.shape[0] + 7
+    o, _ = run_varlen(p, table=bad_t, seqlens=bad_l, cu=cu, max_kv_len=int(p.seqlens_k.max()))
+    say("release build with out-of-range metadata: outputs finite, guard rows intact")
+    assert torch.isfinite(o.float()).all()
+    with pytest.raises(gq.GqaError):
+        gq.debug_flags()
