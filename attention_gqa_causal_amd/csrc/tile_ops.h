@@ -127,7 +127,8 @@ __device__ __forceinline__ void mask_half(f32x16& s, int h, int j0, int plo, int
 // another buffer; the tile loops instead wait for these loads themselves
 // (s_waitcnt vmcnt, then a barrier) before any wave reads the buffer they fill.
 // M0 takes the LDS address (one wait state before the load) and gets its old
-// value back afterwards, since the compiler does not track M0 across asm; the
+// value back afterwards (one wait state after), since the compiler does not
+// track M0 across asm; the
 // leading s_nop covers a base address just written to SGPRs by a vector
 // instruction (five wait states).  Base and LDS address go through
 // readfirstlane, so they are scalar operands whatever the compiler proved.
@@ -144,7 +145,7 @@ __device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, lds_void
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\ts_nop 4\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0\n\ts_nop 0"
       : "=&s"(saved)
       : "v"(voff), "s"(uniform_ptr(gbase)), "s"(lds_addr(lds_dst))
       : "memory");
@@ -154,7 +155,7 @@ __device__ __forceinline__ void dma4(const char* gbase, uint32_t voff, lds_void*
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\ts_nop 4\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
-      "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+      "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0\n\ts_nop 0"
       : "=&s"(saved)
       : "v"(voff), "s"(uniform_ptr(gbase)), "s"(lds_addr(lds_dst))
       : "memory");
@@ -164,7 +165,7 @@ __device__ __forceinline__ void dma16(const void* gaddr, lds_void* lds_dst) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\ts_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0\n\ts_nop 0"
       : "=&s"(saved)
       : "v"(gaddr), "s"(lds_addr(lds_dst))
       : "memory");
