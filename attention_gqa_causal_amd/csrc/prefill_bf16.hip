@@ -366,11 +366,12 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
       const int dl0 = W > 0 ? dh0 - W : -0x40000000, dl1 = W > 0 ? dh1 - W : -0x40000000;
       const int ds = STK ? st - j0 - 4 * lg : 0;  // off < ds: a sink token
       bf16x8 pA0[2], pA1[2], pB0[2], pB1[2];
-      // Issue priority on dense layers: a wave in its exponential phases (a)
-      // and (b) goes before the other wave of the SIMD when that one is in its
-      // matrix-only phase (c), so the vector unit is not left idle behind the
-      // older wave's MFMAs (measured 5-7 % on dense layers; windowed layers,
-      // whose jobs are mostly masked edge tiles, ran a little slower with it).
+      // Issue priority on dense layers, by phase: (b) 2, (a) 1, (c) 0.  Of the
+      // two waves of a SIMD, one in its exponential phases goes before one in
+      // its matrix-only phase (c), so the vector unit is not left idle behind
+      // the older wave's MFMAs (measured: 10 % on dense layers over equal
+      // priorities; windowed layers, whose jobs are mostly masked edge tiles,
+      // ran a little slower with it).
       if (W == 0) __builtin_amdgcn_s_setprio(1);
       // (a): the four k-steps of the half-1 scores, each followed by a quarter
       // of the half-0 exponentials (the order is pinned so that every MFMA
@@ -409,6 +410,7 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
       }
       l_run[0] += r0;
       l_run[1] += r1;
+      if (W == 0) __builtin_amdgcn_s_setprio(2);
       // (b): P V over key half 0 in four steps, each followed by a quarter of
       // the half-1 exponentials
       if (MASK) {
