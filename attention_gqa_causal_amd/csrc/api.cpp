@@ -82,19 +82,43 @@ struct SplitPlan {
   int n_splits;
   int split_len;
   int solo;  // one unit per wave (short key ranges, many units)
+  int rows;  // whole-row form: a workgroup per (sequence, split), all 8 KV heads
 };
 
 // Split of the decode key range: enough workgroups to keep about 16 per CU in
 // the queue (the streaming loads then overlap the merge of finished ones),
 // while every split keeps at least 1024 keys (4 tiles of 64 per wave).
-SplitPlan plan_splits(int B, int Hkv, int G, int Lmax, int window, int sink_tokens) {
+//
+// A contiguous cache with 8 KV heads of at most 8 query heads each and long
+// key ranges (rows_ok: the one-query-per-sequence decode call) takes the
+// whole-row form when its (sequence, split) workgroups fill the chip: splits
+// of at least 512 keys, about two workgroups per CU in all.
+SplitPlan plan_splits(int B, int Hkv, int G, int Lmax, int window, int sink_tokens, bool rows_ok) {
   // keys read per sequence at most: the window plus the sink tokens below it
   const long wk = window > 0 ? (long)window + sink_tokens : (long)Lmax;
   const int eff = (int)(wk < Lmax ? wk : Lmax);
   const int n_hc = (G + 15) / 16;
   const long units = (long)B * Hkv * n_hc;
-  SplitPlan p{1, 64, 0};
+  SplitPlan p{1, 64, 0, 0};
   if (eff <= 0 || units <= 0) return p;
+  const int rows_env = env_int("GQA_DECODE_ROWS", 1);  // 0: never, 1: when it fills the chip, 2: whenever eligible
+  if (rows_ok && Hkv == 8 && G <= 8 && rows_env != 0 && (eff >= 2048 || rows_env == 2)) {
+    const long per_cu = env_int("GQA_DECODE_ROWS_WGS", 2);
+    long want = (per_cu * num_cus() + B - 1) / B;
+    if (want > eff / 512) want = eff / 512;
+    if (want > 64) want = 64;
+    if (want < 1) want = 1;
+    const int forced = env_int("GQA_DECODE_SPLITS", 0);
+    if (forced > 0) want = forced > 256 ? 256 : forced;
+    if (rows_env == 2 || (long)B * want >= num_cus()) {
+      int len = (int)((eff + want - 1) / want);
+      len = (len + 63) & ~63;
+      p.rows = 1;
+      p.split_len = len;
+      p.n_splits = (eff + len - 1) / len;
+      return p;
+    }
+  }
   // Short ranges over many units: one wave per unit fills the chip by itself
   // and skips the cross-wave merge (at most 8 tiles of 64 keys per wave).
   if (eff <= 512 && units >= 8L * num_cus() && env_int("GQA_DECODE_SOLO", 1) != 0) {
@@ -216,7 +240,7 @@ size_t gqa_attn_decode_workspace_size(int B, int Lmax, int Hq, int Hkv, int D, i
   if (dtype != GQA_BF16 || B <= 0 || Lmax <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D != kHeadDim || window < 0 ||
       sink_tokens < 0)
     return 0;
-  const SplitPlan p = plan_splits(B, Hkv, Hq / Hkv, Lmax, window, sink_tokens);
+  const SplitPlan p = plan_splits(B, Hkv, Hq / Hkv, Lmax, window, sink_tokens, true);
   return decode_ws_bytes(p, B, Hq);
 }
 
@@ -251,7 +275,7 @@ int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, con
     return e == hipSuccess ? ok() : hip_fail(e, "decode fp32 launch");
   }
 
-  const SplitPlan p = plan_splits(B, Hkv, G, Lmax, window, sink_tokens);
+  const SplitPlan p = plan_splits(B, Hkv, G, Lmax, window, sink_tokens, true);
   const size_t need = decode_ws_bytes(p, B, Hq);
   if (need && (!workspace || workspace_bytes < need))
     return fail(GQA_ERR_WORKSPACE, "decode needs a workspace of %zu bytes (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
@@ -266,6 +290,7 @@ int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, con
   a.varlen_q = 0;
   a.lse_sb = Hq; a.lse_sh = 1; a.lse_row0 = 0;
   a.solo = p.solo;
+  a.rows = p.rows;
   if ((long long)B * Hkv * a.n_hc * a.n_splits > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
   hipError_t e = launch_decode_bf16(a, KV_BATCHED, st);
   return e == hipSuccess ? ok() : hip_fail(e, "decode bf16 launch");
@@ -276,7 +301,7 @@ size_t gqa_attn_varlen_workspace_size(int B, int max_q_len, int max_kv_len, int 
   if (dtype != GQA_BF16 || B <= 0 || max_q_len <= 0 || max_kv_len <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv ||
       D != kHeadDim || window < 0 || sink_tokens < 0)
     return 0;
-  const SplitPlan p = plan_splits(B, Hkv, Hq / Hkv, max_kv_len, window, sink_tokens);
+  const SplitPlan p = plan_splits(B, Hkv, Hq / Hkv, max_kv_len, window, sink_tokens, false);
   return decode_ws_bytes(p, B, Hq);
 }
 
@@ -335,7 +360,7 @@ int gqa_attn_varlen_paged(const void* q, const void* k_cache, const void* v_cach
     return e == hipSuccess ? ok() : hip_fail(e, "varlen fp32 launch");
   }
 
-  const SplitPlan p = plan_splits(B, Hkv, G, max_kv_len, window, sink_tokens);
+  const SplitPlan p = plan_splits(B, Hkv, G, max_kv_len, window, sink_tokens, false);
   const size_t need = decode_ws_bytes(p, B, Hq);
   if (need && (!workspace || workspace_bytes < need))
     return fail(GQA_ERR_WORKSPACE, "varlen needs a workspace of %zu bytes (got %zu)", need, workspace ? workspace_bytes : (size_t)0);

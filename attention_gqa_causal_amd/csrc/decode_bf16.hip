@@ -49,6 +49,31 @@ __device__ __forceinline__ u32x4 load_stream(const __bf16* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// A wave that holds the whole key range of query head hq (one column of O^T:
+// lane quarter lq has d = 16*dt + 4*lq + r in o[dt][r]; running max m_run in
+// log2 units, sum lt over all four quarters) folds in the sink and writes the
+// output row and its log-sum-exp.
+__device__ __forceinline__ void finish_column(const DecodeArgs& a, int b, int64_t q_row, int64_t lse_row, int hq,
+                                              int lq, float m_run, float lt, const f32x4 (&o)[4]) {
+  const float s2 = a.sinks ? a.sinks[hq] * kLog2e : -INFINITY;
+  const float Mf = fmaxf(m_run, s2);
+  const float sc = fast_exp2(m_run - Mf);
+  const float Z = fast_exp2(s2 - Mf) + lt * sc;
+  const float inv = Z > 0.f ? sc / Z : (Z == 0.f ? 0.f : Z);
+  __bf16* op = a.out + (q_row * a.Hq + hq) * (int64_t)kHeadDim + 4 * lq;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    u32x2 w;
+    w[0] = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+    w[1] = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+    *reinterpret_cast<u32x2*>(op + 16 * dt) = w;
+  }
+  if (a.lse && lq == 0) {
+    const float v = (Z == 0.f) ? -INFINITY : (Mf + __log2f(Z)) * kLn2;
+    a.lse[(int64_t)b * a.lse_sb + (int64_t)hq * a.lse_sh + lse_row] = v;
+  }
+}
+
 template <int MODE, bool SOLO>
 __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a) {
   // per wave: K tile then V tile; after the key loop the same memory holds the
@@ -234,30 +259,10 @@ __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a)
   }
 
   if (SOLO) {
-    // the wave holds its unit's whole key range: fold in the sink and finish.
-    // Lane holds O^T[d = 16*dt + 4*lq + r][head lc]; m_run is uniform over lq.
+    // the wave holds its unit's whole key range: fold in the sink and finish
     float lt = l_run + __shfl_xor(l_run, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
-    if (lc < n_heads) {
-      const int hq = h_base + lc;
-      const float s2 = a.sinks ? a.sinks[hq] * kLog2e : -INFINITY;
-      const float Mf = fmaxf(m_run, s2);
-      const float sc = fast_exp2(m_run - Mf);
-      const float Z = fast_exp2(s2 - Mf) + lt * sc;
-      const float inv = Z > 0.f ? sc / Z : (Z == 0.f ? 0.f : Z);
-      __bf16* op = a.out + (q_row * a.Hq + hq) * (int64_t)kHeadDim + 4 * lq;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        u32x2 w;
-        w[0] = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
-        w[1] = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
-        *reinterpret_cast<u32x2*>(op + 16 * dt) = w;
-      }
-      if (a.lse && lq == 0) {
-        const float v = (Z == 0.f) ? -INFINITY : (Mf + __log2f(Z)) * kLn2;
-        a.lse[(int64_t)b * a.lse_sb + (int64_t)hq * a.lse_sh + (a.lse_row0 ? sv.q_row0 : 0)] = v;
-      }
-    }
+    if (lc < n_heads) finish_column(a, b, q_row, a.lse_row0 ? sv.q_row0 : 0, h_base + lc, lq, m_run, lt, o);
     return;
   }
 
@@ -331,6 +336,202 @@ __global__ __launch_bounds__(DTHREADS, 2) void decode_split_kernel(DecodeArgs a)
   }
 }
 
+// ---- whole-row form: 8 KV heads, contiguous cache --------------------------
+// With 8 KV heads of 64 columns, one cache position's K (or V) row is 1 KB and
+// one wave load brings a whole row (lane i: bytes 16i .. 16i+15).  Whole rows
+// stream from HBM faster than the 128-byte per-head pieces the form above
+// reads, where the eight pieces of a row are fetched by eight workgroups at
+// different times.  A workgroup owns (sequence, split of the key range) and all
+// 8 KV heads.  Per 32-position tile each wave loads 8 rows of K and of V into
+// registers and stores them in the workgroup's LDS tile; then each wave
+// computes 2 KV heads, i.e. 16 query heads as the 16 MFMA columns: columns 0-7
+// are the query heads of KV head 2w, columns 8-15 those of KV head 2w+1.  The
+// S^T and O^T products take each KV head's operand in turn with the other
+// head's columns zeroed in Q^T (resp. P^T), so one accumulator holds both.
+// The next tile's loads are in flight during a tile's math.
+constexpr int RT = 32;           // positions per tile
+constexpr int RROW = 1024 + 32;  // LDS row stride in bytes: successive rows start 8 banks apart
+constexpr int RKV = RT * RROW;   // bytes of one K (or V) tile
+
+template <int MODE>
+__global__ __launch_bounds__(DTHREADS, 2) void decode_rows_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * RKV];  // K tile, V tile
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lc = lane & 15;  // column (query head) of the S^T / O^T tiles; key row of the K operand
+  const int lq = lane >> 4;
+  const int split = (int)blockIdx.x % a.n_splits;
+  const int b = (int)blockIdx.x / a.n_splits;
+
+  const SeqView sv = seq_view<MODE>(a.seq, b, false);
+  const int L = sv.kv_len;
+  const int W = a.window;
+  const int lo_all = W > 0 ? max(0, L - W) : 0;
+  const int ns = W > 0 ? min(a.sink_tokens, lo_all) : 0;  // sink tokens below the window
+  const int nv = ns + (L - lo_all);                        // keys read, "virtual" index as above
+  const int s_lo = split * a.split_len;
+  const int s_hi = min(nv, s_lo + a.split_len);
+  const int nt = s_hi > s_lo ? (s_hi - s_lo + RT - 1) / RT : 0;
+
+  const int hsel = lc >> 3;  // which of the wave's two KV heads the column belongs to
+  const int col = lc & 7;
+  const bool live = col < a.G;
+  const int hq = (2 * wave + hsel) * a.G + col;
+  const int64_t q_row = b;
+
+  // Q^T operands of the two KV heads: the lane's query head, d = 32*ks + 8*lq,
+  // in the operand of its own KV head and zero in the other.  The loads go out
+  // first and are used only once the first K/V tile is requested, so those
+  // requests do not wait for them; idle columns load a valid row and discard it.
+  u32x4 qw[2];
+  {
+    const __bf16* qp = a.q + (q_row * a.Hq + min(hq, a.Hq - 1)) * (int64_t)kHeadDim + 8 * lq;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) qw[ks] = *reinterpret_cast<const u32x4*>(qp + 32 * ks);
+  }
+  bf16x8 qh[2][2];
+  auto take_q = [&]() {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      qh[0][ks] = __builtin_bit_cast(bf16x8, live && hsel == 0 ? qw[ks] : z);
+      qh[1][ks] = __builtin_bit_cast(bf16x8, live && hsel == 1 ? qw[ks] : z);
+    }
+  };
+
+  float m_run = kNegBig, l_run = 0.f;
+  f32x4 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto key_of = [&](int v) { return v < ns ? v : lo_all + (v - ns); };
+  // tile t: this wave's rows 8*wave + i; rows past the split repeat its last
+  // row (masked below, always in bounds)
+  auto load = [&](u32x4 (&kr)[8], u32x4 (&vr)[8], int t) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int v = min(s_lo + t * RT + 8 * wave + i, s_hi - 1);
+      const int64_t row = kv_row<MODE>(a.seq, sv, key_of(v)) * (8 * kHeadDim);
+      kr[i] = load_stream(a.k + row + 8 * lane);
+      vr[i] = load_stream(a.v + row + 8 * lane);
+    }
+  };
+  auto store = [&](const u32x4 (&kr)[8], const u32x4 (&vr)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int ofs = (8 * wave + i) * RROW + 16 * lane;
+      *reinterpret_cast<u32x4*>(lds + ofs) = kr[i];
+      *reinterpret_cast<u32x4*>(lds + RKV + ofs) = vr[i];
+    }
+  };
+  // transposing V reads: lane's row / byte offset within a head's 32 x 64 V block
+  const int vofs = (4 * lq + (lc >> 2)) * RROW + 8 * (lane & 3);
+
+  auto compute = [&](int t) {
+    const int j0 = s_lo + t * RT;
+    // S^T: 2 blocks of 16 keys x 16 columns; K operand = key 16*kb + lc, d 32*ks + 8*lq
+    f32x4 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
+              lds + (16 * kb + lc) * RROW + (2 * wave + e) * 2 * kHeadDim + 2 * (32 * ks + 8 * lq));
+          acc = mfma16(ka, qh[e][ks], acc);
+        }
+      s[kb] = acc;
+    }
+    // lane holds keys j0 + 16*kb + 4*lq + r of column lc
+    if (j0 + RT > s_hi) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (j0 + 16 * kb + 4 * lq + r >= s_hi) s[kb][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx * a.scale_log2);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float rs = 0.f;
+    bf16x8 pbv;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(s[kb][r], a.scale_log2, -m_new));
+        rs += p;
+        pbv[4 * kb + r] = (__bf16)p;
+      }
+    l_run = l_run * alpha + rs;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+    // O^T += V^T P^T over the tile's 32 keys (keys 4lq..4lq+3 and 16+4lq..16+4lq+3
+    // in the lane's P^T operand, matching the rows of the transposing V reads)
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 pw = __builtin_bit_cast(u32x4, pbv);
+    const bf16x8 ph[2] = {__builtin_bit_cast(bf16x8, hsel == 0 ? pw : z), __builtin_bit_cast(bf16x8, hsel == 1 ? pw : z)};
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const char* base = lds + RKV + vofs + (2 * wave + e) * 2 * kHeadDim + 2 * 16 * dt;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * RROW));
+        const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[dt] = mfma16(__builtin_bit_cast(bf16x8, w), ph[e], o[dt]);
+      }
+  };
+  // Per tile: store the registers in LDS, request the next tile into them
+  // (its loads fly during this tile's math), compute.  The last tile is
+  // peeled off, so inside the loop every path has the same loads in flight.
+  auto step = [&](u32x4 (&kr)[8], u32x4 (&vr)[8], int t, bool refill) {
+    __syncthreads();  // every wave is done reading the previous tile
+    store(kr, vr);
+    if (refill) load(kr, vr, t + 1);
+    __syncthreads();  // the tile is in LDS
+    compute(t);
+  };
+
+  if (nt > 0) {
+    u32x4 kr[8], vr[8];
+    __builtin_amdgcn_sched_barrier(0);  // Q requested first, taken after the first tile is requested
+    load(kr, vr, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    take_q();
+    int t = 0;
+    for (; t + 1 < nt; ++t) step(kr, vr, t, true);
+    step(kr, vr, t, false);
+  }
+
+  // the wave holds its 16 columns over the split's whole key range
+  float lt = l_run + __shfl_xor(l_run, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+  if (!live) return;
+  if (a.n_splits == 1) {
+    finish_column(a, b, q_row, 0, hq, lq, m_run, lt, o);
+    return;
+  }
+  const int64_t slot = ((int64_t)b * a.Hq + hq) * a.n_splits + split;
+  if (lq == 0) {
+    a.ws_ml[slot * 2 + 0] = m_run;
+    a.ws_ml[slot * 2 + 1] = lt;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(a.ws_acc + slot * kHeadDim + 16 * dt + 4 * lq) = o[dt];
+}
+
 // Merge of the split partials: one wave per (sequence, query head), lane = output column.
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   const int lane = threadIdx.x;
@@ -379,13 +580,19 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int kv_mode, hipStream_t s) {
       hipLaunchKernelGGL((decode_split_kernel<KV_PACKED, true>), dim3(grid), dim3(DTHREADS), 0, s, a);
     return hipGetLastError();
   }
-  const int grid = units * a.n_splits;
-  if (kv_mode == KV_BATCHED)
-    hipLaunchKernelGGL((decode_split_kernel<KV_BATCHED, false>), dim3(grid), dim3(DTHREADS), 0, s, a);
-  else if (kv_mode == KV_PAGED)
-    hipLaunchKernelGGL((decode_split_kernel<KV_PAGED, false>), dim3(grid), dim3(DTHREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<KV_PACKED, false>), dim3(grid), dim3(DTHREADS), 0, s, a);
+  if (a.rows) {
+    // whole-row form: 8 KV heads of at most 8 query heads each, contiguous cache, one query per sequence
+    if (kv_mode != KV_BATCHED || a.Hkv != 8 || a.G > 8 || a.varlen_q || a.n_hc != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_rows_kernel<KV_BATCHED>), dim3(a.B * a.n_splits), dim3(DTHREADS), 0, s, a);
+  } else {
+    const int grid = units * a.n_splits;
+    if (kv_mode == KV_BATCHED)
+      hipLaunchKernelGGL((decode_split_kernel<KV_BATCHED, false>), dim3(grid), dim3(DTHREADS), 0, s, a);
+    else if (kv_mode == KV_PAGED)
+      hipLaunchKernelGGL((decode_split_kernel<KV_PAGED, false>), dim3(grid), dim3(DTHREADS), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<KV_PACKED, false>), dim3(grid), dim3(DTHREADS), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.Hq), dim3(64), 0, s, a);

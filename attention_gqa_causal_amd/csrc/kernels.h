@@ -51,6 +51,7 @@ struct DecodeArgs {
   int64_t lse_sh;
   int lse_row0;
   int solo;          // one (sequence, KV head, head chunk) per wave, whole key range (n_splits == 1)
+  int rows;          // whole-row form: a workgroup per (sequence, split) covers all 8 KV heads
 };
 
 // fp32 I/O path: one wave per (query row, query head).

@@ -178,7 +178,7 @@ def summarize_counters(fetch_dir, write_dir):
     res = {}
     # the dense B1 S4096 prefill runs the paired kernel (a heavy and a light tile group per workgroup)
     for kind, key, work in (("prefill", "prefill_bf16_paired_kernel", prefill_work(1, 4096, 64, 8, 64, 0)),
-                            ("decode", "decode_split_kernel", decode_work([8192] * 64, 64, 8, 64, 0))):
+                            ("decode", "decode_rows_kernel", decode_work([8192] * 64, 64, 8, 64, 0))):
         fk, wk = pick(fetch, key), pick(write, key)
         rd = fk * 1024.0 / f_scale
         wr = wk * 1024.0 / w_scale
@@ -855,7 +855,7 @@ def main():
             "unit": "GB/s",
             "frac": round(dd["gbps"] / PEAK_HBM_GBPS, 4),
             "traffic": load_traffic("decode"),
-            "kernel": "decode_split_kernel<KV_BATCHED> (dense, B64 x 8192)",
+            "kernel": "decode_rows_kernel (dense, B64 x 8192, whole 1 KB K/V rows)",
         }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

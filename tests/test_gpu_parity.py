@@ -219,6 +219,39 @@ def test_decode_split_counts_agree(device, monkeypatch):
     monkeypatch.delenv("GQA_DECODE_SPLITS")
 
 
+ROWS_CASES = [
+    # B, Lmax, Hq, window, sink tokens, seqlens, forced splits (None: the plan's)
+    (4, 100, 64, 0, 0, "full", None),        # one split: the workgroup finishes the rows itself
+    (3, 1, 64, 0, 0, "full", None),          # one position: an odd tile count, the pair's second tile masked
+    (5, 300, 64, 0, 0, "random", None),
+    (6, 1000, 64, 128, 0, "random", None),   # window: only the last 128 positions
+    (6, 1000, 64, 128, 4, "random", 3),      # window plus sink tokens, over three splits
+    (2, 700, 32, 0, 0, "random", 2),         # 4 query heads per KV head: half the columns idle
+    (2, 6000, 64, 0, 0, [6000, 3333], 64),   # splits past the shorter sequence are empty
+    (3, 4097, 64, 1, 0, "random", None),     # window 1
+    (4, 2500, 64, 0, 0, "random", 5),
+]
+
+
+@pytest.mark.parametrize("B,Lmax,Hq,W,n,sl,splits", ROWS_CASES)
+def test_decode_rows_form(device, monkeypatch, B, Lmax, Hq, W, n, sl, splits):
+    """The whole-row decode form (8 KV heads, every head of a position in one
+    workgroup), forced on for small shapes it would not pick by itself."""
+    monkeypatch.setenv("GQA_DECODE_ROWS", "2")
+    if splits:
+        monkeypatch.setenv("GQA_DECODE_SPLITS", str(splits))
+    cfg = 4300 + B * 7 + Lmax * 13 + Hq + W + n
+    p = gi.decode_problem(cfg, B, Lmax, Hq, 8, 64, "bf16", seqlens=None if sl == "full" else sl)
+    say(f"decode rows form B={B} Lmax={Lmax} Hq={Hq} W={W} n={n} seqlens={sl} splits={splits}")
+    out, lse = gq.attn_decode(dev_tensor(p.q, device), (dev_tensor(p.k, device), dev_tensor(p.v, device)),
+                              dev_i32(p.seqlens, device), dev_f32(p.sinks, device), window=W, sink_tokens=n,
+                              return_lse=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.decode_ref(p.q.f64, p.k.f64, p.v.f64, p.seqlens, p.sinks, W, p.scale, sink_tokens=n)
+    assert_bf16_close(to_f64(out), o_ref, "out")
+    assert_lse_close(to_f64(lse), l_ref, "lse")
+
+
 def test_decode_is_last_prefill_row(device):
     p = gi.prefill_problem(4200, 2, 300, 64, 8, 64, "bf16", std=SQRT_HALF)
     q, k, v = dev_tensor(p.q, device), dev_tensor(p.k, device), dev_tensor(p.v, device)
