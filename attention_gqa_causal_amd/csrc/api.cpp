@@ -89,10 +89,11 @@ struct SplitPlan {
 // the queue (the streaming loads then overlap the merge of finished ones),
 // while every split keeps at least 1024 keys (4 tiles of 64 per wave).
 //
-// A contiguous cache with 8 KV heads of at most 8 query heads each and long
-// key ranges (rows_ok: the one-query-per-sequence decode call) takes the
+// A contiguous cache with 8 KV heads of at most 8 query heads each (rows_ok:
+// the one-query-per-sequence decode call, ring caches included) takes the
 // whole-row form when its (sequence, split) workgroups fill the chip: splits
-// of at least 512 keys, about two workgroups per CU in all.
+// of at least 512 keys (one split for shorter ranges), about two workgroups
+// per CU in all.
 SplitPlan plan_splits(int B, int Hkv, int G, int Lmax, int window, int sink_tokens, bool rows_ok) {
   // keys read per sequence at most: the window plus the sink tokens below it
   const long wk = window > 0 ? (long)window + sink_tokens : (long)Lmax;
@@ -102,7 +103,7 @@ SplitPlan plan_splits(int B, int Hkv, int G, int Lmax, int window, int sink_toke
   SplitPlan p{1, 64, 0, 0};
   if (eff <= 0 || units <= 0) return p;
   const int rows_env = env_int("GQA_DECODE_ROWS", 1);  // 0: never, 1: when it fills the chip, 2: whenever eligible
-  if (rows_ok && Hkv == 8 && G <= 8 && rows_env != 0 && (eff >= 2048 || rows_env == 2)) {
+  if (rows_ok && Hkv == 8 && G <= 8 && rows_env != 0) {
     const long per_cu = env_int("GQA_DECODE_ROWS_WGS", 2);
     long want = (per_cu * num_cus() + B - 1) / B;
     if (want > eff / 512) want = eff / 512;

@@ -166,14 +166,19 @@ def test_ring_decode_full_size(device):
 # with one unit per wave; these cases reach that plan (2048+ units).
 
 def _solo_env(monkeypatch, on: bool):
+    # the per-head forms only (at 256+ sequences the whole-row form would take these shapes)
+    monkeypatch.setenv("GQA_DECODE_ROWS", "0")
     monkeypatch.setenv("GQA_DECODE_SOLO", "1" if on else "0")
 
 
-@pytest.mark.parametrize("solo", [True, False])
-def test_ring_decode_many_sequences(device, monkeypatch, solo):
-    _solo_env(monkeypatch, solo)
+@pytest.mark.parametrize("form", ["solo", "split", "rows"])
+def test_ring_decode_many_sequences(device, monkeypatch, form):
+    if form == "rows":
+        monkeypatch.setenv("GQA_DECODE_ROWS", "1")  # the plan's own choice at 512 sequences
+    else:
+        _solo_env(monkeypatch, form == "solo")
     r = gi.ring_problem(69, 512, 128, "random")
-    say(f"ring decode B512 W128 random lengths solo={solo}")
+    say(f"ring decode B512 W128 random lengths form={form}")
     out, lse = gq.attn_decode_ring(dev_tensor(r.q, device), (dev_tensor(r.k_ring, device),
                                    dev_tensor(r.v_ring, device)), dev_i32(r.seqlens, device),
                                    dev_f32(r.sinks, device), return_lse=True)

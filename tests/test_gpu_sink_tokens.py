@@ -57,6 +57,7 @@ def test_prefill_sink_tokens_layer_shape_sampled(device):
     (300, 400, 128, 4, True),      # one unit per wave
 ])
 def test_decode_sink_tokens(device, monkeypatch, B, Lmax, W, n, solo):
+    monkeypatch.setenv("GQA_DECODE_ROWS", "0")  # per-head forms; the whole-row form's sink-token cases are in the parity tests
     monkeypatch.setenv("GQA_DECODE_SOLO", "1" if solo else "0")
     say(f"decode sink tokens B{B} Lmax{Lmax} W={W} n={n} solo={solo}")
     d = gi.decode_problem(81, B, Lmax, 64, 8, 64, dtype="bf16", seqlens="random")
