@@ -266,11 +266,13 @@ def test_decode_is_last_prefill_row(device):
         assert_bf16_close(to_f64(op[:, -1]), o_ref[:, 0], "prefill last row")
 
 
-@pytest.mark.parametrize("W", [0, 128])
-def test_decode_batched_full(device, W):
-    """B64 cache 8192 64/8 heads bf16 N(0,1) (the batched-decode workload), every sequence checked."""
+@pytest.mark.parametrize("W,rows", [(0, "1"), (128, "1"), (0, "0")])
+def test_decode_batched_full(device, monkeypatch, W, rows):
+    """B64 cache 8192 64/8 heads bf16 N(0,1) (the batched-decode workload), every sequence checked; the
+    plan's own form (whole rows on the dense layer) and the per-head form."""
+    monkeypatch.setenv("GQA_DECODE_ROWS", rows)
     p = gi.c3_decode()
-    say(f"decode batched B64 L8192 W={W}")
+    say(f"decode batched B64 L8192 W={W} rows={rows}")
     out, lse = gq.attn_decode(dev_tensor(p.q, device), (dev_tensor(p.k, device), dev_tensor(p.v, device)),
                               dev_i32(p.seqlens, device), dev_f32(p.sinks, device), window=W, return_lse=True)
     torch.cuda.synchronize()
