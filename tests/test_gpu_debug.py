@@ -208,6 +208,29 @@ def test_decode_lengths_out_of_range_and_reset(use):
     assert torch.equal(o[1], ok[1]) and torch.equal(o[3], ok[3])
 
 
+@pytest.mark.parametrize("rows", ["0", "2"])
+def test_decode_lengths_out_of_range_64_8_heads(use, monkeypatch, rows):
+    """64/8 heads: the per-head form and the whole-row form (forced on) with lengths past Lmax and negative."""
+    monkeypatch.setenv("GQA_DECODE_ROWS", rows)
+    d = gi.decode_problem(44, 4, 256, 64, 8, 64, seqlens=[256, 100, 1, 37])
+    q, k, v, s = (dev_tensor(d.q, "cuda"), dev_tensor(d.k, "cuda"), dev_tensor(d.v, "cuda"),
+                  dev_f32(d.sinks, "cuda"))
+    bad = np.array([300, 100, -2, 37], dtype=np.int32)
+    use("debug")
+    gq.debug_flags(reset=True)
+    big, out = guarded(4, 64, 64)
+    o = gq.attn_decode(q, (k, v), dev_i32(bad, "cuda"), s, out=out)
+    torch.cuda.synchronize()
+    assert_guard_intact(big, 4, "decode")
+    flags = gq.debug_flags(reset=True)
+    say(f"decode 64/8 heads rows={rows}: lengths out of range, flags {flags}")
+    assert flags & gq.GQA_DBG_SEQLENS_K
+    assert torch.isfinite(o.float()).all()
+    use("release")
+    ok = gq.attn_decode(q, (k, v), dev_i32(d.seqlens, "cuda"), s)
+    assert torch.equal(o[1], ok[1]) and torch.equal(o[3], ok[3])
+
+
 def test_release_build_stays_in_bounds(use):
     p = varlen_case()
     use("release")
