@@ -10,9 +10,22 @@ import gqa_inputs as gi
 # bf16 I/O: max |err| <= 2e-2 and mean |err| <= 2e-3; fp32 I/O: max |err| <= 1e-4
 BF16_MAX, BF16_MEAN = 2e-2, 2e-3
 FP32_MAX = 1e-4
-# the log-sum-exp output is held to the same bar as the attention output of its
-# path: the bf16 kernels form the normaliser from the bf16-rounded weights they
-# feed to the matrix cores (relative error up to 2^-9 per weight)
+# Log-sum-exp of the bf16 paths.  The kernels form lse = m + ln Z from the same
+# fp32 scores the weights come from (bf16 products are exact in fp32, 64-term
+# fp32 sums: <= 64 u |x| with u = 2^-24, about 3e-5 for these inputs), weights
+# exp2(x c - m) of unrounded fp32 arguments (<= 4 u relative each, argument
+# rounding plus the exp2 instruction), a normaliser Z summed in fp32 from those
+# unrounded weights, and an fp32 log2.  No normaliser is one long chain of adds:
+# the prefill sums 16 keys per lane per tile in chunks of 4 and adds a running
+# sum once per 32-key half tile; the decode sums a tile per lane, adds a running
+# sum once per tile and merges at most 64 split partials.  So the longest chain
+# in a row with n visible keys is below n/16 + 40 adds, and for positive terms
+# the relative error of Z is at most that many u.  With the log2 and the final
+# multiply (2^-22 (1 + |lse|)), a row of n = 131072 keys (the longest decode
+# here) and |lse| <= 30: |err| <= (8192 + 40 + 4) u + 64 u |x| + 2^-22 * 31
+# ~= 5.2e-4.  Held to max 1e-3; the mean, a sum of independent roundings, far
+# below that, to 1e-4.
+LSE_BF16_MAX, LSE_BF16_MEAN = 1e-3, 1e-4
 
 
 def say(msg: str):
@@ -62,10 +75,12 @@ def assert_lse_close(got, ref, what="", fp32=False):
     assert (got[~fin] == ref[~fin]).all(), f"{what}: infinite lse differs"
     if fin.any():
         e = np.abs(got[fin] - ref[fin])
+        print(f"[gpu]   {what}: lse max err {e.max():.3e} mean err {e.mean():.3e}", flush=True)
         if fp32:
             assert e.max() <= FP32_MAX, f"{what}: lse max err {e.max():.3e}"
         else:
-            assert e.max() <= BF16_MAX and e.mean() <= BF16_MEAN, f"{what}: lse max {e.max():.3e} mean {e.mean():.3e}"
+            assert e.max() <= LSE_BF16_MAX and e.mean() <= LSE_BF16_MEAN, \
+                f"{what}: lse max {e.max():.3e} mean {e.mean():.3e}"
 
 
 # Gradients (backward of the prefill) are compared relative to the largest

@@ -393,20 +393,22 @@ def test_row_subset_matches_full():
 # ---------------------------------------------------------------- planted mistakes must be caught
 
 def core_pins_pass():
-    """A compact run of the independent pins; False as soon as one disagrees."""
-    try:
-        for case in golden_cases():
-            if not check_golden(case):
-                return False
-        for args in [(5, 4, 4, 2, 0, 0.5), (6, 4, 8, 2, 2, -1.0), (7, 2, 2, 1, 3, -math.inf), (4, 8, 4, 2, 1, 1.5)]:
-            if not brute_agrees(*args):
-                return False
-        q, k, v = rand_problem(99, 1, 12, 4, 2, 4)
-        sinks = np.array([0.3, -0.7, 1.1, -math.inf])
-        o, _ = oracle.prefill_ref(q, k, v, sinks, 3, None)
-        if not np.allclose(o, sdpa_reference(q, k, v, sinks, 3, 0.5), rtol=1e-11, atol=1e-12):
+    """A compact run of the independent pins; False as soon as one disagrees.
+
+    Any exception propagates: a planted mistake counts as caught only when a
+    pin compares values and finds them different, never because the mutated
+    oracle crashed.
+    """
+    for case in golden_cases():
+        if not check_golden(case):
             return False
-    except Exception:
+    for args in [(5, 4, 4, 2, 0, 0.5), (6, 4, 8, 2, 2, -1.0), (7, 2, 2, 1, 3, -math.inf), (4, 8, 4, 2, 1, 1.5)]:
+        if not brute_agrees(*args):
+            return False
+    q, k, v = rand_problem(99, 1, 12, 4, 2, 4)
+    sinks = np.array([0.3, -0.7, 1.1, -math.inf])
+    o, _ = oracle.prefill_ref(q, k, v, sinks, 3, None)
+    if not np.allclose(o, sdpa_reference(q, k, v, sinks, 3, 0.5), rtol=1e-11, atol=1e-12):
         return False
     return True
 
@@ -425,22 +427,27 @@ def mutation(fn):
 
 @mutation
 def window_one_too_wide(mp):
-    def vm(q_pos, k_pos, window):
-        p = np.asarray(q_pos)[:, None]
-        j = np.asarray(k_pos)[None, :]
+    # W + 1 keys instead of W (j >= p - W); the sink-token rule is kept
+    def vm(q_pos, k_pos, window, sink_tokens=0):
+        p = np.asarray(q_pos, dtype=np.int64)[:, None]
+        j = np.asarray(k_pos, dtype=np.int64)[None, :]
         vis = j <= p
         if window > 0:
-            vis &= j >= p - window
+            vis &= (j >= p - window) | (j < sink_tokens)
         return vis
     mp.setattr(OA, "visible_mask", vm)
 
 
 @mutation
 def not_causal(mp):
-    def vm(q_pos, k_pos, window):
-        p = np.asarray(q_pos)[:, None]
-        j = np.asarray(k_pos)[None, :]
-        return np.ones(np.broadcast_shapes(p.shape, j.shape), dtype=bool)
+    # every key visible (no causal bound); the window and sink-token rules are kept
+    def vm(q_pos, k_pos, window, sink_tokens=0):
+        p = np.asarray(q_pos, dtype=np.int64)[:, None]
+        j = np.asarray(k_pos, dtype=np.int64)[None, :]
+        vis = np.ones(np.broadcast_shapes(p.shape, j.shape), dtype=bool)
+        if window > 0:
+            vis &= (j > p - window) | (j < sink_tokens)
+        return vis
     mp.setattr(OA, "visible_mask", vm)
 
 
