@@ -11,7 +11,7 @@ Functions (names follow the C ABI in ``include/gqa_attn.h``):
 * ``attn_varlen_paged(q, kv_cache, block_table, cu_seqlens_q, seqlens_k, sinks, ...)``
 * ``rope_append(q, k, v, seqlens, kv_cache, inv_freq=None, ...)``: rotary
   encoding of new rows fused with their KV-cache append (contiguous, paged or
-  ring cache); ``rope_inv_freq(D)`` is the default frequency table
+  ring cache); inv_freq=None selects the library's default table θ_i = 10000^(-2i/D)
 * ``kv_ring_append(k_new, v_new, kv_ring, seqlens, cu_seqlens_q=None)`` and
   ``attn_decode_ring(q, kv_ring, seqlens, sinks, scale=None)``: the W-slot ring
   cache of sliding-window layers (position p in slot p % W)
@@ -37,7 +37,6 @@ __all__ = [
     "attn_varlen_paged",
     "kv_ring_append",
     "rope_append",
-    "rope_inv_freq",
     "attn_decode_ring",
     "attn_prefill_backward",
     "backward_workspace_size",
@@ -445,13 +444,6 @@ ROPE_INTERLEAVED = 0
 ROPE_HALVES = 1
 
 
-def rope_inv_freq(D: int = 64, base: float = 10000.0, device=None) -> torch.Tensor:
-    """The default RoPE frequency table θ_i = base^(-2i/D), i < D/2, fp32 (formed in fp64, rounded once)."""
-    i = torch.arange(D // 2, dtype=torch.float64)
-    t = (base ** (-2.0 * i / D)).to(torch.float32)
-    return t if device is None else t.to(device)
-
-
 def rope_append(q, k, v, seqlens, kv_cache, inv_freq=None, q_out=None, cu_seqlens_q=None, pairing=ROPE_INTERLEAVED,
                 mscale: float = 1.0, block_table=None, ring: bool = False):
     """Rotate new rows' queries and keys and append keys and values to the cache.
@@ -479,10 +471,9 @@ def rope_append(q, k, v, seqlens, kv_cache, inv_freq=None, q_out=None, cu_seqlen
     if cu_seqlens_q is not None:
         _check_tensor(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev, 1)
         _need(cu_seqlens_q.shape[0] == B + 1, "cu_seqlens_q must have B+1 entries")
-    if inv_freq is None:
-        inv_freq = rope_inv_freq(D, device=dev)
-    _check_tensor(inv_freq, "inv_freq", torch.float32, dev, 1)
-    _need(inv_freq.shape[0] == D // 2, "inv_freq must have D/2 entries")
+    if inv_freq is not None:  # None: the library's default table θ_i = 10000^(-2i/D)
+        _check_tensor(inv_freq, "inv_freq", torch.float32, dev, 1)
+        _need(inv_freq.shape[0] == D // 2, "inv_freq must have D/2 entries")
     if q_out is None:
         q_out = torch.empty_like(q)
     else:

@@ -151,7 +151,7 @@ size_t decode_ws_bytes(const SplitPlan& p, int B, int Hq) {
 
 extern "C" {
 
-int gqa_attn_version(void) { return 500; }
+int gqa_attn_version(void) { return 600; }
 
 int gqa_attn_debug_flags(unsigned int* flags, int reset) {
   if (!flags) return fail(GQA_ERR_INVALID_ARG, "flags is NULL");
@@ -245,10 +245,17 @@ size_t gqa_attn_decode_workspace_size(int B, int Lmax, int Hq, int Hkv, int D, i
   return decode_ws_bytes(p, B, Hq);
 }
 
-int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
-                    const float* sinks, void* out, float* lse, int B, int Lmax, int Hq, int Hkv, int D,
-                    int window, int sink_tokens, float scale, int dtype, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Decode over a batched cache of Lmax rows per sequence.  ring != 0: the cache
+// is a ring of Lmax slots and seqlens[b] counts the whole history; the kernels
+// take min(seqlens[b], Lmax) positions, every one of them visible.
+int decode_call(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
+                const float* sinks, void* out, float* lse, int B, int Lmax, int Hq, int Hkv, int D,
+                int window, int sink_tokens, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                void* stream, int ring) {
   int rc = check_common(Hq, Hkv, D, window, sink_tokens, scale, dtype);
   if (rc) return rc;
   if (B < 0 || Lmax < 0) return fail(GQA_ERR_INVALID_ARG, "negative size (B=%d, Lmax=%d)", B, Lmax);
@@ -263,6 +270,7 @@ int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, con
   seq.q_len_fixed = 1;
   seq.kv_len_fixed = Lmax;
   seq.lmax = Lmax;
+  seq.ring = ring;
   const float sl2 = scale_log2_of(scale, D);
 
   if (dtype == GQA_FP32) {
@@ -295,6 +303,18 @@ int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, con
   if ((long long)B * Hkv * a.n_hc * a.n_splits > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
   hipError_t e = launch_decode_bf16(a, KV_BATCHED, st);
   return e == hipSuccess ? ok() : hip_fail(e, "decode bf16 launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
+                    const float* sinks, void* out, float* lse, int B, int Lmax, int Hq, int Hkv, int D,
+                    int window, int sink_tokens, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return decode_call(q, k_cache, v_cache, seqlens, sinks, out, lse, B, Lmax, Hq, Hkv, D, window, sink_tokens,
+                     scale, dtype, workspace, workspace_bytes, stream, 0);
 }
 
 size_t gqa_attn_varlen_workspace_size(int B, int max_q_len, int max_kv_len, int Hq, int Hkv, int D, int window,
@@ -442,8 +462,8 @@ int gqa_rope_append(const void* q, const void* k, const void* v, void* q_out, co
     return fail(GQA_ERR_INVALID_ARG, "cache_kind %d is not 0 (contiguous), 1 (paged) or 2 (ring)", cache_kind);
   }
   if (B == 0 || T == 0) return ok();
-  if (!q || !k || !v || !q_out || !seqlens || !inv_freq || !k_cache || !v_cache)
-    return fail(GQA_ERR_INVALID_ARG, "q, k, v, q_out, seqlens, inv_freq, k_cache and v_cache must be non-NULL");
+  if (!q || !k || !v || !q_out || !seqlens || !k_cache || !v_cache)
+    return fail(GQA_ERR_INVALID_ARG, "q, k, v, q_out, seqlens, k_cache and v_cache must be non-NULL");
   RopeAppendArgs a{};
   a.q = q; a.k = k; a.v = v; a.q_out = q_out; a.k_cache = k_cache; a.v_cache = v_cache;
   a.inv_freq = inv_freq; a.cu_seqlens_q = cu_seqlens_q; a.seqlens = seqlens; a.block_table = block_table;
@@ -465,10 +485,10 @@ int gqa_attn_decode_ring(const void* q, const void* k_ring, const void* v_ring, 
   if (W <= 0) return fail(GQA_ERR_INVALID_ARG, "ring size W=%d must be >= 1", W);
   // The ring holds exactly the positions of the window ending at the query:
   // min(seqlens[b], W) slots, all visible.  Key order does not enter the
-  // result, so this is dense attention over the valid slots of a W-slot cache
-  // (the kernels clamp each length to W).
-  return gqa_attn_decode(q, k_ring, v_ring, seqlens, sinks, out, lse, B, W, Hq, Hkv, D, 0, 0, scale, dtype,
-                         workspace, workspace_bytes, stream);
+  // result, so this is dense attention over the valid slots of a W-slot cache,
+  // whose kernels take min(seqlens[b], W) keys as the ring's length.
+  return decode_call(q, k_ring, v_ring, seqlens, sinks, out, lse, B, W, Hq, Hkv, D, 0, 0, scale, dtype, workspace,
+                     workspace_bytes, stream, 1);
 }
 
 size_t gqa_attn_prefill_backward_workspace_size(int B, int S, int Hq, int Hkv, int D, int dtype) {

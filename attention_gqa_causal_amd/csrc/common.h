@@ -91,8 +91,10 @@ struct SeqArgs {
   int max_blocks;
   int log2_block;
   int num_blocks;  // paged: number of physical blocks; packed: number of rows
-  int lmax;        // batched: Lmax (row stride per sequence)
+  int lmax;        // batched: Lmax (row stride per sequence); varlen: max_kv_len
   int q_rows;      // varlen: packed query rows (Tq), the bound of cu_seqlens_q
+  int ring;        // batched: the cache is a ring of lmax slots and seqlens_k counts the
+                   // whole history; the ring holds min(seqlens_k[b], lmax) positions
 };
 
 struct SeqView {
@@ -125,10 +127,16 @@ __device__ __forceinline__ SeqView seq_view(const SeqArgs& a, int b, bool varlen
     s.q_len = a.q_len_fixed;
   }
   if (a.seqlens_k) {
-    const int L0 = a.seqlens_k[b];
+    int L0 = a.seqlens_k[b];
+    // a ring holds the newest min(L, W) positions of a history of L: in contract
+    if (MODE == KV_BATCHED && a.ring) L0 = min(L0, a.lmax);
     int L = L0;
+    // bounds of the length: the cache rows of a sequence (batched), the block
+    // table's capacity (paged), and max_kv_len (varlen calls: the split plan of
+    // their decode rows covers that many keys)
     if (MODE == KV_BATCHED) L = min(L, a.lmax);
-    if (MODE == KV_PAGED) L = min(L, a.max_blocks << a.log2_block);
+    if (MODE == KV_PAGED) L = min(L, min(a.lmax, a.max_blocks << a.log2_block));
+    if (MODE == KV_PACKED) L = min(L, a.lmax);
     L = max(L, 0);
     GQA_FLAG(L != L0, kDbgSeqlensK);
     s.kv_len = L;

@@ -5,8 +5,8 @@
 // Qwen3», "Adoption de RoPE": the query and key vectors are turned by an angle
 // that depends on the position.  Pair i of a head, (a, b), becomes
 // (a cos - b sin, a sin + b cos) at angle m·inv_freq[i]; the pairs are
-// (2i, 2i+1) or (i, i + d/2).  The frequency table is an input (θ_i by
-// default), and `mscale` scales cos and sin alike.
+// (2i, 2i+1) or (i, i + d/2).  The frequency table is an input; without one
+// the kernel forms θ_i itself.  `mscale` scales cos and sin alike.
 //
 // One pass over the new rows: the queries are rotated into q_out (which may
 // be q itself), the keys are rotated and written with the values into the
@@ -113,6 +113,13 @@ __device__ __forceinline__ void rotate_heads(T* dst, const T* src, int h0, int n
   }
 }
 
+// The default frequency θ_i = 10000^(-2i/d) of «GPT-OSS-20B : Architecture MoE
+// & Résumé du Model Card» §3.4, formed in fp64 and rounded once to fp32 (for
+// d = 64 every θ_i lies at least 3e-10 of its size away from an fp32 rounding
+// boundary, far beyond the fp64 error, so this is the correctly rounded fp32
+// value).
+__device__ __forceinline__ float default_inv_freq(int i) { return (float)pow(10000.0, -2.0 * i / kHeadDim); }
+
 template <typename T, int PAIRING>
 __global__ __launch_bounds__(RP_THREADS) void rope_append_kernel(RopeAppendArgs a) {
   const int lane = threadIdx.x & 63;
@@ -149,7 +156,8 @@ __global__ __launch_bounds__(RP_THREADS) void rope_append_kernel(RopeAppendArgs 
   float cs[4], sn[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const double turns = (double)p * (double)a.inv_freq[4 * c + j] * 0.15915494309189535;  // 1 / (2 pi)
+    const float f = a.inv_freq ? a.inv_freq[4 * c + j] : default_inv_freq(4 * c + j);
+    const double turns = (double)p * (double)f * 0.15915494309189535;  // 1 / (2 pi)
     const float r = (float)(turns - __builtin_rint(turns));
     cs[j] = __builtin_amdgcn_cosf(r) * a.mscale;
     sn[j] = __builtin_amdgcn_sinf(r) * a.mscale;

@@ -593,10 +593,9 @@ def add_rope(stages, gq, up, i32, dev):
     qo = torch.empty_like(q)
     sl = i32([S])
     cu = i32([0, S])
-    inv = gq.rope_inv_freq(D, device=dev)
     by = 2 * 2 * (S * Hq * D + 2 * S * Hkv * D)
     stages["rope_append_s4096"] = dict(
-        fn=(lambda: gq.rope_append(q, k, v, sl, (kc, vc), inv_freq=inv, q_out=qo, cu_seqlens_q=cu)),
+        fn=(lambda: gq.rope_append(q, k, v, sl, (kc, vc), q_out=qo, cu_seqlens_q=cu)),
         flop=0, bytes=by, bound="hbm")
     # one decode step of 64 sequences
     B = 64
@@ -609,7 +608,7 @@ def add_rope(stages, gq, up, i32, dev):
     sld = i32([1000] * B)
     byd = 2 * 2 * (B * Hq * D + 2 * B * Hkv * D)
     stages["rope_append_decode_b64"] = dict(
-        fn=(lambda: gq.rope_append(qd, kd, vd, sld, (kcd, vcd), inv_freq=inv, q_out=qod)),
+        fn=(lambda: gq.rope_append(qd, kd, vd, sld, (kcd, vcd), q_out=qod)),
         flop=0, bytes=byd, bound="hbm")
 
 

@@ -110,7 +110,7 @@ const char* gqa_attn_last_error(void);
  * records each kind of value it had to clamp:
  */
 enum gqa_debug_flag {
-  GQA_DBG_SEQLENS_K = 1,     /* a sequence length < 0 or above the cache capacity */
+  GQA_DBG_SEQLENS_K = 1,     /* a sequence length < 0, above the cache capacity or above max_kv_len */
   GQA_DBG_BLOCK_TABLE = 2,   /* a block table entry outside [0, num_blocks) */
   GQA_DBG_CU_SEQLENS_Q = 4,  /* cu_seqlens_q outside [0, Tq] or decreasing */
   GQA_DBG_PACKED_ROW = 8,    /* a packed KV row outside [0, num_rows) */
@@ -176,7 +176,8 @@ int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
  *     int32, device); num_blocks is then the row count and block_size is ignored.
  *   max_q_len (host): upper bound of any q_len; max_kv_len (host): upper
  *     bound of any seqlens_k[b] (for paged caches at most
- *     max_blocks * block_size).  Both size the grids.
+ *     max_blocks * block_size).  Both size the grids; a seqlens_k[b] above
+ *     max_kv_len is metadata out of range (clamped to it, GQA_DBG_SEQLENS_K).
  *   lse [Hq, Tq] fp32 (optional).
  */
 size_t gqa_attn_varlen_workspace_size(int B, int max_q_len, int max_kv_len, int Hq, int Hkv,
@@ -226,9 +227,11 @@ int gqa_kv_ring_append(const void* k_new, const void* v_new,
  * Decode on a windowed layer against its ring: the new query of sequence b
  * (position seqlens[b] - 1; seqlens counts the new token, whose K/V row is
  * already appended) attends to the min(seqlens[b], W) positions the ring
- * holds, which are exactly the window of W keys ending at the query.  q, out,
- * lse, sinks, scale and dtype as for gqa_attn_decode; the workspace must hold
- * gqa_attn_decode_ring_workspace_size(...) bytes (0 for W <= 1024).
+ * holds, which are exactly the window of W keys ending at the query.
+ *   seqlens [B] int32 (device): the whole history of sequence b, any value
+ *     >= 1 (it may exceed W; the kernels bound the key count by W themselves).
+ * q, out, lse, sinks, scale and dtype as for gqa_attn_decode; the workspace
+ * must hold gqa_attn_decode_ring_workspace_size(...) bytes (0 for W <= 1024).
  */
 size_t gqa_attn_decode_ring_workspace_size(int B, int W, int Hq, int Hkv, int D, int dtype);
 
@@ -250,9 +253,10 @@ int gqa_attn_decode_ring(const void* q, const void* k_ring, const void* v_ring,
  * sin both multiplied by mscale (1 for plain RoPE).
  *   pairing: GQA_ROPE_INTERLEAVED pairs coordinates (2i, 2i+1);
  *            GQA_ROPE_HALVES pairs (i, i + D/2).
- *   inv_freq [D/2] fp32 (device): θ_i for plain RoPE; a context-extension
- *     scheme (e.g. YaRN, whose parameters the pages do not give in full)
- *     passes its own table.
+ *   inv_freq [D/2] fp32 (device), or NULL for the default table
+ *     θ_i = 10000^(-2i/D) (formed by the kernel in fp64 and rounded once to
+ *     fp32); a context-extension scheme (e.g. YaRN, whose parameters the
+ *     pages do not give in full) passes its own table.
  * Rows and positions as for gqa_kv_ring_append: q [T, Hq, D], k, v [T, Hkv, D];
  * without cu_seqlens_q, T == B and row b is at position seqlens[b] - 1; with
  * cu_seqlens_q [B+1], sequence b's rows are its newest q_len positions.

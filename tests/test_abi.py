@@ -29,7 +29,7 @@ def L():
 
 
 def test_library_loads(L):
-    assert L.gqa_attn_version() == 500
+    assert L.gqa_attn_version() == 600
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -237,7 +237,6 @@ def rope(L, B=4, T=4, Hq=64, Hkv=8, D=64, dt=0, cu=None, pairing=0, mscale=1.0, 
     (dict(kind=1, bs=16, maxblk=0, nblk=9, table=DUMMY), -1),
     (dict(kind=1, bs=16, maxblk=4, nblk=9, table=None), -1),
     (dict(seqlens=None), -1),
-    (dict(inv=None), -1),
     (dict(q=None), -1),
     (dict(kc=None), -1),
     (dict(Hq=0), -1),
@@ -245,6 +244,14 @@ def rope(L, B=4, T=4, Hq=64, Hkv=8, D=64, dt=0, cu=None, pairing=0, mscale=1.0, 
 def test_rope_append_rejects(L, kw, code):
     assert rope(L, **kw) == code
     assert L.gqa_attn_last_error() != b""
+
+
+def test_rope_append_null_table_is_the_default(L):
+    # inv_freq NULL selects the library's own table: it is not an argument
+    # error (the call below fails only on the missing cache)
+    assert rope(L, inv=None, kc=None) == -1
+    err = L.gqa_attn_last_error()
+    assert b"k_cache" in err and b"inv_freq" not in err
 
 
 def test_rope_append_empty_is_ok(L):
@@ -317,7 +324,7 @@ def test_debug_library_exports_the_same_symbols():
     for n in declared_functions():
         assert hasattr(D, n), n
     D.gqa_attn_version.restype = ctypes.c_int
-    assert D.gqa_attn_version() == 500
+    assert D.gqa_attn_version() == 600
     # a NULL flags pointer is rejected before any device access
     D.gqa_attn_debug_flags.argtypes = [ctypes.c_void_p, ctypes.c_int]
     assert D.gqa_attn_debug_flags(None, 0) == gq.GQA_ERR_INVALID_ARG

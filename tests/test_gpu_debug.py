@@ -245,3 +245,52 @@ def test_release_build_stays_in_bounds(use):
     assert torch.isfinite(o.float()).all()
     with pytest.raises(gq.GqaError):
         gq.debug_flags()
+
+
+@pytest.mark.parametrize("rows,dtype", [("0", "bf16"), ("2", "bf16"), ("0", "fp32")])
+def test_valid_ring_decode_records_nothing(use, monkeypatch, rows, dtype):
+    """A ring decode whose histories are longer than, equal to and shorter than the ring is
+    within its contract: the kernels bound the key count by W themselves, so the debug build
+    records no flag, and its results are the release build's bit for bit."""
+    monkeypatch.setenv("GQA_DECODE_ROWS", rows)
+    r = gi.ring_problem(45, 4, 128, [8192, 128, 5, 129], dtype=dtype)
+    q, kr, vr, s = (dev_tensor(r.q, "cuda"), dev_tensor(r.k_ring, "cuda"), dev_tensor(r.v_ring, "cuda"),
+                    dev_f32(r.sinks, "cuda"))
+    sl = dev_i32(r.seqlens, "cuda")
+    use("debug")
+    gq.debug_flags(reset=True)
+    o_d, l_d = gq.attn_decode_ring(q, (kr, vr), sl, s, return_lse=True)
+    torch.cuda.synchronize()
+    flags = gq.debug_flags(reset=True)
+    say(f"valid ring decode rows={rows} {dtype}: flags {flags}")
+    assert flags == 0
+    use("release")
+    o_r, l_r = gq.attn_decode_ring(q, (kr, vr), sl, s, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_d, o_r) and torch.equal(l_d, l_r)
+
+
+def test_varlen_length_above_max_kv_len(use):
+    """A seqlens_k[b] above max_kv_len but within the block table's capacity is metadata out
+    of range: recorded, and clamped to max_kv_len by the decode rows and the prefill-style
+    rows alike (the split plan of decode rows covers max_kv_len keys, so no key the
+    sequence would read is silently dropped)."""
+    p = varlen_case()
+    max_kv = int(p.seqlens_k.max())
+    cap = p.block_table.shape[1] * p.block_size
+    assert max_kv + 40 <= cap
+    bad = p.seqlens_k.copy()
+    bad[1] = max_kv + 40   # a decode row (q_len 1)
+    bad[3] = max_kv + 30   # prefill-style rows (q_len 5)
+    clamped = p.seqlens_k.copy()
+    clamped[1] = max_kv
+    clamped[3] = max_kv
+    use("release")
+    o_ok, l_ok = run_varlen(p, seqlens=clamped, max_kv_len=max_kv)
+    use("debug")
+    gq.debug_flags(reset=True)
+    o, lse = run_varlen(p, seqlens=bad, max_kv_len=max_kv)
+    flags = gq.debug_flags(reset=True)
+    say(f"varlen lengths above max_kv_len: flags {flags}")
+    assert flags & gq.GQA_DBG_SEQLENS_K
+    assert torch.equal(o, o_ok) and torch.equal(lse, l_ok)

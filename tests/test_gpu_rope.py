@@ -53,11 +53,12 @@ def test_rope_decode_step_contiguous(device, dtype, pairing):
     vcache = gi.make_tensor(91, gi.T_V, (B, Lmax, Hkv, 64), 1.0, dtype)
     kc, vc = dev_tensor(cache, device), dev_tensor(vcache, device)
     k0, v0 = bits(kc), bits(vc)
-    inv = gq.rope_inv_freq(64, device=device)
+    # the oracle's default table passed explicitly (the other cases take the library's own: inv_freq NULL)
+    inv = R.default_inv_freq(64)
     qo = gq.rope_append(dev_tensor(q, device), dev_tensor(k, device), dev_tensor(v, device), dev_i32(seqlens, device),
-                        (kc, vc), inv_freq=inv, pairing=pairing)
+                        (kc, vc), inv_freq=dev_f32(inv, device), pairing=pairing)
     torch.cuda.synchronize()
-    q_ref, kc_ref, vc_ref = R.rope_append_ref(q.f64, k.f64, v.f64, seqlens, inv.cpu().numpy(), cache.f64, vcache.f64,
+    q_ref, kc_ref, vc_ref = R.rope_append_ref(q.f64, k.f64, v.f64, seqlens, inv, cache.f64, vcache.f64,
                                               R.CACHE_CONTIGUOUS, cache_len=Lmax, pairing=pairing)
     close_to_dtype(to_f64(qo), q_ref, dtype, "q")
     got_k, got_v = to_f64(kc), to_f64(vc)
@@ -138,3 +139,23 @@ def test_rope_then_decode_end_to_end(device):
                                               R.CACHE_CONTIGUOUS, cache_len=Lmax)
     o_ref, _ = oracle.decode_ref(q_ref, kc_ref, vc_ref, seqlens, d.sinks, 128, d.scale)
     assert_bf16_close(to_f64(out), o_ref, "decode after rope append")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_rope_default_table_is_the_oracles(device, dtype):
+    # inv_freq=None: the library forms θ_i = 10000^(-2i/64) itself; the results equal those
+    # of the oracle's fp32 table passed explicitly, bit for bit, out to position 131071
+    B, Lmax = 4, 64
+    seqlens = np.array([1, 4097, 65536, 131072], dtype=np.int32)
+    say(f"rope default table vs explicit oracle table {dtype}")
+    q, k, v = make_rows(98, B, 64, 8, dtype)
+    outs = []
+    for table in (None, dev_f32(R.default_inv_freq(64), device)):
+        ring_k = torch.zeros((B, Lmax, 8, 64), dtype=dev_tensor(q, device).dtype, device=device)
+        ring_v = torch.zeros_like(ring_k)
+        qo = gq.rope_append(dev_tensor(q, device), dev_tensor(k, device), dev_tensor(v, device),
+                            dev_i32(seqlens, device), (ring_k, ring_v), inv_freq=table, ring=True)
+        torch.cuda.synchronize()
+        outs.append((bits(qo), bits(ring_k)))
+    assert np.array_equal(outs[0][0], outs[1][0]), "queries"
+    assert np.array_equal(outs[0][1], outs[1][1]), "keys"
