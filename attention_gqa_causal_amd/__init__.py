@@ -38,6 +38,7 @@ __all__ = [
     "kv_ring_append",
     "rope_append",
     "attn_decode_ring",
+    "attn_decode_noalloc",
     "attn_prefill_backward",
     "backward_workspace_size",
     "decode_workspace_size",
@@ -88,6 +89,7 @@ _SIGNATURES = {
     "gqa_attn_prefill": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "gqa_attn_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "gqa_attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "gqa_attn_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "gqa_attn_varlen_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "gqa_attn_varlen_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _P, _P, _P,
                                    _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
@@ -313,6 +315,34 @@ def attn_decode(q, kv_cache, seqlens, sinks=None, window: int = 0, scale=None, r
     _check(lib().gqa_attn_decode(_ptr(q), _ptr(kc), _ptr(vc), _ptr(seqlens), _ptr(sinks), _ptr(out), _ptr(lse),
                                  B, Lmax, Hq, Hkv, D, int(window), int(sink_tokens), _scale(scale), dt,
                                  _ptr(workspace), ws_have, _stream(dev)))
+    return (out, lse) if return_lse else out
+
+
+def attn_decode_noalloc(q, kv_cache, seqlens, sinks=None, window: int = 0, scale=None, return_lse: bool = False,
+                        sink_tokens: int = 0, out=None):
+    """attn_decode through the allocation-free entry point: the split partials live in
+    the library's fixed per-GPU array (GQA_NOALLOC_SCRATCH_BYTES), not in a workspace.
+
+    Arguments as attn_decode.  Pass `out` (and nothing that needs lse) for a call that
+    allocates no device memory at all; calls that overlap on one GPU share the array.
+    """
+    dev = q.device
+    _check_tensor(q, "q", q.dtype, dev, 3)
+    dt = _dtype_code(q)
+    B, Hq, D = q.shape
+    kc, vc = _split_cache(kv_cache)
+    _check_tensor(kc, "k_cache", q.dtype, dev, 4)
+    _check_tensor(vc, "v_cache", q.dtype, dev, 4)
+    _need(kc.shape[0] == B and kc.shape[3] == D and vc.shape == kc.shape, "caches must be [B, Lmax, Hkv, D]")
+    Lmax, Hkv = kc.shape[1], kc.shape[2]
+    _check_tensor(seqlens, "seqlens", torch.int32, dev, 1)
+    _need(seqlens.shape[0] == B, "seqlens must have B entries")
+    sinks = _sinks_arg(sinks, Hq, dev)
+    out = _out_arg(out, q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None
+    _check(lib().gqa_attn_decode_noalloc(_ptr(q), _ptr(kc), _ptr(vc), _ptr(seqlens), _ptr(sinks), _ptr(out),
+                                         _ptr(lse), B, Lmax, Hq, Hkv, D, int(window), int(sink_tokens), _scale(scale),
+                                         dt, _stream(dev)))
     return (out, lse) if return_lse else out
 
 

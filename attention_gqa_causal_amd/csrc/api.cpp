@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "gqa_attn.h"
 #include "kernels.h"
@@ -315,6 +316,67 @@ int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, con
                     void* stream) {
   return decode_call(q, k_cache, v_cache, seqlens, sinks, out, lse, B, Lmax, Hq, Hkv, D, window, sink_tokens,
                      scale, dtype, workspace, workspace_bytes, stream, 0);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free decode: the split partials live in this fixed device array
+// (one copy per GPU the library runs on, held until the process ends) instead
+// of a caller's workspace.  Host code never uses the array's name as an
+// address: the per-device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[GQA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+// Device address of this GPU's scratch array, looked up once per device (with
+// that device current, on the first allocation-free call made on it).
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(GQA_ERR_UNSUPPORTED, "device %d is beyond the 64 the library tracks", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(GQA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
+                            const float* sinks, void* out, float* lse, int B, int Lmax, int Hq, int Hkv, int D,
+                            int window, int sink_tokens, float scale, int dtype, void* stream) {
+  int rc = check_common(Hq, Hkv, D, window, sink_tokens, scale, dtype);
+  if (rc) return rc;
+  if (B < 0 || Lmax < 0) return fail(GQA_ERR_INVALID_ARG, "negative size (B=%d, Lmax=%d)", B, Lmax);
+  // the partials this call needs, checked before the device is touched
+  size_t need = 0;
+  if (dtype == GQA_BF16 && B > 0 && Lmax > 0) {
+    const SplitPlan p = plan_splits(B, Hkv, Hq / Hkv, Lmax, window, sink_tokens, true);
+    need = decode_ws_bytes(p, B, Hq);
+  }
+  if (need > (size_t)GQA_NOALLOC_SCRATCH_BYTES)
+    return fail(GQA_ERR_WORKSPACE,
+                "this decode needs %zu bytes of split partials; the allocation-free decode holds at most %zu "
+                "(use gqa_attn_decode with a workspace)",
+                need, (size_t)GQA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc) return rc;
+  return decode_call(q, k_cache, v_cache, seqlens, sinks, out, lse, B, Lmax, Hq, Hkv, D, window, sink_tokens, scale,
+                     dtype, ws, (size_t)GQA_NOALLOC_SCRATCH_BYTES, stream, 0);
 }
 
 size_t gqa_attn_varlen_workspace_size(int B, int max_q_len, int max_kv_len, int Hq, int Hkv, int D, int window,

@@ -159,6 +159,29 @@ int gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): gqa_attn_decode with the same arguments, minus the workspace.
+ * Its split partials live in a fixed array of GQA_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) that the library holds on every GPU it runs on until the process
+ * ends; the call allocates nothing and makes no allocating library call.
+ * A decode that needs more partials than that (gqa_attn_decode_workspace_size
+ * of the same arguments above the limit; for 64 query heads roughly
+ * B * splits > 990) returns GQA_ERR_WORKSPACE before touching the device.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (on different streams, or from different threads without ordering) race and
+ * give unspecified results; calls in order on one stream are safe.  The array
+ * needs no clearing (every partial a call reads is written by that call).
+ */
+#define GQA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int gqa_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seqlens, const float* sinks,
+                            void* out, float* lse,
+                            int B, int Lmax, int Hq, int Hkv, int D,
+                            int window, int sink_tokens, float scale, int dtype, void* stream);
+
+/*
  * Variable-length packed queries over a paged (or packed) KV cache; mixes
  * prefill chunks and single-token decode steps in one call.
  *   q [Tq, Hq, D], out [Tq, Hq, D]; sequence b owns query rows

@@ -34,7 +34,7 @@ def test_library_loads(L):
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -328,3 +328,20 @@ def test_debug_library_exports_the_same_symbols():
     # a NULL flags pointer is rejected before any device access
     D.gqa_attn_debug_flags.argtypes = [ctypes.c_void_p, ctypes.c_int]
     assert D.gqa_attn_debug_flags(None, 0) == gq.GQA_ERR_INVALID_ARG
+
+
+def test_noalloc_decode_rejects_beyond_its_array_on_the_host(L):
+    # 64 query heads over 4 KV heads at B16 x 65536 needs 17.3 MB of split partials, more than the
+    # 16 MiB array; the call is refused before the device is touched (no GPU needed here)
+    L.gqa_attn_decode_workspace_size.restype = ctypes.c_size_t
+    assert L.gqa_attn_decode_workspace_size(16, 65536, 64, 4, 64, 0, 0, 0) > 16 << 20
+    L.gqa_attn_decode_noalloc.restype = ctypes.c_int
+    L.gqa_attn_decode_noalloc.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int,
+                                                                                         ctypes.c_void_p]
+    rc = L.gqa_attn_decode_noalloc(DUMMY, DUMMY, DUMMY, DUMMY, None, DUMMY, None, 16, 65536, 64, 4, 64, 0, 0, 0.0, 0,
+                                   None)
+    assert rc == -3
+    assert b"allocation-free" in L.gqa_attn_last_error()
+    # argument errors come first, as for every entry point
+    assert L.gqa_attn_decode_noalloc(DUMMY, DUMMY, DUMMY, DUMMY, None, DUMMY, None, 4, 64, 64, 8, 128, 0, 0, 0.0, 0,
+                                     None) == -2
