@@ -39,6 +39,7 @@ __all__ = [
     "rope_append",
     "attn_decode_ring",
     "attn_decode_noalloc",
+    "attn_decode_step",
     "attn_prefill_backward",
     "backward_workspace_size",
     "decode_workspace_size",
@@ -98,6 +99,8 @@ _SIGNATURES = {
     "gqa_attn_decode_ring": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "gqa_rope_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _I, _I, _P, _I, _I, _I,
                              _I, _I, _I, _I, _I, _I, _P]),
+    "gqa_attn_decode_step": (_I, [_P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _P,
+                                  _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "gqa_attn_prefill_backward_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "gqa_attn_prefill_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
@@ -472,6 +475,57 @@ def attn_decode_ring(q, kv_ring, seqlens, sinks=None, scale=None, return_lse: bo
 
 ROPE_INTERLEAVED = 0
 ROPE_HALVES = 1
+
+
+def attn_decode_step(q, k_new, v_new, seqlens, kv_cache, sinks=None, window: int = 0, scale=None,
+                     sink_tokens: int = 0, inv_freq=None, mscale: float = 1.0, pairing=ROPE_INTERLEAVED,
+                     block_table=None, ring: bool = False, q_out=None, return_lse: bool = False, out=None):
+    """One decode step in one launch: rotate the new token's query and key, append the
+    rotated key and the value to the cache, attend.
+
+    q [B, Hq, 64], k_new/v_new [B, Hkv, 64] bf16 (not rotated); seqlens [B] int32 counts
+    the new token.  kv_cache = (k_cache, v_cache): contiguous [B, L, Hkv, 64]; paged
+    [num_blocks, block_size, Hkv, 64] with block_table; or, with ring=True, rings
+    [B, W, Hkv, 64] (the window is W).  Returns out [B, Hq, 64] (and lse [B, Hq]);
+    q_out, if given, receives the rotated queries.
+    """
+    dev = q.device
+    _check_tensor(q, "q", torch.bfloat16, dev, 3)
+    B, Hq, D = q.shape
+    _check_tensor(k_new, "k_new", torch.bfloat16, dev, 3)
+    _check_tensor(v_new, "v_new", torch.bfloat16, dev, 3)
+    _need(k_new.shape[0] == B and k_new.shape[2] == D and v_new.shape == k_new.shape, "k_new/v_new must be [B, Hkv, D]")
+    Hkv = k_new.shape[1]
+    kc, vc = _split_cache(kv_cache)
+    _check_tensor(kc, "k_cache", torch.bfloat16, dev, 4)
+    _check_tensor(vc, "v_cache", torch.bfloat16, dev, 4)
+    _need(vc.shape == kc.shape and kc.shape[2] == Hkv and kc.shape[3] == D, "caches must be [.., .., Hkv, D]")
+    _check_tensor(seqlens, "seqlens", torch.int32, dev, 1)
+    _need(seqlens.shape[0] == B, "seqlens must have B entries")
+    if inv_freq is not None:
+        _check_tensor(inv_freq, "inv_freq", torch.float32, dev, 1)
+        _need(inv_freq.shape[0] == D // 2, "inv_freq must have D/2 entries")
+    if q_out is not None:
+        _check_tensor(q_out, "q_out", torch.bfloat16, dev, 3)
+        _need(q_out.shape == q.shape, "q_out must match q")
+    sinks = _sinks_arg(sinks, Hq, dev)
+    out = _out_arg(out, q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None
+    if block_table is not None:
+        _check_tensor(block_table, "block_table", torch.int32, dev, 2)
+        _need(block_table.shape[0] == B, "block_table must have B rows")
+        kind, cache_len = 1, 0
+        max_blocks, block_size, num_blocks = block_table.shape[1], kc.shape[1], kc.shape[0]
+    else:
+        _need(kc.shape[0] == B, "a contiguous or ring cache has B rows")
+        kind, cache_len = (2 if ring else 0), kc.shape[1]
+        max_blocks, block_size, num_blocks = 0, 0, 0
+    _check(lib().gqa_attn_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(q_out), _ptr(seqlens), _ptr(inv_freq),
+                                      float(mscale), int(pairing), _ptr(kc), _ptr(vc), kind, cache_len,
+                                      _ptr(block_table), max_blocks, block_size, num_blocks, _ptr(sinks), _ptr(out),
+                                      _ptr(lse), B, Hq, Hkv, D, int(window), int(sink_tokens), _scale(scale),
+                                      GQA_BF16, _stream(dev)))
+    return (out, lse) if return_lse else out
 
 
 def rope_append(q, k, v, seqlens, kv_cache, inv_freq=None, q_out=None, cu_seqlens_q=None, pairing=ROPE_INTERLEAVED,

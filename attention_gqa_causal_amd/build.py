@@ -25,7 +25,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgqa_attn.so")
 LIB_DEBUG = os.path.join(PKG, "libgqa_attn_debug.so")
 
-SOURCES = ["api.cpp", "prefill_bf16.hip", "decode_bf16.hip", "generic_fp32.hip", "ring.hip", "rope.hip", "backward.hip"]
+SOURCES = ["api.cpp", "prefill_bf16.hip", "decode_bf16.hip", "generic_fp32.hip", "ring.hip", "rope.hip", "backward.hip",
+           "decode_step.hip"]
 ARCH = "gfx950"
 
 

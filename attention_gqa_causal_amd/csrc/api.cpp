@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 
 #include "gqa_attn.h"
@@ -163,7 +164,8 @@ int gqa_attn_debug_flags(unsigned int* flags, int reset) {
 #else
   hipError_t (*const fns[])(unsigned int*, bool) = {gqa::debug_flags_prefill, gqa::debug_flags_decode,
                                                     gqa::debug_flags_fp32,    gqa::debug_flags_ring,
-                                                    gqa::debug_flags_rope,    gqa::debug_flags_backward};
+                                                    gqa::debug_flags_rope,    gqa::debug_flags_backward,
+                                                    gqa::debug_flags_step};
   for (auto fn : fns) {
     unsigned int v = 0;
     const hipError_t e = fn(&v, reset != 0);
@@ -535,6 +537,65 @@ int gqa_rope_append(const void* q, const void* k, const void* v, void* q_out, co
   a.pairing = pairing; a.mscale = mscale; a.fp32 = dtype == GQA_FP32;
   hipError_t e = launch_rope_append(a, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "rope append launch");
+}
+
+int gqa_attn_decode_step(const void* q, const void* k_new, const void* v_new, void* q_out, const int32_t* seqlens,
+                         const float* inv_freq, float mscale, int pairing, void* k_cache, void* v_cache,
+                         int cache_kind, int cache_len, const int32_t* block_table, int max_blocks, int block_size,
+                         int num_blocks, const float* sinks, void* out, float* lse, int B, int Hq, int Hkv, int D,
+                         int window, int sink_tokens, float scale, int dtype, void* stream) {
+  int rc = check_common(Hq, Hkv, D, window, sink_tokens, scale, dtype);
+  if (rc) return rc;
+  if (dtype != GQA_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "the fused decode step is bf16 only (fp32: gqa_rope_append, then gqa_attn_decode)");
+  if (Hq / Hkv > kStepMaxG)
+    return fail(GQA_ERR_UNSUPPORTED, "the fused decode step takes at most %d query heads per KV head (got %d)",
+                kStepMaxG, Hq / Hkv);
+  if (B < 0) return fail(GQA_ERR_INVALID_ARG, "negative batch B=%d", B);
+  if (pairing != 0 && pairing != 1) return fail(GQA_ERR_INVALID_ARG, "pairing %d is not 0 or 1", pairing);
+  if (std::isnan(mscale) || std::isinf(mscale)) return fail(GQA_ERR_INVALID_ARG, "mscale must be finite");
+  int log2b = 0;
+  long long span = 0;  // the most keys a query reads: one workgroup per (sequence, KV head) streams them all
+  if (cache_kind == GQA_CACHE_CONTIGUOUS) {
+    if (cache_len <= 0) return fail(GQA_ERR_INVALID_ARG, "cache_len %d must be >= 1", cache_len);
+    span = window > 0 ? std::min<long long>((long long)window + sink_tokens, cache_len) : cache_len;
+  } else if (cache_kind == GQA_CACHE_PAGED) {
+    if (block_size < 1 || block_size > 1024 || (block_size & (block_size - 1)))
+      return fail(GQA_ERR_UNSUPPORTED, "block_size %d is not a power of two in [1, 1024]", block_size);
+    if (max_blocks <= 0 || num_blocks <= 0) return fail(GQA_ERR_INVALID_ARG, "max_blocks and num_blocks must be >= 1");
+    if (!block_table && B > 0) return fail(GQA_ERR_INVALID_ARG, "a paged cache needs block_table");
+    while ((1 << log2b) < block_size) ++log2b;
+    const long long cap = (long long)max_blocks * block_size;
+    span = window > 0 ? std::min<long long>((long long)window + sink_tokens, cap) : cap;
+  } else if (cache_kind == GQA_CACHE_RING) {
+    if (cache_len <= 0) return fail(GQA_ERR_INVALID_ARG, "ring size %d must be >= 1", cache_len);
+    if (window != 0 && window != cache_len)
+      return fail(GQA_ERR_INVALID_ARG, "a ring of %d slots is the window; window must be 0 or %d", cache_len, cache_len);
+    if (sink_tokens != 0) return fail(GQA_ERR_UNSUPPORTED, "a ring cache holds no start-of-sequence sink tokens");
+    window = cache_len;
+    span = cache_len;
+  } else {
+    return fail(GQA_ERR_INVALID_ARG, "cache_kind %d is not 0 (contiguous), 1 (paged) or 2 (ring)", cache_kind);
+  }
+  if (span > kStepMaxKeys)
+    return fail(GQA_ERR_UNSUPPORTED,
+                "the fused decode step streams each query's keys in one workgroup and takes at most %d of them "
+                "(this call: up to %lld); use gqa_rope_append, then gqa_attn_decode",
+                kStepMaxKeys, span);
+  if (B == 0) return ok();
+  if (!q || !k_new || !v_new || !seqlens || !k_cache || !v_cache || !out)
+    return fail(GQA_ERR_INVALID_ARG, "q, k_new, v_new, seqlens, k_cache, v_cache and out must be non-NULL");
+  DecodeStepArgs a{};
+  a.q = (const __bf16*)q; a.k_new = (const __bf16*)k_new; a.v_new = (const __bf16*)v_new; a.q_out = (__bf16*)q_out;
+  a.k_cache = (__bf16*)k_cache; a.v_cache = (__bf16*)v_cache; a.seqlens = seqlens;
+  a.inv_freq = inv_freq; a.mscale = mscale; a.pairing = pairing;
+  a.cache_kind = cache_kind; a.cache_len = cache_len; a.block_table = block_table;
+  a.max_blocks = max_blocks; a.log2_block = log2b; a.num_blocks = num_blocks;
+  a.sinks = sinks; a.out = (__bf16*)out; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+  a.window = window; a.sink_tokens = sink_tokens; a.scale_log2 = scale_log2_of(scale, D);
+  hipError_t e = launch_decode_step(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "decode step launch");
 }
 
 size_t gqa_attn_decode_ring_workspace_size(int B, int W, int Hq, int Hkv, int D, int dtype) {

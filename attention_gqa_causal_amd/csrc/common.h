@@ -196,6 +196,34 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------------------
+// rotary position encoding («GPT-OSS-20B : Architecture MoE & Résumé du Model
+// Card» §3.4): position m turns pair i of a head by the angle m·θ_i
+
+// The default frequency θ_i = 10000^(-2i/d), formed in fp64 and rounded once to
+// fp32 (for d = 64 every θ_i lies at least 3e-10 of its size away from an fp32
+// rounding boundary, far beyond the fp64 error, so this is the correctly
+// rounded fp32 value).
+__device__ __forceinline__ float rope_default_freq(int i) { return (float)pow(10000.0, -2.0 * i / kHeadDim); }
+
+// cos and sin (times mscale) of the angle p·f: the angle is formed in fp64 as a
+// number of turns (the product of an integer position and an fp32 frequency is
+// exact there) and reduced to [-1/2, 1/2] before the hardware sine and cosine,
+// which take turns, so positions up to the 131 072-token context keep full
+// accuracy.
+__device__ __forceinline__ void rope_cos_sin(int p, float f, float mscale, float& cs, float& sn) {
+  const double turns = (double)p * (double)f * 0.15915494309189535;  // 1 / (2 pi)
+  const float r = (float)(turns - __builtin_rint(turns));
+  cs = __builtin_amdgcn_cosf(r) * mscale;
+  sn = __builtin_amdgcn_sinf(r) * mscale;
+}
+
+// One rotated pair: (a, b) -> (a cos - b sin, a sin + b cos).
+__device__ __forceinline__ void rope_rotate(float a, float b, float cs, float sn, float& ra, float& rb) {
+  ra = __builtin_fmaf(a, cs, -b * sn);
+  rb = __builtin_fmaf(a, sn, b * cs);
+}
+
 // Make this wave's LDS writes visible to its other lanes (and order later
 // writes after earlier reads): a wavefront-scope release/acquire pair around a
 // wave barrier.

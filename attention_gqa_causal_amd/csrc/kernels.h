@@ -109,6 +109,35 @@ struct RopeAppendArgs {
   int fp32;
 };
 
+// One decode step in one launch: rotary encoding of the new token's query and
+// key, append of the rotated key and the value to the cache, attention.
+constexpr int kStepMaxG = 8;      // query heads per KV head the fused step supports
+constexpr int kStepMaxKeys = 2048;  // keys a query of the fused step may read (one workgroup streams them)
+enum StepCacheKind : int { STEP_CACHE_CONTIGUOUS = 0, STEP_CACHE_PAGED = 1, STEP_CACHE_RING = 2 };
+struct DecodeStepArgs {
+  const __bf16* q;          // [B, Hq, D] new queries, not rotated
+  const __bf16* k_new;      // [B, Hkv, D] new keys, not rotated
+  const __bf16* v_new;      // [B, Hkv, D]
+  __bf16* q_out;            // [B, Hq, D] rotated queries, or NULL
+  __bf16* k_cache;          // contiguous [B, cache_len, Hkv, D], paged [Nblk, bs, Hkv, D], ring [B, W, Hkv, D]
+  __bf16* v_cache;
+  const int32_t* seqlens;   // [B] positions including the new token
+  const float* inv_freq;    // [D/2] or NULL (the default table)
+  float mscale;
+  int pairing;              // 0: (2i, 2i+1); 1: (i, i + D/2)
+  int cache_kind;           // StepCacheKind
+  int cache_len;            // contiguous: rows per sequence; ring: slots W
+  const int32_t* block_table;
+  int max_blocks, log2_block, num_blocks;
+  const float* sinks;
+  __bf16* out;              // [B, Hq, D]
+  float* lse;               // [B, Hq] or NULL
+  int B, Hq, Hkv, G;
+  int window;               // keys of the query: the last `window` positions (0: all), plus sink tokens
+  int sink_tokens;
+  float scale_log2;
+};
+
 // Backward of the prefill over whole sequences [B, S, H, D].
 struct BwdArgs {
   const void* q;       // [B, S, Hq, D]
@@ -143,6 +172,7 @@ hipError_t launch_fp32(const Fp32Args& a, int kv_mode, hipStream_t s);
 hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t s);
 hipError_t launch_rope_append(const RopeAppendArgs& a, hipStream_t s);
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
+hipError_t launch_decode_step(const DecodeStepArgs& a, hipStream_t s);
 void backward_plan(int B, int S, int Hkv, int window, int sink_tokens, int* n_slabs, int* slab_len);  // split of the dK/dV query ranges
 
 // Metadata-check flag words, one per kernel file (common.h); zero unless built
@@ -153,5 +183,6 @@ hipError_t debug_flags_fp32(unsigned int* flags, bool reset);
 hipError_t debug_flags_prefill(unsigned int* flags, bool reset);
 hipError_t debug_flags_ring(unsigned int* flags, bool reset);
 hipError_t debug_flags_rope(unsigned int* flags, bool reset);
+hipError_t debug_flags_step(unsigned int* flags, bool reset);
 
 }  // namespace gqa

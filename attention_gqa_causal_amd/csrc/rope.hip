@@ -84,8 +84,10 @@ __device__ __forceinline__ void rotate_heads(T* dst, const T* src, int h0, int n
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float a = Elt<T>::get(x[u], 2 * j), b = Elt<T>::get(x[u], 2 * j + 1);
-        Elt<T>::put(x[u], 2 * j, __builtin_fmaf(a, cs[j], -b * sn[j]));
-        Elt<T>::put(x[u], 2 * j + 1, __builtin_fmaf(a, sn[j], b * cs[j]));
+        float ra, rb;
+        rope_rotate(a, b, cs[j], sn[j], ra, rb);
+        Elt<T>::put(x[u], 2 * j, ra);
+        Elt<T>::put(x[u], 2 * j + 1, rb);
       }
       store_n<T, 8>(dst + (h0 + 8 * u) * kHeadDim + 8 * c, x[u]);
     }
@@ -104,21 +106,16 @@ __device__ __forceinline__ void rotate_heads(T* dst, const T* src, int h0, int n
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float a = Elt<T>::get(x[u], j), b = Elt<T>::get(y[u], j);
-        Elt<T>::put(x[u], j, __builtin_fmaf(a, cs[j], -b * sn[j]));
-        Elt<T>::put(y[u], j, __builtin_fmaf(a, sn[j], b * cs[j]));
+        float ra, rb;
+        rope_rotate(a, b, cs[j], sn[j], ra, rb);
+        Elt<T>::put(x[u], j, ra);
+        Elt<T>::put(y[u], j, rb);
       }
       store_n<T, 4>(dst + (h0 + 8 * u) * kHeadDim + 4 * c, x[u]);
       store_n<T, 4>(dst + (h0 + 8 * u) * kHeadDim + 32 + 4 * c, y[u]);
     }
   }
 }
-
-// The default frequency θ_i = 10000^(-2i/d) of «GPT-OSS-20B : Architecture MoE
-// & Résumé du Model Card» §3.4, formed in fp64 and rounded once to fp32 (for
-// d = 64 every θ_i lies at least 3e-10 of its size away from an fp32 rounding
-// boundary, far beyond the fp64 error, so this is the correctly rounded fp32
-// value).
-__device__ __forceinline__ float default_inv_freq(int i) { return (float)pow(10000.0, -2.0 * i / kHeadDim); }
 
 template <typename T, int PAIRING>
 __global__ __launch_bounds__(RP_THREADS) void rope_append_kernel(RopeAppendArgs a) {
@@ -150,18 +147,10 @@ __global__ __launch_bounds__(RP_THREADS) void rope_append_kernel(RopeAppendArgs 
   const int c = lane & 7;   // lane within its head group: pairs 4c .. 4c+3
   const int hg = lane >> 3; // head group: heads hg, hg + 8, ...
 
-  // angle in fp64 as a number of turns, reduced to [-1/2, 1/2] there (the
-  // product is exact and the reduction error is ~1e-16 of the angle); the
-  // hardware sine and cosine take turns
   float cs[4], sn[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float f = a.inv_freq ? a.inv_freq[4 * c + j] : default_inv_freq(4 * c + j);
-    const double turns = (double)p * (double)f * 0.15915494309189535;  // 1 / (2 pi)
-    const float r = (float)(turns - __builtin_rint(turns));
-    cs[j] = __builtin_amdgcn_cosf(r) * a.mscale;
-    sn[j] = __builtin_amdgcn_sinf(r) * a.mscale;
-  }
+  for (int j = 0; j < 4; ++j)
+    rope_cos_sin(p, a.inv_freq ? a.inv_freq[4 * c + j] : rope_default_freq(4 * c + j), a.mscale, cs[j], sn[j]);
 
   // heads hg, hg + 8, ... in batches of 8 per lane (64 heads: one batch)
   const T* q = reinterpret_cast<const T*>(a.q) + row * a.Hq * kHeadDim;

@@ -6,7 +6,8 @@ already resident in HBM:
      dense layer, one 128-token sliding-window layer, and one windowed layer
      that keeps 4 start-of-sequence sink tokens visible;
   2. batched decode        B64, cache 8192, same heads -- dense, window 128,
-     window 128 with 4 sink tokens;
+     window 128 with 4 sink tokens, and the windowed layer's whole decode step
+     (rotary encoding of the new token, KV append, attention) in one launch;
   3. ragged + paged        16 sequences, lengths U{128..8192}, 512-token
      prefill chunks and single-token decode steps, 16-token pages under a
      permuted block table -- dense, then window 128;
@@ -510,6 +511,18 @@ def add_decode(stages, gq, d, up, i32, f32, dev):
         ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
         stages[name] = dict(fn=(lambda W=W, ws=ws: gq.attn_decode(dq, (dk, dv), dsl, ds, window=W, workspace=ws)),
                             flop=fl, bytes=by, exp=fl // (4 * D), bound="hbm")
+    # the windowed layer's whole decode step in one launch: rotate the new token's query and key, append the
+    # key and value at the last position, attend over the last 128 (the alternative is rope_append + decode)
+    import gqa_inputs as gi
+    sq = up(gi.make_tensor(9, gi.T_Q, (Bd, Hq, D), 1.0, "bf16"))
+    sk = up(gi.make_tensor(9, gi.T_K, (Bd, Hkv, D), 1.0, "bf16"))
+    sv = up(gi.make_tensor(9, gi.T_V, (Bd, Hkv, D), 1.0, "bf16"))
+    sout = torch.empty_like(sq)
+    fl, by = decode_work([int(x) for x in d.seqlens], Hq, Hkv, D, 128)
+    by += 2 * Bd * Hkv * D * 2 * 2  # the new key and value rows: read, then written to the cache
+    stages["decode_step_swa128"] = dict(
+        fn=(lambda: gq.attn_decode_step(sq, sk, sv, dsl, (dk, dv), ds, window=128, out=sout)),
+        flop=fl, bytes=by, exp=fl // (4 * D), bound="hbm")
     fl, by = decode_work([int(x) for x in d.seqlens], Hq, Hkv, D, 128, n_sink=4)
     nbytes = gq.decode_workspace_size(Bd, Ld, Hq, Hkv, D, 128, sink_tokens=4)
     ws4 = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)

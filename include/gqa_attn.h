@@ -306,6 +306,39 @@ int gqa_rope_append(const void* q, const void* k, const void* v, void* q_out,
                     int B, int T, int Hq, int Hkv, int D, int dtype, void* stream);
 
 /*
+ * One decode step of a layer in one launch: the rotary encoding of each
+ * sequence's new token (query and key, as gqa_rope_append), the append of the
+ * rotated key and the value to the cache, and the attention of the rotated
+ * query over the cache (as gqa_attn_decode, or gqa_attn_decode_ring for a ring
+ * cache), which sees the new key and value at the new position.  It computes
+ * what gqa_rope_append followed by gqa_attn_decode computes, in one launch.
+ *   q [B, Hq, D], k_new, v_new [B, Hkv, D] bf16: the new rows, not rotated;
+ *   seqlens [B] int32 (device): positions of sequence b including the new
+ *     token, which sits at position seqlens[b] - 1;
+ *   inv_freq, mscale, pairing: as gqa_rope_append (inv_freq NULL: the default
+ *     table θ_i = 10000^(-2i/D));
+ *   q_out [B, Hq, D] bf16 or NULL: the rotated queries, if wanted;
+ *   cache_kind, cache_len, block_table, max_blocks, block_size, num_blocks:
+ *     as gqa_rope_append (contiguous, paged or ring cache);
+ *   sinks, out [B, Hq, D], lse [B, Hq] (optional), window, sink_tokens,
+ *     scale: as gqa_attn_decode.  With a ring cache the ring is the window
+ *     (window 0 or cache_len) and sink_tokens must be 0.
+ * bf16 only (fp32: GQA_ERR_UNSUPPORTED), at most 8 query heads per KV head,
+ * and at most 2048 keys per query (window + sink_tokens on windowed layers,
+ * the cache capacity on dense ones): one workgroup streams a (sequence, KV
+ * head)'s keys, which suits windowed layers and short caches; longer key
+ * ranges return GQA_ERR_UNSUPPORTED (use gqa_rope_append, then
+ * gqa_attn_decode).  Metadata out of range is clamped as for every call.
+ */
+int gqa_attn_decode_step(const void* q, const void* k_new, const void* v_new, void* q_out,
+                         const int32_t* seqlens, const float* inv_freq, float mscale, int pairing,
+                         void* k_cache, void* v_cache, int cache_kind, int cache_len,
+                         const int32_t* block_table, int max_blocks, int block_size, int num_blocks,
+                         const float* sinks, void* out, float* lse,
+                         int B, int Hq, int Hkv, int D, int window, int sink_tokens, float scale,
+                         int dtype, void* stream);
+
+/*
  * Backward of the prefill: the gradients of a loss L with respect to q, k, v
  * and the sink logits, given dL/dout.  Training the model calls for them
  * («GPT-OSS-20B : Architecture MoE & Résumé du Model Card», §5: pre-training

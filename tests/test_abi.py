@@ -34,7 +34,7 @@ def test_library_loads(L):
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
 
