@@ -38,6 +38,7 @@ __all__ = [
     "kv_ring_append",
     "rope_append",
     "attn_decode_ring",
+    "attn_prefill_ring",
     "attn_decode_noalloc",
     "attn_decode_step",
     "attn_prefill_backward",
@@ -97,6 +98,8 @@ _SIGNATURES = {
     "gqa_kv_ring_append": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "gqa_attn_decode_ring_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "gqa_attn_decode_ring": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "gqa_attn_prefill_ring": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
+                                   _P]),
     "gqa_rope_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _I, _I, _P, _I, _I, _I,
                              _I, _I, _I, _I, _I, _I, _P]),
     "gqa_attn_decode_step": (_I, [_P, _P, _P, _P, _P, _P, _F, _I, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _P,
@@ -470,6 +473,49 @@ def attn_decode_ring(q, kv_ring, seqlens, sinks=None, scale=None, return_lse: bo
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().gqa_attn_decode_ring(_ptr(q), _ptr(kr), _ptr(vr), _ptr(seqlens), _ptr(sinks), _ptr(out), _ptr(lse),
                                       B, W, Hq, Hkv, D, _scale(scale), dt, _ptr(workspace), ws_have, _stream(dev)))
+    return (out, lse) if return_lse else out
+
+
+def attn_prefill_ring(q, k_new, v_new, cu_seqlens_q, seqlens, kv_ring, sinks=None, scale=None, append: bool = True,
+                      max_q_len: int | None = None, return_lse: bool = False, out=None):
+    """Chunked prefill of a sliding-window layer over its ring: attend, then append.
+
+    q [Tq, Hq, 64], k_new/v_new [Tq, Hkv, 64]: the chunks' rows, sequence b's at
+    cu_seqlens_q[b]..cu_seqlens_q[b+1]-1 (int32 [B+1]), its newest positions;
+    seqlens [B] int32 counts each sequence's chunk.  kv_ring = (k_ring, v_ring) each
+    [B, W, Hkv, 64] holding the positions before the chunks; the window is W.  With
+    append the chunks are written to the rings after the attention.  max_q_len is a
+    host-side bound (read back from the GPU when omitted).  Returns out [Tq, Hq, 64]
+    (and lse [Hq, Tq]).
+    """
+    dev = q.device
+    _check_tensor(q, "q", q.dtype, dev, 3)
+    dt = _dtype_code(q)
+    Tq, Hq, D = q.shape
+    kr, vr = _split_cache(kv_ring)
+    _check_tensor(kr, "k_ring", q.dtype, dev, 4)
+    _check_tensor(vr, "v_ring", q.dtype, dev, 4)
+    _need(kr.shape[3] == D and vr.shape == kr.shape, "rings must be [B, W, Hkv, D]")
+    B, W, Hkv = kr.shape[0], kr.shape[1], kr.shape[2]
+    _check_tensor(k_new, "k_new", q.dtype, dev, 3)
+    _check_tensor(v_new, "v_new", q.dtype, dev, 3)
+    _need(k_new.shape == (Tq, Hkv, D) and v_new.shape == k_new.shape, "k_new/v_new must be [Tq, Hkv, D]")
+    _check_tensor(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev, 1)
+    _check_tensor(seqlens, "seqlens", torch.int32, dev, 1)
+    _need(seqlens.shape[0] == B and cu_seqlens_q.shape[0] == B + 1,
+          "seqlens must have B entries and cu_seqlens_q B+1")
+    if max_q_len is None:
+        max_q_len = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if B else 0
+    sinks = _sinks_arg(sinks, Hq, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor(out, "out", q.dtype, dev, 3)
+        _need(out.shape == q.shape, "out must have q's shape")
+    lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev) if return_lse else None
+    _check(lib().gqa_attn_prefill_ring(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(cu_seqlens_q), _ptr(seqlens), _ptr(kr),
+                                       _ptr(vr), int(bool(append)), _ptr(sinks), _ptr(out), _ptr(lse), B, Tq,
+                                       int(max_q_len), W, Hq, Hkv, D, _scale(scale), dt, _stream(dev)))
     return (out, lse) if return_lse else out
 
 

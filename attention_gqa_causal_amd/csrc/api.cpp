@@ -501,6 +501,65 @@ int gqa_kv_ring_append(const void* k_new, const void* v_new, const int32_t* cu_s
   return e == hipSuccess ? ok() : hip_fail(e, "ring append launch");
 }
 
+int gqa_attn_prefill_ring(const void* q, const void* k_new, const void* v_new, const int32_t* cu_seqlens_q,
+                          const int32_t* seqlens, void* k_ring, void* v_ring, int append, const float* sinks,
+                          void* out, float* lse, int B, int Tq, int max_q_len, int W, int Hq, int Hkv, int D,
+                          float scale, int dtype, void* stream) {
+  int rc = check_common(Hq, Hkv, D, W, 0, scale, dtype);
+  if (rc) return rc;
+  if (W <= 0) return fail(GQA_ERR_INVALID_ARG, "ring size W=%d must be >= 1", W);
+  if (B < 0 || Tq < 0 || max_q_len < 0)
+    return fail(GQA_ERR_INVALID_ARG, "negative size (B=%d, Tq=%d, max_q_len=%d)", B, Tq, max_q_len);
+  if (B == 0 || Tq == 0 || max_q_len == 0) return ok();
+  if (!q || !k_new || !v_new || !k_ring || !v_ring || !out || !cu_seqlens_q || !seqlens)
+    return fail(GQA_ERR_INVALID_ARG, "q, k_new, v_new, k_ring, v_ring, cu_seqlens_q, seqlens and out must be non-NULL");
+  const int G = Hq / Hkv;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  SeqArgs seq{};
+  seq.cu_seqlens_q = cu_seqlens_q;
+  seq.seqlens_k = seqlens;
+  seq.lmax = W;
+  seq.q_rows = Tq;
+  const float sl2 = scale_log2_of(scale, D);
+  hipError_t e;
+  if (dtype == GQA_FP32) {
+    if ((long long)B * max_q_len * Hq > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "problem too large for the fp32 path");
+    Fp32Args a{};
+    a.q = (const float*)q; a.k = (const float*)k_ring; a.v = (const float*)v_ring;
+    a.k2 = (const float*)k_new; a.v2 = (const float*)v_new; a.sinks = sinks;
+    a.out = (float*)out; a.lse = lse; a.seq = seq;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = W; a.sink_tokens = 0; a.scale_log2 = sl2;
+    a.max_q_len = max_q_len; a.varlen_q = 1;
+    a.lse_sb = 0; a.lse_sh = Tq; a.lse_row0 = 1;
+    e = launch_fp32(a, KV_RING, st);
+    if (e != hipSuccess) return hip_fail(e, "ring prefill fp32 launch");
+  } else {
+    PrefillArgs a{};
+    a.q = (const __bf16*)q; a.k = (const __bf16*)k_ring; a.v = (const __bf16*)v_ring;
+    a.k2 = (const __bf16*)k_new; a.v2 = (const __bf16*)v_new; a.sinks = sinks;
+    a.out = (__bf16*)out; a.lse = lse; a.seq = seq;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.window = W; a.sink_tokens = 0; a.scale_log2 = sl2;
+    const long ntiles = (long)((max_q_len + 31) / 32) * G;
+    a.wg_per_seq = (int)((ntiles + prefill_ntiles_per_wg() - 1) / prefill_ntiles_per_wg());
+    a.skip_single = 0;
+    a.lse_sb = 0; a.lse_sh = Tq; a.lse_row0 = 1;
+    a.sort_seq = B <= 256 && env_int("GQA_VARLEN_SORT", 1) != 0;
+    if ((long long)B * Hkv * a.wg_per_seq > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
+    e = launch_prefill_bf16(a, KV_RING, true, st);
+    if (e != hipSuccess) return hip_fail(e, "ring prefill launch");
+  }
+  if (!append) return ok();
+  // the chunk joins its rings once every query has read them: same stream, next launch
+  RingAppendArgs r{};
+  r.k_new = (const char*)k_new; r.v_new = (const char*)v_new;
+  r.k_ring = (char*)k_ring; r.v_ring = (char*)v_ring;
+  r.cu_seqlens_q = cu_seqlens_q; r.seqlens = seqlens;
+  r.T = Tq; r.B = B; r.W = W;
+  r.row_bytes = Hkv * D * (dtype == GQA_BF16 ? 2 : 4);
+  e = launch_ring_append(r, st);
+  return e == hipSuccess ? ok() : hip_fail(e, "ring append launch");
+}
+
 int gqa_rope_append(const void* q, const void* k, const void* v, void* q_out, const int32_t* cu_seqlens_q,
                     const int32_t* seqlens, const float* inv_freq, float mscale, int pairing, void* k_cache,
                     void* v_cache, int cache_kind, int cache_len, const int32_t* block_table, int max_blocks,

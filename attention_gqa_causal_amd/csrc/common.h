@@ -21,6 +21,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -3.0e38f;  // finite floor for running maxima (avoids inf - inf)
 
 constexpr int kHeadDim = 64;
+constexpr int kMaxPosition = 1 << 30;  // history lengths of a chunk over a ring are clamped below this
 
 // ---------------------------------------------------------------------------
 // device-side metadata checks
@@ -76,7 +77,10 @@ static __device__ unsigned int g_debug_flags;  // one per translation unit
 enum KvMode : int {
   KV_BATCHED = 0,  // k [B, Lmax, Hkv, D]: row = b * Lmax + j
   KV_PAGED = 1,    // k [Nblk, bs, Hkv, D]: row = table[b][j >> log2bs] * bs + (j & (bs - 1))
-  KV_PACKED = 2    // k [Nrows, Hkv, D]: row = cu_seqlens_k[b] + j
+  KV_PACKED = 2,   // k [Nrows, Hkv, D]: row = cu_seqlens_k[b] + j
+  KV_RING = 3      // a chunk over a ring: positions j >= kv_len - q_len are the chunk's own
+                   // rows [Tq, Hkv, D] (row q_row0 + j - (kv_len - q_len)); older ones sit in
+                   // the ring [B, W, Hkv, D] of lmax = W slots (row b * W + j % W)
 };
 
 struct SeqArgs {
@@ -137,6 +141,7 @@ __device__ __forceinline__ SeqView seq_view(const SeqArgs& a, int b, bool varlen
     if (MODE == KV_BATCHED) L = min(L, a.lmax);
     if (MODE == KV_PAGED) L = min(L, min(a.lmax, a.max_blocks << a.log2_block));
     if (MODE == KV_PACKED) L = min(L, a.lmax);
+    if (MODE == KV_RING) L = min(L, kMaxPosition);
     L = max(L, 0);
     GQA_FLAG(L != L0, kDbgSeqlensK);
     s.kv_len = L;
@@ -147,6 +152,13 @@ __device__ __forceinline__ SeqView seq_view(const SeqArgs& a, int b, bool varlen
   GQA_FLAG(s.q_len > s.kv_len, kDbgQLen);
   if (s.q_len > s.kv_len) s.q_len = s.kv_len;
   return s;
+}
+
+// KV_RING: the row of key position j, >= 0 in the ring, or -1 - r for row r of the chunk.
+__device__ __forceinline__ int64_t ring_chunk_row(const SeqArgs& a, const SeqView& s, int j) {
+  const int j0 = s.kv_len - s.q_len;
+  if (j >= j0) return -1 - (s.q_row0 + (j - j0));
+  return (int64_t)s.b * a.lmax + j % a.lmax;
 }
 
 template <int MODE>

@@ -52,8 +52,8 @@ __global__ __launch_bounds__(64) void attn_fp32_kernel(Fp32Args a) {
     float x = -INFINITY;
     int64_t row = 0;
     if (live) {
-      row = kv_row<MODE>(a.seq, sv, j);
-      const float* kp = a.k + row * kv_stride + g * kHeadDim;
+      row = MODE == KV_RING ? ring_chunk_row(a.seq, sv, j) : kv_row<MODE>(a.seq, sv, j);
+      const float* kp = (row < 0 ? a.k2 + (-1 - row) * kv_stride : a.k + row * kv_stride) + g * kHeadDim;
       float dot = 0.f;
       for (int d = 0; d < kHeadDim; ++d) dot = __builtin_fmaf(qs[d], kp[d], dot);
       x = dot * a.scale_log2;
@@ -69,7 +69,11 @@ __global__ __launch_bounds__(64) void attn_fp32_kernel(Fp32Args a) {
     rows[lane] = row;
     __syncthreads();
     const int n = min(64, nv - v0);
-    for (int jj = 0; jj < n; ++jj) acc = __builtin_fmaf(ps[jj], a.v[rows[jj] * kv_stride + g * kHeadDim + lane], acc);
+    for (int jj = 0; jj < n; ++jj) {
+      const int64_t r = rows[jj];  // KV_RING: -1 - r is a row of the chunk
+      const float* vp = r < 0 ? a.v2 + (-1 - r) * kv_stride : a.v + r * kv_stride;
+      acc = __builtin_fmaf(ps[jj], vp[g * kHeadDim + lane], acc);
+    }
     __syncthreads();
   }
   const float inv = l_run > 0.f ? 1.f / l_run : (l_run == 0.f ? 0.f : l_run);
@@ -90,8 +94,12 @@ hipError_t launch_fp32(const Fp32Args& a, int kv_mode, hipStream_t s) {
     hipLaunchKernelGGL((attn_fp32_kernel<KV_BATCHED>), dim3((unsigned)grid), dim3(64), 0, s, a);
   else if (kv_mode == KV_PAGED)
     hipLaunchKernelGGL((attn_fp32_kernel<KV_PAGED>), dim3((unsigned)grid), dim3(64), 0, s, a);
-  else
+  else if (kv_mode == KV_PACKED)
     hipLaunchKernelGGL((attn_fp32_kernel<KV_PACKED>), dim3((unsigned)grid), dim3(64), 0, s, a);
+  else if (kv_mode == KV_RING)
+    hipLaunchKernelGGL((attn_fp32_kernel<KV_RING>), dim3((unsigned)grid), dim3(64), 0, s, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -9,8 +9,10 @@ namespace gqa {
 // (sequence, KV head, group of 8 tiles of 32 (position, head) query rows).
 struct PrefillArgs {
   const __bf16* q;
-  const __bf16* k;
+  const __bf16* k;   // KV_RING: the rings
   const __bf16* v;
+  const __bf16* k2;  // KV_RING: the chunk's own rows [Tq, Hkv, D]
+  const __bf16* v2;
   const float* sinks;
   __bf16* out;
   float* lse;
@@ -57,8 +59,10 @@ struct DecodeArgs {
 // fp32 I/O path: one wave per (query row, query head).
 struct Fp32Args {
   const float* q;
-  const float* k;
+  const float* k;   // KV_RING: the rings
   const float* v;
+  const float* k2;  // KV_RING: the chunk's own rows [Tq, Hkv, D]
+  const float* v2;
   const float* sinks;
   float* out;
   float* lse;

@@ -280,6 +280,8 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
   const int64_t kv_stride = (int64_t)a.Hkv * kHeadDim;
   const __bf16* kbase = a.k + g * kHeadDim;
   const __bf16* vbase = a.v + g * kHeadDim;
+  const __bf16* kbase2 = MODE == KV_RING ? a.k2 + g * kHeadDim : nullptr;
+  const __bf16* vbase2 = MODE == KV_RING ? a.v2 + g * kHeadDim : nullptr;
   const int dma_chunk = ((lane & 7) ^ kswz(lane >> 3)) * 8;  // logical chunk this lane's LDS slot holds
   auto fetch_blk = [&](int t, int (&blk)[2]) {
 #pragma unroll
@@ -313,17 +315,26 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
     for (int i = 0; i < 2; ++i) {
       const int j = min(tile_j0(t) + 16 * wave + 8 * i + (lane >> 3), hi);
       int64_t row;
+      const __bf16* kb = kbase;
+      const __bf16* vb = vbase;
       if (MODE == KV_PAGED) {
         const int bb = min(max(blk[i], 0), a.seq.num_blocks - 1);
         GQA_FLAG(bb != blk[i], kDbgBlockTable);
         row = ((int64_t)bb << a.seq.log2_block) + (j & ((1 << a.seq.log2_block) - 1));
+      } else if (MODE == KV_RING) {
+        row = ring_chunk_row(a.seq, sv, j);
+        if (row < 0) {  // the chunk's own row
+          row = -1 - row;
+          kb = kbase2;
+          vb = vbase2;
+        }
       } else {
         row = kv_row<MODE>(a.seq, sv, j);
       }
       const int64_t off = row * kv_stride + dma_chunk;
       const int lofs = (16 * wave + 8 * i) * RS;  // wave-uniform slice of 8 rows
-      dma16((const void*)(kbase + off), (lds_void*)(&Ks[buf][lofs]));
-      dma16((const void*)(vbase + off), (lds_void*)(&Vs[buf][lofs]));
+      dma16((const void*)(kb + off), (lds_void*)(&Ks[buf][lofs]));
+      dma16((const void*)(vb + off), (lds_void*)(&Vs[buf][lofs]));
     }
   };
 
@@ -613,6 +624,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int kv_mode, bool varlen_q,
     GQA_LAUNCH(KV_PAGED, true);
   else if (varlen_q && kv_mode == KV_PACKED)
     GQA_LAUNCH(KV_PACKED, true);
+  else if (varlen_q && kv_mode == KV_RING && !stk)
+    hipLaunchKernelGGL((prefill_bf16_kernel<KV_RING, true, false>), dim3(grid), dim3(NTHREADS), 0, s, a);
   else
     return hipErrorInvalidValue;
 #undef GQA_LAUNCH

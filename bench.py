@@ -10,7 +10,9 @@ already resident in HBM:
      (rotary encoding of the new token, KV append, attention) in one launch;
   3. ragged + paged        16 sequences, lengths U{128..8192}, 512-token
      prefill chunks and single-token decode steps, 16-token pages under a
-     permuted block table -- dense, then window 128;
+     permuted block table -- dense, then window 128; then the windowed layer
+     of the same batch over 128-slot rings (each chunk attends over its ring
+     plus its own rows, then joins the ring);
   4. ring cache of a windowed layer (128 slots per sequence): append of one
      new token per sequence (B64), then decode from the rings at position 8191
      for B64 and for B4096 (the B4096 rings hold as many bytes as the dense
@@ -545,6 +547,21 @@ def add_varlen(stages, gq, r, up, i32, f32, dev):
         stages[name] = dict(fn=(lambda W=W, ws=ws: gq.attn_varlen_paged(
             rq, (rk, rv), rbt, rcu, rsl, rs, window=W, max_q_len=r.max_q_len, max_kv_len=r.max_kv_len,
             workspace=ws)), flop=fl, bytes=by, exp=fl // (4 * D), bound="mfma" if W == 0 else "hbm")
+    # the windowed layer of the same batch with a 128-slot ring per sequence instead of pages: each chunk
+    # (or decode row) attends over its ring plus its own rows, then joins the ring
+    import gqa_inputs as gi
+    W = 128
+    Tq = r.q.shape[0]
+    kr = up(gi.make_tensor(69, gi.T_K, (nseq, W, Hkv, D), 1.0, "bf16"))
+    vr = up(gi.make_tensor(69, gi.T_V, (nseq, W, Hkv, D), 1.0, "bf16"))
+    kn = up(gi.make_tensor(70, gi.T_K, (Tq, Hkv, D), 1.0, "bf16"))
+    vn = up(gi.make_tensor(70, gi.T_V, (Tq, Hkv, D), 1.0, "bf16"))
+    rout = torch.empty_like(rq)
+    fl, by = varlen_work(r.seqlens_k, r.q_lens, Hq, Hkv, D, W)
+    by += 2 * 2 * sum(min(int(n), W) for n in r.q_lens) * Hkv * D  # the append: rows written to the rings
+    stages["varlen_ring_swa128"] = dict(
+        fn=(lambda: gq.attn_prefill_ring(rq, kn, vn, rcu, rsl, (kr, vr), rs, max_q_len=r.max_q_len, out=rout)),
+        flop=fl, bytes=by, exp=fl // (4 * D), bound="hbm")
 
 
 def add_ring(stages, gq, up, i32, f32, dev):
@@ -844,8 +861,8 @@ def main():
         "config": {
             "workload": "layer-shaped prefill B1 S4096 Hq64 Hkv8 D64 bf16, dense layer then 128-token sliding-window "
                         "layer (value); each step also runs batched decode B64 cache 8192 (dense, window 128) and "
-                        "ragged+paged 16 sequences (dense, window 128), and a windowed layer's 128-slot ring cache (append B64; "
-                        "decode B64 and B4096), the rotary encoding + KV append of the prefill rows and of a decode step, "
+                        "ragged+paged 16 sequences (dense, window 128; the windowed layer also over 128-slot rings), and a "
+                        "windowed layer's 128-slot ring cache (append B64; decode B64 and B4096), the rotary encoding + KV append of the prefill rows and of a decode step, "
                         "the backward of the layer-shaped prefill (dense, window 128), and the long-context prefill "
                         "S32768 and decode B8 x 131072 (dense, window 128)",
             "global_batch": 1,

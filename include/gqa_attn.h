@@ -266,6 +266,45 @@ int gqa_attn_decode_ring(const void* q, const void* k_ring, const void* v_ring,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Chunked prefill of a sliding-window layer over its ring: a chunk of new
+ * tokens attends over the positions its ring still holds plus its own rows,
+ * and is appended to the ring afterwards.  «GPT-OSS vs Qwen3», section
+ * "Utilisation de Sliding Window Attention": the layer sees the last W tokens
+ * only.  A query at position p of a chunk starting at position L0 sees
+ * positions p - W + 1 .. p, none older than L0 - W + 1: before the chunk is
+ * written the ring holds all of those below L0, and the chunk the rest, so a
+ * chunk of any length (shorter than, equal to or longer than W) needs nothing
+ * the ring has lost.  Appending first would overwrite slots the chunk's first
+ * queries still read.
+ *   q [Tq, Hq, D], k_new, v_new [Tq, Hkv, D]: the chunks' rows (rotated, as
+ *     every attention input); sequence b owns rows cu_seqlens_q[b] ..
+ *     cu_seqlens_q[b+1]-1 (cu_seqlens_q [B+1] int32, device, non-decreasing,
+ *     cu_seqlens_q[B] == Tq), its newest q_len positions: row t at position
+ *     seqlens[b] - q_len + t.  A chunk of one row is a decode step; q_len 0
+ *     leaves the sequence alone.
+ *   seqlens [B] int32 (device): positions of sequence b including its chunk
+ *     (clamped to [q_len, 2^30]: GQA_DBG_SEQLENS_K / GQA_DBG_Q_LEN).
+ *   k_ring, v_ring [B, W, Hkv, D]: before the call, the positions before the
+ *     chunk (the last min(L0, W) of 0 .. L0-1, position p in slot p % W, as
+ *     gqa_kv_ring_append leaves them); slots never written are not read.
+ *   append: nonzero: after the attention the chunk's rows are written to the
+ *     rings (gqa_kv_ring_append, on the same stream, so after every read);
+ *     0: the rings are left unchanged.
+ *   sinks [Hq] fp32 or NULL, out [Tq, Hq, D], lse [Hq, Tq] fp32 (optional),
+ *     scale: as gqa_attn_varlen_paged.  The window is W; there are no sink
+ *     tokens (a ring does not hold them).
+ *   max_q_len (host): upper bound of any q_len (sizes the grid; rows of a
+ *     longer chunk past it are not computed).
+ * bf16 or fp32.  No workspace.
+ */
+int gqa_attn_prefill_ring(const void* q, const void* k_new, const void* v_new,
+                          const int32_t* cu_seqlens_q, const int32_t* seqlens,
+                          void* k_ring, void* v_ring, int append,
+                          const float* sinks, void* out, float* lse,
+                          int B, int Tq, int max_q_len, int W, int Hq, int Hkv, int D,
+                          float scale, int dtype, void* stream);
+
+/*
  * Rotary position encoding of new tokens fused with their KV-cache append.
  *
  * «GPT-OSS-20B : Architecture MoE & Résumé du Model Card», §3.4 "Encodage de

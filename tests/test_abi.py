@@ -34,7 +34,7 @@ def test_library_loads(L):
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -206,6 +206,38 @@ def ring_decode(L, B=2, W=128, Hq=64, Hkv=8, D=64, scale=0.0, dt=0, q=DUMMY, seq
 ])
 def test_ring_decode_rejects(L, kw, code):
     assert ring_decode(L, **kw) == code
+
+
+def ring_prefill(L, B=2, Tq=4, max_q_len=2, W=128, Hq=64, Hkv=8, D=64, scale=0.0, dt=0, q=DUMMY, kn=DUMMY,
+                 cu=DUMMY, seqlens=DUMMY, kr=DUMMY, out=DUMMY, append=1):
+    return L.gqa_attn_prefill_ring(q, kn, DUMMY, cu, seqlens, kr, DUMMY, append, None, out, None, B, Tq, max_q_len,
+                                   W, Hq, Hkv, D, scale, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=0), -1),
+    (dict(W=-3), -1),
+    (dict(D=128), -2),
+    (dict(dt=5), -2),
+    (dict(Hq=12), -2),
+    (dict(scale=float("nan")), -1),
+    (dict(B=-1), -1),
+    (dict(max_q_len=-1), -1),
+    (dict(cu=None), -1),
+    (dict(seqlens=None), -1),
+    (dict(kn=None), -1),
+    (dict(kr=None), -1),
+    (dict(out=None), -1),
+])
+def test_ring_prefill_rejects(L, kw, code):
+    assert ring_prefill(L, **kw) == code
+    assert L.gqa_attn_last_error() != b""
+
+
+def test_ring_prefill_empty_is_ok(L):
+    # nothing to do: no pointer is looked at, no launch
+    for kw in (dict(B=0), dict(Tq=0), dict(max_q_len=0)):
+        assert ring_prefill(L, q=None, kn=None, cu=None, seqlens=None, kr=None, out=None, **kw) == 0
 
 
 def test_ring_decode_workspace(L):
