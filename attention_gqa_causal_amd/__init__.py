@@ -33,6 +33,7 @@ import torch
 
 __all__ = [
     "attn_prefill",
+    "attn_prefill_rope",
     "attn_decode",
     "attn_varlen_paged",
     "kv_ring_append",
@@ -89,6 +90,7 @@ _SIGNATURES = {
     "gqa_attn_last_error": (ctypes.c_char_p, []),
     "gqa_attn_debug_flags": (_I, [ctypes.POINTER(ctypes.c_uint), _I]),
     "gqa_attn_prefill": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "gqa_attn_prefill_rope": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _F, _I, _I, _P]),
     "gqa_attn_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "gqa_attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "gqa_attn_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
@@ -235,6 +237,39 @@ def attn_prefill(q, k, v, sinks=None, window: int = 0, scale=None, return_lse: b
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev) if return_lse else None
     _check(lib().gqa_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(out), _ptr(lse),
                                   B, S, Hq, Hkv, D, int(window), int(sink_tokens), _scale(scale), dt, _stream(dev)))
+    return (out, lse) if return_lse else out
+
+
+def attn_prefill_rope(q, k, v, sinks=None, window: int = 0, scale=None, inv_freq=None, mscale: float = 1.0,
+                      pairing=0, return_lse: bool = False, out=None, sink_tokens: int = 0):
+    """Prefill whose queries arrive unrotated: the kernel rotates each query row at its
+    position as it loads it (the rotary append's angles and rotation, bit for bit).
+
+    q [B, S, Hq, 64] unrotated, k [B, S, Hkv, 64] already rotated, v [B, S, Hkv, 64]
+    (bf16); inv_freq [32] fp32 or None (the default table); pairing 0: (2i, 2i+1),
+    1: (i, i + 32).  Returns out (and lse) as ``attn_prefill``.
+    """
+    dev = q.device
+    _check_tensor(q, "q", q.dtype, dev, 4)
+    dt = _dtype_code(q)
+    B, S, Hq, D = q.shape
+    _check_tensor(k, "k", q.dtype, dev, 4)
+    _check_tensor(v, "v", q.dtype, dev, 4)
+    _need(k.shape[:2] == (B, S) and k.shape[3] == D and v.shape == k.shape, "k/v must be [B, S, Hkv, D] matching q")
+    Hkv = k.shape[2]
+    if inv_freq is not None:
+        _check_tensor(inv_freq, "inv_freq", torch.float32, dev, 1)
+        _need(inv_freq.shape[0] == D // 2, "inv_freq must have D/2 entries")
+    sinks = _sinks_arg(sinks, Hq, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor(out, "out", q.dtype, dev, 4)
+        _need(out.shape == q.shape, "out must match q")
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev) if return_lse else None
+    _check(lib().gqa_attn_prefill_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(out), _ptr(lse), B, S, Hq, Hkv,
+                                       D, int(window), int(sink_tokens), _scale(scale), _ptr(inv_freq),
+                                       float(mscale), int(pairing), dt, _stream(dev)))
     return (out, lse) if return_lse else out
 
 
@@ -582,19 +617,27 @@ def rope_append(q, k, v, seqlens, kv_cache, inv_freq=None, q_out=None, cu_seqlen
     without cu_seqlens_q, T == B (one row per sequence).  kv_cache = (k_cache, v_cache):
     contiguous [B, L, Hkv, 64]; paged [num_blocks, block_size, Hkv, 64] with block_table
     [B, max_blocks]; or, with ring=True, rings [B, W, Hkv, 64].  Returns q_out [T, Hq, 64]
-    (pass q_out=q to rotate in place).
+    (pass q_out=q to rotate in place).  q=None: keys only (for attn_prefill_rope, which
+    rotates its queries itself); returns None.
     """
-    dev = q.device
-    dt = _dtype_code(q)
-    _check_tensor(q, "q", q.dtype, dev, 3)
-    T, Hq, D = q.shape
-    _check_tensor(k, "k", q.dtype, dev, 3)
-    _check_tensor(v, "v", q.dtype, dev, 3)
-    _need(k.shape[0] == T and k.shape[2] == D and v.shape == k.shape, "k/v must be [T, Hkv, D]")
+    dev = k.device
+    dt = _dtype_code(k)
+    _check_tensor(k, "k", k.dtype, dev, 3)
+    _check_tensor(v, "v", k.dtype, dev, 3)
+    T, Hkv, D = k.shape
+    _need(v.shape == k.shape, "k/v must be [T, Hkv, D]")
+    if q is None:
+        _need(q_out is None, "q_out needs q")
+        Hq = 1
+    else:
+        _check_tensor(q, "q", k.dtype, dev, 3)
+        _need(q.shape[0] == T and q.shape[2] == D, "q must be [T, Hq, D]")
+        Hq = q.shape[1]
+    q_dtype = k.dtype
     Hkv = k.shape[1]
     kc, vc = _split_cache(kv_cache)
-    _check_tensor(kc, "k_cache", q.dtype, dev, 4)
-    _check_tensor(vc, "v_cache", q.dtype, dev, 4)
+    _check_tensor(kc, "k_cache", q_dtype, dev, 4)
+    _check_tensor(vc, "v_cache", q_dtype, dev, 4)
     _need(vc.shape == kc.shape and kc.shape[2] == Hkv and kc.shape[3] == D, "caches must be [.., .., Hkv, D]")
     _check_tensor(seqlens, "seqlens", torch.int32, dev, 1)
     B = seqlens.shape[0]
@@ -604,10 +647,12 @@ def rope_append(q, k, v, seqlens, kv_cache, inv_freq=None, q_out=None, cu_seqlen
     if inv_freq is not None:  # None: the library's default table θ_i = 10000^(-2i/D)
         _check_tensor(inv_freq, "inv_freq", torch.float32, dev, 1)
         _need(inv_freq.shape[0] == D // 2, "inv_freq must have D/2 entries")
-    if q_out is None:
+    if q is None:
+        pass
+    elif q_out is None:
         q_out = torch.empty_like(q)
     else:
-        _check_tensor(q_out, "q_out", q.dtype, dev, 3)
+        _check_tensor(q_out, "q_out", q_dtype, dev, 3)
         _need(q_out.shape == q.shape, "q_out must match q")
     if block_table is not None:
         _check_tensor(block_table, "block_table", torch.int32, dev, 2)

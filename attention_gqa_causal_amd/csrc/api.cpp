@@ -189,11 +189,18 @@ const char* gqa_attn_status_string(int status) {
 
 const char* gqa_attn_last_error(void) { return g_err; }
 
-int gqa_attn_prefill(const void* q, const void* k, const void* v, const float* sinks, void* out, float* lse,
-                     int B, int S, int Hq, int Hkv, int D, int window, int sink_tokens, float scale, int dtype,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Whole-sequence prefill; rope != 0: the queries arrive unrotated and the
+// kernel rotates them (1: pairs (2i, 2i+1), 2: pairs (i, i + D/2)).
+int prefill_call(const void* q, const void* k, const void* v, const float* sinks, void* out, float* lse, int B,
+                 int S, int Hq, int Hkv, int D, int window, int sink_tokens, float scale, int dtype, int rope,
+                 const float* inv_freq, float mscale, void* stream) {
   int rc = check_common(Hq, Hkv, D, window, sink_tokens, scale, dtype);
   if (rc) return rc;
+  if (rope && dtype != GQA_BF16) return fail(GQA_ERR_UNSUPPORTED, "the prefill with rotary encoding is bf16 only");
   if (B < 0 || S < 0) return fail(GQA_ERR_INVALID_ARG, "negative size (B=%d, S=%d)", B, S);
   if (B == 0 || S == 0) return ok();
   if (!q || !k || !v || !out) return fail(GQA_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
@@ -227,16 +234,31 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, const float* s
   a.skip_single = 0;
   a.lse_sb = (int64_t)Hq * S; a.lse_sh = S; a.lse_row0 = 0;
   if ((long long)B * Hkv * a.wg_per_seq > 0x7fffffffLL) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
-  // Causal layers with two to four tile groups per slot (2 workgroups per CU)
-  // pair a heavy and a light group per workgroup; with more groups the
-  // dispatch order balances by itself, and windowed layers give every group
-  // about the same work.
-  const bool dense_like = window == 0 || window >= S;
-  const long long groups = (long long)B * Hkv * a.wg_per_seq;
-  a.paired = dense_like && sink_tokens == 0 && groups >= 4LL * num_cus() && groups < 8LL * num_cus() &&
-             env_int("GQA_PREFILL_PAIRED", 1);
+  a.rope = rope;
+  a.inv_freq = inv_freq;
+  a.rope_mscale = mscale;
   hipError_t e = launch_prefill_bf16(a, KV_BATCHED, false, st);
   return e == hipSuccess ? ok() : hip_fail(e, "prefill bf16 launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_attn_prefill(const void* q, const void* k, const void* v, const float* sinks, void* out, float* lse,
+                     int B, int S, int Hq, int Hkv, int D, int window, int sink_tokens, float scale, int dtype,
+                     void* stream) {
+  return prefill_call(q, k, v, sinks, out, lse, B, S, Hq, Hkv, D, window, sink_tokens, scale, dtype, 0, nullptr,
+                      1.f, stream);
+}
+
+int gqa_attn_prefill_rope(const void* q, const void* k, const void* v, const float* sinks, void* out, float* lse,
+                          int B, int S, int Hq, int Hkv, int D, int window, int sink_tokens, float scale,
+                          const float* inv_freq, float mscale, int pairing, int dtype, void* stream) {
+  if (pairing != 0 && pairing != 1) return fail(GQA_ERR_INVALID_ARG, "pairing %d is not 0 or 1", pairing);
+  if (std::isnan(mscale) || std::isinf(mscale)) return fail(GQA_ERR_INVALID_ARG, "mscale must be finite");
+  return prefill_call(q, k, v, sinks, out, lse, B, S, Hq, Hkv, D, window, sink_tokens, scale, dtype, pairing + 1,
+                      inv_freq, mscale, stream);
 }
 
 size_t gqa_attn_decode_workspace_size(int B, int Lmax, int Hq, int Hkv, int D, int window, int sink_tokens,
@@ -584,9 +606,11 @@ int gqa_rope_append(const void* q, const void* k, const void* v, void* q_out, co
   } else {
     return fail(GQA_ERR_INVALID_ARG, "cache_kind %d is not 0 (contiguous), 1 (paged) or 2 (ring)", cache_kind);
   }
+  if ((q == nullptr) != (q_out == nullptr))
+    return fail(GQA_ERR_INVALID_ARG, "q and q_out are both given or both NULL (keys only)");
   if (B == 0 || T == 0) return ok();
-  if (!q || !k || !v || !q_out || !seqlens || !k_cache || !v_cache)
-    return fail(GQA_ERR_INVALID_ARG, "q, k, v, q_out, seqlens, k_cache and v_cache must be non-NULL");
+  if (!k || !v || !seqlens || !k_cache || !v_cache)
+    return fail(GQA_ERR_INVALID_ARG, "k, v, seqlens, k_cache and v_cache must be non-NULL");
   RopeAppendArgs a{};
   a.q = q; a.k = k; a.v = v; a.q_out = q_out; a.k_cache = k_cache; a.v_cache = v_cache;
   a.inv_freq = inv_freq; a.cu_seqlens_q = cu_seqlens_q; a.seqlens = seqlens; a.block_table = block_table;

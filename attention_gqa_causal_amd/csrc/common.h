@@ -215,8 +215,16 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // The default frequency θ_i = 10000^(-2i/d), formed in fp64 and rounded once to
 // fp32 (for d = 64 every θ_i lies at least 3e-10 of its size away from an fp32
 // rounding boundary, far beyond the fp64 error, so this is the correctly
-// rounded fp32 value).
-__device__ __forceinline__ float rope_default_freq(int i) { return (float)pow(10000.0, -2.0 * i / kHeadDim); }
+// rounded fp32 value).  The arguments of every power are constants, so the
+// compiler forms the 32 values once, at build time, and a lane selects its own
+// (a chain of selects instead of an fp64 power per lane).
+__device__ __forceinline__ float rope_default_freq(int i) {
+  float f = 0.f;
+#pragma unroll
+  for (int j = 0; j < kHeadDim / 2; ++j)
+    if (i == j) f = (float)__builtin_pow(10000.0, -2.0 * j / kHeadDim);
+  return f;
+}
 
 // cos and sin (times mscale) of the angle p·f: the angle is formed in fp64 as a
 // number of turns (the product of an integer position and an fp32 frequency is

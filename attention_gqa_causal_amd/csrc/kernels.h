@@ -26,8 +26,10 @@ struct PrefillArgs {
   int64_t lse_sb;    // lse index = b*lse_sb + h*lse_sh + t (+ q_row0 when lse_row0)
   int64_t lse_sh;
   int lse_row0;
-  int paired;        // each workgroup runs a heavy and a light tile group in turn (batched causal prefill)
   int sort_seq;      // ragged batches (B <= 256): dispatch the sequences with the most work first
+  int rope;          // queries arrive unrotated: 0 no, 1 pairs (2i, 2i+1), 2 pairs (i, i + D/2)
+  const float* inv_freq;  // rope: [D/2] or NULL (the default table)
+  float rope_mscale;
 };
 
 // Decode-style attention: one query token per sequence, KV split over

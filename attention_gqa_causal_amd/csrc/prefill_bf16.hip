@@ -168,19 +168,71 @@ __device__ __forceinline__ float refit_half(f32x16& s, bf16x8 (&pb)[2], float& m
   return exp_half(s, pb, m, c);
 }
 
+// Rotary encoding of queries that arrive unrotated, applied to the Q operands
+// in registers.  Lane (lr, lg) holds row lr of an N-tile, elements
+// d = 16k + 8lg + e of qb[k]: with pairs (2j, 2j+1) the four pairs of qb[k] are
+// j = 8k + 4lg + e/2; with pairs (j, j + 32) element e of qb[k] (k < 2) pairs
+// with element e of qb[k + 2], j = 16k + 8lg + e.  So a lane needs the angles of
+// 16 frequencies at its row's position.  Angles and rotation are the helpers the
+// rotary append uses, so the operands equal, bit for bit, what it writes.
+template <int PAIRING>
+__device__ __forceinline__ int rope_pair_index(int u, int lg) {
+  return PAIRING == 0 ? 8 * (u >> 2) + 4 * lg + (u & 3) : 16 * (u >> 3) + 8 * lg + (u & 7);
+}
+
+// The lane's 16 frequencies: for each u the two candidates (lg = 0, 1) are the
+// same for the whole wave, so they come from scalar loads of the table (or are
+// the default table's constants) and the lane picks one; nothing here waits on
+// the vector loads in flight.
+typedef const float __attribute__((address_space(4))) const_f32;  // read through the scalar cache
+
+template <int PAIRING>
+__device__ __forceinline__ void rope_freqs(const PrefillArgs& a, int lg, float (&f)[16]) {
+  const const_f32* tab = (const const_f32*)a.inv_freq;
+  if (tab) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      float f0 = tab[rope_pair_index<PAIRING>(u, 0)], f1 = tab[rope_pair_index<PAIRING>(u, 1)];
+      asm("" : "+s"(f0), "+s"(f1));  // two scalar values, then the lane's pick (not one load per lane)
+      f[u] = lg ? f1 : f0;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      f[u] = lg ? rope_default_freq(rope_pair_index<PAIRING>(u, 1)) : rope_default_freq(rope_pair_index<PAIRING>(u, 0));
+  }
+}
+
+template <int PAIRING>
+__device__ __forceinline__ void rope_angles(const PrefillArgs& a, const float (&f)[16], int p, float (&cs)[16],
+                                            float (&sn)[16]) {
+#pragma unroll
+  for (int u = 0; u < 16; ++u) rope_cos_sin(p, f[u], a.rope_mscale, cs[u], sn[u]);
+}
+
+template <int PAIRING>
+__device__ __forceinline__ void rope_rotate_q(bf16x8 (&q)[4], const float (&cs)[16], const float (&sn)[16]) {
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int k = PAIRING == 0 ? u >> 2 : u >> 3;
+    const int ea = PAIRING == 0 ? 2 * (u & 3) : u & 7;
+    const int kb = PAIRING == 0 ? k : k + 2;
+    const int eb = PAIRING == 0 ? ea + 1 : ea;
+    float ra, rb;
+    rope_rotate((float)q[k][ea], (float)q[kb][eb], cs[u], sn[u], ra, rb);
+    q[k][ea] = (__bf16)ra;
+    q[kb][eb] = (__bf16)rb;
+  }
+}
+
 // One job: the tile group x of the dispatch order (see below) of one
 // (sequence, KV head).  STK: the layer keeps start-of-sequence sink tokens
 // visible past its window (a separate instantiation, so that other layers
 // carry none of its code).
-template <int MODE, bool VARLEN, bool STK, bool IN_LOOP = false>
+template <int MODE, bool VARLEN, bool STK, int ROPE = 0>
 __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, __bf16 (*Ks)[BK * RS],
                                             __bf16 (*Vs)[BK * RS], const int* order = nullptr) {
-
-  // In the paired kernel the thread index passes through an empty asm so that
-  // lane-derived values are formed inside each job: hoisted out of its job
-  // loop they would stay live across it (and be spilled).
-  int tid = threadIdx.x;
-  if (IN_LOOP) asm volatile("" : "+v"(tid));
+  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (lets per-wave values live in SGPRs)
   const int lr = lane & 31;  // row of the 32-wide MFMA tile this lane serves
@@ -253,6 +305,17 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
     const bool ok = nt_valid[i] && t < sv.q_len;
     const char* qt = reinterpret_cast<const char*>(a.q + ((sv.q_row0 + nt_t0[i]) * a.Hq + nt_hq[i]) * (int64_t)kHeadDim);
     const uint32_t qo = (uint32_t)(lr * a.Hq * kHeadDim + 8 * lg) * 2u;
+    if constexpr (ROPE != 0) {
+      // Unconditional loads: a row past the end reads the sequence's last row
+      // (its head is valid; its results are never stored).  Without the
+      // branches the compiler keeps each operand where its load puts it, so
+      // nothing waits for the loads before the rotation needs them.
+      const int ts = ok ? t : sv.q_len - 1;
+      const __bf16* qr = a.q + ((sv.q_row0 + ts) * a.Hq + nt_hq[i]) * (int64_t)kHeadDim + 8 * lg;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qb[i][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qr + 16 * k));
+      continue;
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       u32x4 v = {0u, 0u, 0u, 0u};
@@ -363,6 +426,16 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
       fetch_blk(1, blk0);
       if (n_tiles > 1) dma_tile(1, blk0, 1);
       fetch_blk(2, blk_next);
+    }
+    if constexpr (ROPE != 0) {
+      // the angles go while the loads fly; the rotation once Q has landed
+      float f[16], cs[16], sn[16];
+      rope_freqs<ROPE - 1>(a, lg, f);
+      rope_angles<ROPE - 1>(a, f, pos0[0] + lr, cs, sn);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      rope_rotate_q<ROPE - 1>(qb[0], cs, sn);
+      if (nt_t0[1] != nt_t0[0]) rope_angles<ROPE - 1>(a, f, pos0[1] + lr, cs, sn);
+      rope_rotate_q<ROPE - 1>(qb[1], cs, sn);
     }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
@@ -532,7 +605,7 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
   }
 }
 
-template <int MODE, bool VARLEN, bool STK>
+template <int MODE, bool VARLEN, bool STK, int ROPE = 0>
 __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 Ks[NBUF][BK * RS];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[NBUF][BK * RS];
@@ -567,36 +640,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
       order = seq_order;
     }
   }
-  prefill_job<MODE, VARLEN, STK>(a, blockIdx.x, Ks, Vs, order);  // one call site: inlined once
-}
-
-// Under the causal mask the tile groups of a sequence carry work in
-// proportion to their position.  When there are between two and four of them
-// per slot of the chip (2 workgroups per CU), the last ones to start run
-// alone at the end; then a workgroup takes two jobs in turn, the k-th heaviest
-// and the k-th lightest of its XCD's list, so every workgroup carries the same
-// work.  A kernel of its own, so that the one-job kernel keeps its registers.
-__global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_paired_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[NBUF][BK * RS];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[NBUF][BK * RS];
-  const int total = a.B * a.Hkv * a.wg_per_seq;
-  int x = blockIdx.x, j2;
-  if (((a.B * a.Hkv) & 7) == 0) {  // jobs of XCD c are c + 8m, m = 0 .. M-1, heaviest first
-    const int c = blockIdx.x & 7, m = blockIdx.x >> 3, M = total >> 3;
-    x = c + 8 * m;
-    j2 = c + 8 * (M - 1 - m);
-  } else {
-    j2 = total - 1 - blockIdx.x;
-  }
-  int x2 = j2 != x ? j2 : -1;  // the middle job of an odd list runs once
-  // one call site, so that the job is inlined once
-  for (;;) {
-    prefill_job<KV_BATCHED, false, false, true>(a, x, Ks, Vs);
-    if (x2 < 0) break;
-    __syncthreads();  // every wave is done with the LDS buffers
-    x = x2;
-    x2 = -1;
-  }
+  prefill_job<MODE, VARLEN, STK, ROPE>(a, blockIdx.x, Ks, Vs, order);  // one call site: inlined once
 }
 
 }  // namespace
@@ -604,15 +648,21 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_paired_kernel(Prefil
 int prefill_ntiles_per_wg() { return NT_WG; }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int kv_mode, bool varlen_q, hipStream_t s) {
-  int grid = a.B * a.Hkv * a.wg_per_seq;
+  const int grid = a.B * a.Hkv * a.wg_per_seq;
   if (grid <= 0) return hipSuccess;
-  if (a.paired) {
-    if (kv_mode != KV_BATCHED || varlen_q || (a.window > 0 && a.sink_tokens > 0)) return hipErrorInvalidValue;
-    grid = ((a.B * a.Hkv) & 7) == 0 ? 8 * ((grid / 8 + 1) / 2) : (grid + 1) / 2;
-    hipLaunchKernelGGL(prefill_bf16_paired_kernel, dim3(grid), dim3(NTHREADS), 0, s, a);
+  const bool stk = a.window > 0 && a.sink_tokens > 0;
+  if (a.rope) {  // queries rotated in the kernel: whole-sequence prefill only
+    if (kv_mode != KV_BATCHED || varlen_q) return hipErrorInvalidValue;
+#define GQA_ROPE_LAUNCH(R)                                                                                          \
+  do {                                                                                                              \
+    if (stk) hipLaunchKernelGGL((prefill_bf16_kernel<KV_BATCHED, false, true, R>), dim3(grid), dim3(NTHREADS), 0, s, a); \
+    else hipLaunchKernelGGL((prefill_bf16_kernel<KV_BATCHED, false, false, R>), dim3(grid), dim3(NTHREADS), 0, s, a);    \
+  } while (0)
+    if (a.rope == 1) GQA_ROPE_LAUNCH(1);
+    else GQA_ROPE_LAUNCH(2);
+#undef GQA_ROPE_LAUNCH
     return hipGetLastError();
   }
-  const bool stk = a.window > 0 && a.sink_tokens > 0;
 #define GQA_LAUNCH(M, V)                                                                               \
   do {                                                                                                 \
     if (stk) hipLaunchKernelGGL((prefill_bf16_kernel<M, V, true>), dim3(grid), dim3(NTHREADS), 0, s, a); \

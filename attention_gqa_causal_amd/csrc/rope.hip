@@ -153,10 +153,12 @@ __global__ __launch_bounds__(RP_THREADS) void rope_append_kernel(RopeAppendArgs 
     rope_cos_sin(p, a.inv_freq ? a.inv_freq[4 * c + j] : rope_default_freq(4 * c + j), a.mscale, cs[j], sn[j]);
 
   // heads hg, hg + 8, ... in batches of 8 per lane (64 heads: one batch)
-  const T* q = reinterpret_cast<const T*>(a.q) + row * a.Hq * kHeadDim;
-  T* qo = reinterpret_cast<T*>(a.q_out) + row * a.Hq * kHeadDim;
-  for (int h0 = hg; h0 < a.Hq; h0 += 64)
-    rotate_heads<T, PAIRING, 8>(qo, q, h0, (a.Hq - h0 + 7) / 8, c, cs, sn);
+  if (a.q) {  // NULL: keys only (the attention rotates its queries itself)
+    const T* q = reinterpret_cast<const T*>(a.q) + row * a.Hq * kHeadDim;
+    T* qo = reinterpret_cast<T*>(a.q_out) + row * a.Hq * kHeadDim;
+    for (int h0 = hg; h0 < a.Hq; h0 += 64)
+      rotate_heads<T, PAIRING, 8>(qo, q, h0, (a.Hq - h0 + 7) / 8, c, cs, sn);
+  }
 
   // destination row of this position in the cache (or none)
   int64_t dst = -1;

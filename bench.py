@@ -18,7 +18,9 @@ already resident in HBM:
      for B64 and for B4096 (the B4096 rings hold as many bytes as the dense
      B64 x 8192 cache);
   5. rotary encoding of new rows fused with their KV-cache append: the 4096
-     rows of the layer-shaped prefill, and a decode step of 64 sequences;
+     rows of the layer-shaped prefill (queries and keys, and keys only, for
+     the prefill that rotates its queries as it loads them: "prefill_rope_*"
+     in stage 1), and a decode step of 64 sequences;
   6. backward of the layer-shaped prefill (dq, dk, dv, dsinks from dL/dout,
      the forward's output and log-sum-exp), dense and window 128: algorithmic
      work 10*D*Hq per visible pair (the five matrix products S, dP, dV, dK, dQ);
@@ -185,8 +187,8 @@ def summarize_counters(fetch_dir, write_dir):
     f_scale = (f_copy * 1024.0) / COPY_BYTES  # counter bytes per true byte read
     w_scale = (w_copy * 1024.0) / COPY_BYTES
     res = {}
-    # the dense B1 S4096 prefill runs the paired kernel (a heavy and a light tile group per workgroup)
-    for kind, key, work in (("prefill", "prefill_bf16_paired_kernel", prefill_work(1, 4096, 64, 8, 64, 0)),
+    # the dense B1 S4096 prefill: one job per workgroup, batched keys, no sink tokens, queries already rotated
+    for kind, key, work in (("prefill", "prefill_bf16_kernel<0, false, false, 0>", prefill_work(1, 4096, 64, 8, 64, 0)),
                             ("decode", "decode_rows_kernel", decode_work([8192] * 64, 64, 8, 64, 0))):
         fk, wk = pick(fetch, key), pick(write, key)
         rd = fk * 1024.0 / f_scale
@@ -494,6 +496,12 @@ def add_prefill(stages, gq, p, up, f32, dev):
         fl, by = prefill_work(B, S, Hq, Hkv, D, W)
         stages[name] = dict(fn=(lambda W=W: gq.attn_prefill(pq, pk, pv, ps, window=W, out=pout)), flop=fl, bytes=by,
                             exp=fl // (4 * D), bound="mfma" if W == 0 else "hbm")
+    # the same layers with the queries arriving unrotated: the kernel rotates them as it loads them (with the
+    # keys-only rotary append below, this replaces the rotary append of all rows + the prefill)
+    for name, W in (("prefill_rope_dense", 0), ("prefill_rope_swa128", 128)):
+        fl, by = prefill_work(B, S, Hq, Hkv, D, W)
+        stages[name] = dict(fn=(lambda W=W: gq.attn_prefill_rope(pq, pk, pv, ps, window=W, out=pout)), flop=fl,
+                            bytes=by, exp=fl // (4 * D), bound="mfma" if W == 0 else "hbm")
     # windowed layer with 4 start-of-sequence sink tokens kept visible
     fl, by = prefill_work_sink_tokens(B, S, Hq, Hkv, D, 128, 4)
     stages["prefill_swa128_sink4"] = dict(
@@ -633,6 +641,10 @@ def add_rope(stages, gq, up, i32, dev):
     stages["rope_append_s4096"] = dict(
         fn=(lambda: gq.rope_append(q, k, v, sl, (kc, vc), q_out=qo, cu_seqlens_q=cu)),
         flop=0, bytes=by, bound="hbm")
+    # keys only (the prefill rotates its queries itself)
+    stages["rope_k_append_s4096"] = dict(
+        fn=(lambda: gq.rope_append(None, k, v, sl, (kc, vc), cu_seqlens_q=cu)),
+        flop=0, bytes=2 * 2 * 2 * S * Hkv * D, bound="hbm")
     # one decode step of 64 sequences
     B = 64
     qd = up(gi.make_tensor(8, gi.T_Q, (B, Hq, D), 1.0, "bf16"))
@@ -884,7 +896,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(pd["tflops"] / PEAK_BF16_TFLOPS, 4),
             "traffic": load_traffic("prefill"),
-            "kernel": "prefill_bf16_paired_kernel (dense, B1 S4096)",
+            "kernel": "prefill_bf16_kernel (dense, B1 S4096)",
         }
     if "decode_dense" in parts:
         dd = parts["decode_dense"]

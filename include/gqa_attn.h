@@ -138,6 +138,25 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, const float* s
                      int window, int sink_tokens, float scale, int dtype, void* stream);
 
 /*
+ * Prefill whose queries arrive unrotated: the kernel applies the rotary
+ * encoding of «GPT-OSS-20B : Architecture MoE & Résumé du Model Card» §3.4
+ * («GPT-OSS vs Qwen3», "Adoption de RoPE") to each query row as it loads it,
+ * at the row's position t, with the same angles and rotation as
+ * gqa_rope_append (inv_freq [D/2] fp32 device or NULL for the default table,
+ * mscale, pairing GQA_ROPE_INTERLEAVED or GQA_ROPE_HALVES).  The result
+ * equals, bit for bit, gqa_rope_append's q_out passed to gqa_attn_prefill;
+ * the rotated queries are not written out.  k must already be rotated
+ * (gqa_rope_append with q = q_out = NULL rotates and appends the keys alone).
+ * Other arguments, layouts and errors as gqa_attn_prefill; bf16 only
+ * (GQA_FP32: GQA_ERR_UNSUPPORTED).
+ */
+int gqa_attn_prefill_rope(const void* q, const void* k, const void* v, const float* sinks,
+                          void* out, float* lse,
+                          int B, int S, int Hq, int Hkv, int D,
+                          int window, int sink_tokens, float scale,
+                          const float* inv_freq, float mscale, int pairing, int dtype, void* stream);
+
+/*
  * Decode: one new query token per sequence against a contiguous KV cache.
  *   q [B, Hq, D]    k_cache, v_cache [B, Lmax, Hkv, D]    out [B, Hq, D]
  *   seqlens [B] int32 (device): cached positions of sequence b INCLUDING the
@@ -316,13 +335,15 @@ int gqa_attn_prefill_ring(const void* q, const void* k_new, const void* v_new,
  *   pairing: GQA_ROPE_INTERLEAVED pairs coordinates (2i, 2i+1);
  *            GQA_ROPE_HALVES pairs (i, i + D/2).
  *   inv_freq [D/2] fp32 (device), or NULL for the default table
- *     θ_i = 10000^(-2i/D) (formed by the kernel in fp64 and rounded once to
- *     fp32); a context-extension scheme (e.g. YaRN, whose parameters the
+ *     θ_i = 10000^(-2i/D) (formed in fp64 when the library is built and
+ *     rounded once to fp32: the correctly rounded values); a context-extension scheme (e.g. YaRN, whose parameters the
  *     pages do not give in full) passes its own table.
  * Rows and positions as for gqa_kv_ring_append: q [T, Hq, D], k, v [T, Hkv, D];
  * without cu_seqlens_q, T == B and row b is at position seqlens[b] - 1; with
  * cu_seqlens_q [B+1], sequence b's rows are its newest q_len positions.
- * Outputs: q_out [T, Hq, D] (may be q itself) holds the rotated queries; the
+ * Outputs: q_out [T, Hq, D] (may be q itself) holds the rotated queries (q and
+ * q_out both NULL: keys only, for an attention call that rotates its queries
+ * itself, gqa_attn_prefill_rope); the
  * rotated key row and the value row of position p are written to the cache:
  *   GQA_CACHE_CONTIGUOUS: k_cache, v_cache [B, cache_len, Hkv, D], row p
  *     (positions >= cache_len are not stored);

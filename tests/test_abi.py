@@ -34,7 +34,7 @@ def test_library_loads(L):
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -208,6 +208,40 @@ def test_ring_decode_rejects(L, kw, code):
     assert ring_decode(L, **kw) == code
 
 
+def prefill_rope(L, B=1, S=64, Hq=8, Hkv=2, D=64, window=0, st=0, scale=0.0, mscale=1.0, pairing=0, dt=0,
+                 q=DUMMY, out=DUMMY):
+    return L.gqa_attn_prefill_rope(q, DUMMY, DUMMY, None, out, None, B, S, Hq, Hkv, D, window, st, scale, None,
+                                   mscale, pairing, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=1), -2),             # bf16 only
+    (dict(pairing=2), -1),
+    (dict(mscale=float("inf")), -1),
+    (dict(D=128), -2),
+    (dict(Hq=6, Hkv=4), -2),
+    (dict(window=-1), -1),
+    (dict(q=None), -1),
+])
+def test_prefill_rope_rejects(L, kw, code):
+    assert prefill_rope(L, **kw) == code
+    assert L.gqa_attn_last_error() != b""
+
+
+def test_prefill_rope_empty_is_ok(L):
+    assert prefill_rope(L, B=0, q=None, out=None) == 0
+    assert prefill_rope(L, S=0, q=None, out=None) == 0
+
+
+def test_rope_append_keys_only_needs_both_null(L):
+    # q without q_out (or the reverse) is an error; both NULL is the keys-only form
+    rc = L.gqa_rope_append(DUMMY, DUMMY, DUMMY, None, None, DUMMY, None, 1.0, 0, DUMMY, DUMMY, 0, 16, None, 0, 0, 0,
+                           2, 2, 8, 2, 64, 0, None)
+    assert rc == -1
+    assert L.gqa_rope_append(None, DUMMY, DUMMY, None, None, DUMMY, None, 1.0, 0, DUMMY, DUMMY, 0, 16, None, 0, 0, 0,
+                             0, 0, 8, 2, 64, 0, None) == 0
+
+
 def ring_prefill(L, B=2, Tq=4, max_q_len=2, W=128, Hq=64, Hkv=8, D=64, scale=0.0, dt=0, q=DUMMY, kn=DUMMY,
                  cu=DUMMY, seqlens=DUMMY, kr=DUMMY, out=DUMMY, append=1):
     return L.gqa_attn_prefill_ring(q, kn, DUMMY, cu, seqlens, kr, DUMMY, append, None, out, None, B, Tq, max_q_len,
@@ -250,8 +284,8 @@ def test_ring_decode_workspace(L):
 
 
 def rope(L, B=4, T=4, Hq=64, Hkv=8, D=64, dt=0, cu=None, pairing=0, mscale=1.0, kind=0, cache_len=128,
-         table=None, maxblk=0, bs=0, nblk=0, seqlens=DUMMY, inv=DUMMY, q=DUMMY, kc=DUMMY):
-    return L.gqa_rope_append(q, DUMMY, DUMMY, DUMMY, cu, seqlens, inv, mscale, pairing, kc, DUMMY, kind, cache_len,
+         table=None, maxblk=0, bs=0, nblk=0, seqlens=DUMMY, inv=DUMMY, q=DUMMY, kc=DUMMY, q_out=DUMMY):
+    return L.gqa_rope_append(q, DUMMY, DUMMY, q_out, cu, seqlens, inv, mscale, pairing, kc, DUMMY, kind, cache_len,
                              table, maxblk, bs, nblk, B, T, Hq, Hkv, D, dt, None)
 
 
@@ -287,7 +321,8 @@ def test_rope_append_null_table_is_the_default(L):
 
 
 def test_rope_append_empty_is_ok(L):
-    assert rope(L, B=0, T=0, seqlens=None, inv=None, q=None, kc=None) == 0
+    assert rope(L, B=0, T=0, seqlens=None, inv=None, q=None, q_out=None, kc=None) == 0
+    assert rope(L, B=0, T=0, seqlens=None, inv=None, q=None, kc=None) == -1  # q_out without q
 
 
 def backward(L, B=1, S=16, Hq=64, Hkv=8, D=64, window=0, sink_tokens=0, scale=0.0, dt=0, q=DUMMY, lse=DUMMY,

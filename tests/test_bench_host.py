@@ -68,7 +68,7 @@ def test_summarize_units_on_synthetic_counters(tmp_path, monkeypatch):
             0.25 * 2e5 * 1024, "SQ_ACTIVE_INST_VALU": 0.5 * 2e5 * 256, "SQ_INSTS_VALU_TRANS_F32": 1000,
             "SQ_LDS_BANK_CONFLICT": 10, "SQ_LDS_IDX_ACTIVE": 110, "SQ_ACTIVE_INST_LDS": 0.1 * 2e5 * 256}
     calib = {k: 1.0 for k in base}
-    lib = "void gqa::(anonymous namespace)::prefill_bf16_paired_kernel(gqa::PrefillArgs)"
+    lib = "void gqa::(anonymous namespace)::prefill_bf16_kernel<0, false, false, 0>(gqa::PrefillArgs)"
     _write_counter_csv(d / "run_counter_collection.csv",
                        [(lib, 65536, 256, 100000, base),  # before the calibration copy: not counted
                         ("__amd_rocclr_copyBuffer", 131072, 256, 5000, calib)]
