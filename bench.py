@@ -393,7 +393,7 @@ def summarize_units(dirs):
     lines = ["# Execution-unit counters per stage", "",
              "Commands (repository root, one MI355X; one rocprofv3 run per stage, 3 calls each after a 256 MiB "
              "calibration copy):", "",
-             "    cd /tmp && export TMPDIR=/tmp",
+             "    R=$PWD; cd /tmp && export TMPDIR=/tmp",
              "    for s in " + " ".join(r["stage"] for r in rows) + "; do",
              f"      rocprofv3 --pmc {UNIT_COUNTERS} --output-format csv -d $R/gpurun_out/units_$s -o run -- \\",
              "        python3 $R/bench.py --counters --parts $s --manifest $R/gpurun_out/units_$s/stage.json",
