@@ -294,3 +294,92 @@ def test_varlen_length_above_max_kv_len(use):
     say(f"varlen lengths above max_kv_len: flags {flags}")
     assert flags & gq.GQA_DBG_SEQLENS_K
     assert torch.equal(o, o_ok) and torch.equal(lse, l_ok)
+
+
+def _ring_chunks(cfg=46):
+    """A ragged batch of chunks over 128-slot rings: fresh, partly filled and full rings."""
+    L0s, q_lens, W = np.array([0, 50, 500, 3000]), np.array([130, 78, 129, 1]), 128
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q = dev_tensor(gi.make_tensor(cfg, gi.T_Q, (T, 64, 64), 1.0, "bf16"), "cuda")
+    k = dev_tensor(gi.make_tensor(cfg, gi.T_K, (T, 8, 64), 1.0, "bf16"), "cuda")
+    v = dev_tensor(gi.make_tensor(cfg, gi.T_V, (T, 8, 64), 1.0, "bf16"), "cuda")
+    kr = dev_tensor(gi.make_tensor(cfg + 1, gi.T_K, (4, W, 8, 64), 1.0, "bf16"), "cuda")
+    vr = dev_tensor(gi.make_tensor(cfg + 1, gi.T_V, (4, W, 8, 64), 1.0, "bf16"), "cuda")
+    return q, k, v, kr, vr, cu, (L0s + q_lens).astype(np.int32), dev_f32(gi.make_sinks(cfg, 64), "cuda")
+
+
+def test_valid_calls_of_the_fused_entry_points_record_nothing(use):
+    """Chunked prefill over rings, the one-launch decode step (contiguous, paged, ring) and the
+    prefill that rotates its queries, on valid metadata: the debug build records no flag and
+    gives the release build's results (and cache contents) bit for bit."""
+    q, k, v, kr, vr, cu, sl, s = _ring_chunks()
+    p = gi.prefill_problem(47, 1, 700, 64, 8)
+    pq, pk, pv = dev_tensor(p.q, "cuda"), dev_tensor(p.k, "cuda"), dev_tensor(p.v, "cuda")
+    d = gi.decode_problem(48, 3, 400, 64, 8, seqlens=[1, 250, 400])
+    r = gi.varlen_problem(49, [40, 300], [1, 1], 64, 8, block_size=16, maxblk=32)
+    ring = gi.ring_problem(50, 3, 128, [5, 128, 9000])
+    nq = dev_tensor(gi.make_tensor(51, gi.T_Q, (3, 64, 64), 1.0, "bf16"), "cuda")
+    nk = dev_tensor(gi.make_tensor(51, gi.T_K, (3, 8, 64), 1.0, "bf16"), "cuda")
+    nv = dev_tensor(gi.make_tensor(51, gi.T_V, (3, 8, 64), 1.0, "bf16"), "cuda")
+    rq, rk, rv = (dev_tensor(gi.make_tensor(52, t, (2, h, 64), 1.0, "bf16"), "cuda")
+                  for t, h in ((gi.T_Q, 64), (gi.T_K, 8), (gi.T_V, 8)))
+
+    def calls():
+        outs = []
+        krc, vrc = kr.clone(), vr.clone()
+        outs += list(gq.attn_prefill_ring(q, k, v, dev_i32(cu, "cuda"), dev_i32(sl, "cuda"), (krc, vrc), s,
+                                          return_lse=True)) + [krc, vrc]
+        outs += list(gq.attn_prefill_rope(pq, pk, pv, s, window=128, pairing=1, return_lse=True))
+        kc, vc = dev_tensor(d.k, "cuda"), dev_tensor(d.v, "cuda")
+        outs += list(gq.attn_decode_step(nq, nk, nv, dev_i32(d.seqlens, "cuda"), (kc, vc), s, window=128,
+                                         return_lse=True)) + [kc, vc]
+        pkc, pvc = dev_tensor(r.k, "cuda"), dev_tensor(r.v, "cuda")
+        outs += list(gq.attn_decode_step(rq, rk, rv, dev_i32(r.seqlens_k, "cuda"), (pkc, pvc), s, window=0,
+                                         block_table=dev_i32(r.block_table, "cuda"), return_lse=True)) + [pkc, pvc]
+        rkc, rvc = dev_tensor(ring.k_ring, "cuda"), dev_tensor(ring.v_ring, "cuda")
+        outs += list(gq.attn_decode_step(nq, nk, nv, dev_i32(ring.seqlens, "cuda"), (rkc, rvc), s, ring=True,
+                                         return_lse=True)) + [rkc, rvc]
+        torch.cuda.synchronize()
+        return outs
+
+    use("debug")
+    say("fused entry points, valid metadata, debug build")
+    gq.debug_flags(reset=True)
+    got = calls()
+    flags = gq.debug_flags(reset=True)
+    say(f"fused entry points: flags {flags}")
+    assert flags == 0
+    use("release")
+    want = calls()
+    for i, (a, b) in enumerate(zip(got, want)):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b), i
+
+
+def test_ring_prefill_more_queries_than_positions(use):
+    """A chunk longer than its sequence's position count (seqlens below q_len) is metadata out
+    of range: recorded as GQA_DBG_Q_LEN, the writes stay inside the output, and the other
+    sequences get the rows of a call with all metadata valid."""
+    q, k, v, kr, vr, cu, sl, s = _ring_chunks()
+    bad = sl.copy()
+    bad[1] = 30  # 78 new rows but 30 positions
+    T = q.shape[0]
+    use("release")
+    ok = gq.attn_prefill_ring(q, k, v, dev_i32(cu, "cuda"), dev_i32(sl, "cuda"), (kr.clone(), vr.clone()), s,
+                              append=False)
+    for which in ("debug", "release"):
+        use(which)
+        say(f"ring prefill, seqlens below q_len, {which} build")
+        if which == "debug":
+            gq.debug_flags(reset=True)
+        big, out = guarded(T, 64, 64)
+        gq.attn_prefill_ring(q, k, v, dev_i32(cu, "cuda"), dev_i32(bad, "cuda"), (kr.clone(), vr.clone()), s,
+                             append=False, out=out)
+        torch.cuda.synchronize()
+        assert_guard_intact(big, T, f"ring prefill ({which})")
+        if which == "debug":
+            assert gq.debug_flags(reset=True) & gq.GQA_DBG_Q_LEN
+        for b in (0, 2, 3):
+            r0, r1 = int(cu[b]), int(cu[b + 1])
+            assert torch.equal(out[r0:r1].view(torch.int16), ok[r0:r1].view(torch.int16)), (which, b)
