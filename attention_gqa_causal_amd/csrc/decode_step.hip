@@ -16,21 +16,31 @@
 // KV head and the new key row, writes the key and value rows to the cache slot
 // of the new position (no other workgroup touches that slot), and attends over
 // the key range, taking the new position's row from its own LDS copy, so
-// nothing in the launch waits for another workgroup's write.  The key range
-// (the window, or the whole sequence on a dense layer with a short cache) is
-// staged through LDS in chunks of 128 keys; each half-wave owns one query
-// head (its rotated query in registers, four keys per lane, the online softmax
-// within the half-wave, two output columns per lane).  Scores and P V are
-// plain fp32 vector arithmetic: the step is bound by its K/V bytes and its
-// launch, not by arithmetic.
+// nothing in the launch waits for another workgroup's write.  The attention is
+// the decode kernels' matrix-core form: the 4 waves take interleaved 32-key
+// tiles of the key range (a window of 128 keys: one tile each), stage each
+// tile's K and V rows in their own LDS slice, compute S^T = K Q^T on
+// v_mfma_f32_16x16x32_bf16 (the query heads as the 16 columns) and
+// O^T += V^T P^T with V^T through the transposing LDS read, each with its own
+// online softmax; the 4 states are merged in LDS, where the sink enters.
 #include "kernels.h"
 
 namespace gqa {
 namespace {
 
-constexpr int ST_THREADS = 256;
-constexpr int ST_CHUNK = 128;  // keys staged in LDS at a time
-constexpr int ST_RS = 72;      // LDS row stride of a staged K/V row (bf16): 144 bytes spreads the rows' banks
+constexpr int ST_THREADS = 256;  // 4 waves
+constexpr int TK = 32;           // keys per wave tile
+constexpr int KSD = 72;          // LDS row stride (elements) of a wave's K tile [key][d]
+constexpr int VSD = 80;          // LDS row stride (elements) of a wave's V tile [key][d]
+constexpr int WAVE_LDS = TK * KSD + TK * VSD;  // elements per wave
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 template <int KIND>
 __device__ __forceinline__ int64_t step_row(const DecodeStepArgs& a, int b, int pos) {
@@ -44,32 +54,35 @@ __device__ __forceinline__ int64_t step_row(const DecodeStepArgs& a, int b, int 
 
 template <int KIND>
 __global__ __launch_bounds__(ST_THREADS) void decode_step_kernel(DecodeStepArgs a) {
-  __shared__ float q_s[kStepMaxG][kHeadDim];  // rotated queries (their bf16 values)
+  // per wave: K tile then V tile; after the key loop the same memory holds the merge buffers
+  __shared__ __attribute__((aligned(16))) __bf16 lds[4 * WAVE_LDS];
   __shared__ __attribute__((aligned(16))) __bf16 kn_s[kHeadDim];  // the new key row, rotated
   __shared__ __attribute__((aligned(16))) __bf16 vn_s[kHeadDim];  // the new value row
-  __shared__ __attribute__((aligned(16))) __bf16 k_s[ST_CHUNK * ST_RS];
-  __shared__ __attribute__((aligned(16))) __bf16 v_s[ST_CHUNK * ST_RS];
-  __shared__ __attribute__((aligned(16))) float p_s[kStepMaxG][ST_CHUNK];  // weights of the chunk
 
   const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int lc = lane & 15;  // head column (and key row of the K operand)
+  const int lq = lane >> 4;  // lane quarter
   const int b = blockIdx.x / a.Hkv;
   const int g = blockIdx.x % a.Hkv;
   const int G = a.G;
 
   // The new rows do not depend on the sequence length: they are requested
-  // first, beside it.  Thread t takes pair i = t % 32 of query head t / 32 of
-  // this KV head; threads 0..31 also pair t of the key, threads 64..127 one
-  // element of the value.
-  const int rh = t >> 5, ri = t & 31;
-  const int ia = a.pairing ? ri : 2 * ri, ib = a.pairing ? ri + kHeadDim / 2 : 2 * ri + 1;
-  const int64_t qo = ((int64_t)b * a.Hq + g * G + rh) * kHeadDim;
-  const int64_t ko = ((int64_t)b * a.Hkv + g) * kHeadDim;
-  float qa = 0.f, qb = 0.f, ka = 0.f, kb = 0.f;
-  __bf16 vv = (__bf16)0.f;
-  if (rh < G) {
-    qa = (float)a.q[qo + ia];
-    qb = (float)a.q[qo + ib];
+  // first, beside it.  Every wave loads the Q^T operand (head lc, d = 32 ks +
+  // 8 lq .. +7); threads 0..31 take pair t of the new key, threads 64..127 one
+  // element of the new value.
+  const int64_t qrow = ((int64_t)b * a.Hq + g * G + lc) * kHeadDim;
+  u32x4 qw[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+  if (lc < G) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) qw[ks] = *reinterpret_cast<const u32x4*>(a.q + qrow + 32 * ks + 8 * lq);
   }
+  const int ri = t & 31;
+  const int ia = a.pairing ? ri : 2 * ri, ib = a.pairing ? ri + kHeadDim / 2 : 2 * ri + 1;
+  const int64_t ko = ((int64_t)b * a.Hkv + g) * kHeadDim;
+  float ka = 0.f, kb = 0.f;
+  __bf16 vv = (__bf16)0.f;
   if (t < kHeadDim / 2) {
     ka = (float)a.k_new[ko + ia];
     kb = (float)a.k_new[ko + ib];
@@ -91,61 +104,76 @@ __global__ __launch_bounds__(ST_THREADS) void decode_step_kernel(DecodeStepArgs 
   const int lo = W > 0 ? max(0, L - W) : 0;
   const int ns = W > 0 ? min(a.sink_tokens, lo) : 0;
   const int nv = ns + (L - lo);
+  auto pos_of = [&](int v) { return v < ns ? v : lo + (v - ns); };
 
-  // The chunk's K and V rows go through registers: thread t moves 16-byte
-  // piece t % 8 of rows t / 8 + 32 r (r < 4).  The first chunk is requested
-  // before the rotation work, so its latency overlaps it; the new position's
-  // row is filled in from LDS once it is rotated.
-  static_assert(ST_CHUNK * 8 == 4 * ST_THREADS, "four 16-byte pieces of K and of V per thread and chunk");
+  // A wave's tile: load i brings key 8 i + lane / 8 of the tile, 16 bytes at
+  // d = 8 (lane % 8); rows past the range repeat its last key (masked below,
+  // always in bounds), the new position's row is not read (it comes from LDS).
+  // The first tile is requested before the rotation work, so its latency
+  // overlaps it.
+  const int piece = lane & 7;
   u32x4 kreg[4], vreg[4];
-  auto request = [&](int c0) {
+  auto request = [&](int v0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = (t >> 3) + 32 * r, piece = t & 7;
-      kreg[r] = u32x4{0u, 0u, 0u, 0u};
-      vreg[r] = u32x4{0u, 0u, 0u, 0u};
-      const int v = c0 + j;
-      const int pos = v < ns ? v : lo + (v - ns);
-      if (v < nv && pos != p) {
+    for (int i = 0; i < 4; ++i) {
+      const int pos = pos_of(min(v0 + 8 * i + (lane >> 3), nv - 1));
+      kreg[i] = u32x4{0u, 0u, 0u, 0u};
+      vreg[i] = u32x4{0u, 0u, 0u, 0u};
+      if (pos != p) {
         const int64_t off = (step_row<KIND>(a, b, pos) * a.Hkv + g) * kHeadDim + 8 * piece;
-        kreg[r] = *reinterpret_cast<const u32x4*>(a.k_cache + off);
-        vreg[r] = *reinterpret_cast<const u32x4*>(a.v_cache + off);
+        kreg[i] = *reinterpret_cast<const u32x4*>(a.k_cache + off);
+        vreg[i] = *reinterpret_cast<const u32x4*>(a.v_cache + off);
       }
     }
   };
-  auto stage = [&](int c0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = (t >> 3) + 32 * r, piece = t & 7;
-      const int v = c0 + j;
-      const int pos = v < ns ? v : lo + (v - ns);
-      u32x4 kw = kreg[r], vw = vreg[r];
-      if (v < nv && pos == p) {
-        kw = *reinterpret_cast<const u32x4*>(kn_s + 8 * piece);
-        vw = *reinterpret_cast<const u32x4*>(vn_s + 8 * piece);
-      }
-      *reinterpret_cast<u32x4*>(k_s + j * ST_RS + 8 * piece) = kw;
-      *reinterpret_cast<u32x4*>(v_s + j * ST_RS + 8 * piece) = vw;
-    }
-  };
-  request(0);
+  int v0 = wave * TK;
+  if (v0 < nv) request(v0);
 
-  // ---- rotate (every thread forms the cos and sin of its own pair's angle)
+  // ---- rotate: the lane's query operand (8 pairs of head lc) and, for threads
+  // 0..31, pair t of the new key; every thread forms the cos and sin it needs
+  bf16x8 qb[2];
   {
-    float cs, sn;
-    rope_cos_sin(p, a.inv_freq ? a.inv_freq[ri] : rope_default_freq(ri), a.mscale, cs, sn);
-    float ra, rb;
-    if (rh < G) {
-      rope_rotate(qa, qb, cs, sn, ra, rb);
-      const __bf16 ba = (__bf16)ra, bb = (__bf16)rb;
-      q_s[rh][ia] = (float)ba;
-      q_s[rh][ib] = (float)bb;
-      if (a.q_out) {
-        a.q_out[qo + ia] = ba;
-        a.q_out[qo + ib] = bb;
+    const float ms = a.mscale;
+    if (a.pairing == 0) {
+      // pairs (2i, 2i+1): element pairs (2e', 2e'+1) of qw[ks], i = 16 ks + 4 lq + e'
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * ks + 4 * lq + e;
+          float cs, sn, ra, rb;
+          rope_cos_sin(p, a.inv_freq ? a.inv_freq[i] : rope_default_freq(i), ms, cs, sn);
+          rope_rotate(bf16_lo(qw[ks][e]), bf16_hi(qw[ks][e]), cs, sn, ra, rb);
+          qw[ks][e] = pack_bf16x2(ra, rb);
+        }
       }
+    } else {
+      // pairs (i, i + 32): element e of qw[0] with element e of qw[1], i = 8 lq + e
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        float r0[2], r1[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int i = 8 * lq + 2 * e2 + h;
+          float cs, sn;
+          rope_cos_sin(p, a.inv_freq ? a.inv_freq[i] : rope_default_freq(i), ms, cs, sn);
+          const float xa = h ? bf16_hi(qw[0][e2]) : bf16_lo(qw[0][e2]);
+          const float xb = h ? bf16_hi(qw[1][e2]) : bf16_lo(qw[1][e2]);
+          rope_rotate(xa, xb, cs, sn, r0[h], r1[h]);
+        }
+        qw[0][e2] = pack_bf16x2(r0[0], r0[1]);
+        qw[1][e2] = pack_bf16x2(r1[0], r1[1]);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, qw[ks]);
+    if (a.q_out && wave == 0 && lc < G) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) *reinterpret_cast<u32x4*>(a.q_out + qrow + 32 * ks + 8 * lq) = qw[ks];
     }
     if (t < kHeadDim / 2) {
+      float cs, sn, ra, rb;
+      rope_cos_sin(p, a.inv_freq ? a.inv_freq[ri] : rope_default_freq(ri), ms, cs, sn);
       rope_rotate(ka, kb, cs, sn, ra, rb);
       kn_s[ia] = (__bf16)ra;
       kn_s[ib] = (__bf16)rb;
@@ -157,89 +185,150 @@ __global__ __launch_bounds__(ST_THREADS) void decode_step_kernel(DecodeStepArgs 
   // ---- append: the new key and value rows to the cache slot of position p (16-byte words)
   if (t < 16) {
     const int64_t row = step_row<KIND>(a, b, p);
-    const int piece = t & 7;
-    const u32x4 w = t < 8 ? *reinterpret_cast<const u32x4*>(kn_s + 8 * piece)
-                          : *reinterpret_cast<const u32x4*>(vn_s + 8 * piece);
-    __bf16* dst = (t < 8 ? a.k_cache : a.v_cache) + (row * a.Hkv + g) * kHeadDim + 8 * piece;
+    const u32x4 w = t < 8 ? *reinterpret_cast<const u32x4*>(kn_s + 8 * (t & 7))
+                          : *reinterpret_cast<const u32x4*>(vn_s + 8 * (t & 7));
+    __bf16* dst = (t < 8 ? a.k_cache : a.v_cache) + (row * a.Hkv + g) * kHeadDim + 8 * (t & 7);
     *reinterpret_cast<u32x4*>(dst) = w;
   }
 
+  // ---- attention over the wave's tiles
   const float c = a.scale_log2;
+  __bf16* Kw = lds + wave * WAVE_LDS;
+  __bf16* Vw = Kw + TK * KSD;
+  const int vofs = (4 * lq + ((lane & 15) >> 2)) * VSD + 4 * (lane & 3);
+  float m_run = kNegBig, l_run = 0.f;
+  f32x4 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (; v0 < nv; v0 += 4 * TK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = 8 * i + (lane >> 3);
+      const int pos = pos_of(min(v0 + key, nv - 1));
+      u32x4 kw = kreg[i], vw = vreg[i];
+      if (pos == p) {
+        kw = *reinterpret_cast<const u32x4*>(kn_s + 8 * piece);
+        vw = *reinterpret_cast<const u32x4*>(vn_s + 8 * piece);
+      }
+      *reinterpret_cast<u32x4*>(Kw + key * KSD + 8 * piece) = kw;
+      *reinterpret_cast<u32x4*>(Vw + key * VSD + 8 * piece) = vw;
+    }
+    wave_lds_sync();  // the tile is visible to every lane of the wave
+    if (v0 + 4 * TK < nv) request(v0 + 4 * TK);  // the wave's next tile flies during this one's math
 
-  // Half-wave hw = t / 32 owns query head hw of this KV head: its rotated
-  // query in registers, its running max and sum (log2 units, the sink as the
-  // starting reference: its own term is 1), two output columns per lane.
-  const int hh = t >> 5, jj = t & 31;
-  const bool live = hh < G;
-  float qr[kHeadDim];
+    // S^T: 2 blocks of 16 keys x 16 heads; A operand = K rows 16 kb + lc, d 32 ks + 8 lq
+    f32x4 sc[2];
 #pragma unroll
-  for (int e = 0; e < kHeadDim; ++e) qr[e] = live ? q_s[hh][e] : 0.f;
-  const float s2 = (a.sinks && live) ? a.sinks[g * G + hh] * kLog2e : -INFINITY;
-  float m_run = s2 == -INFINITY ? kNegBig : s2;
-  float l_run = s2 == -INFINITY ? 0.f : 1.f;
-  float o0 = 0.f, o1 = 0.f;  // output columns 2 jj, 2 jj + 1
-  for (int c0 = 0; c0 < nv; c0 += ST_CHUNK) {
-    const int nc = min(ST_CHUNK, nv - c0);
-    stage(c0);  // the chunk's rows (requested earlier) into LDS, the new position's from its LDS copy
-    if (c0 + ST_CHUNK < nv) request(c0 + ST_CHUNK);  // the next chunk flies during this one
-    __syncthreads();
-    // scores of keys jj + 32 i (i < 4): a half-wave reads 32 consecutive rows at once
-    float x[4];
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = jj + 32 * i;
-      float acc = 0.f;
-#pragma unroll
-      for (int d8 = 0; d8 < 8; ++d8) {
-        const u32x4 kw = *reinterpret_cast<const u32x4*>(k_s + j * ST_RS + 8 * d8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc = __builtin_fmaf(qr[8 * d8 + 2 * e], bf16_lo(kw[e]), acc);
-          acc = __builtin_fmaf(qr[8 * d8 + 2 * e + 1], bf16_hi(kw[e]), acc);
-        }
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(Kw + (16 * kb2 + lc) * KSD + 32 * ks + 8 * lq);
+        acc = mfma16(kop, qb[ks], acc);
       }
-      x[i] = (j < nc && live) ? acc * c : -INFINITY;
+      sc[kb2] = acc;
     }
-    // online softmax over the chunk, within the half-wave
-    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    // lane holds keys v0 + 16 kb + 4 lq + r of head lc
+    if (v0 + TK > nv) {
 #pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    const float m_new = fmaxf(m_run, mx);
-    float sum = 0.f;
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = fast_exp2(x[i] - m_new);
-      sum += x[i];
-      p_s[hh][jj + 32 * i] = x[i];
+        for (int r = 0; r < 4; ++r)
+          if (v0 + 16 * kb2 + 4 * lq + r >= nv) sc[kb2][r] = -INFINITY;
     }
+    float mx = -INFINITY;
 #pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
-    const float al = fast_exp2(m_run - m_new);
-    l_run = l_run * al + sum;
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kb2][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx * c);
+    const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
-    wave_lds_sync();  // the half-wave's weights are visible to its own lanes
-    // P V: columns 2 jj, 2 jj + 1 over the chunk's keys, 4 keys per step
-    o0 *= al;
-    o1 *= al;
-    for (int j = 0; j < nc; j += 4) {
-      const f32x4 pw = *reinterpret_cast<const f32x4*>(&p_s[hh][j]);
+    float rs = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t vw = *reinterpret_cast<const uint32_t*>(v_s + (j + i) * ST_RS + 2 * jj);
-        o0 = __builtin_fmaf(pw[i], bf16_lo(vw), o0);
-        o1 = __builtin_fmaf(pw[i], bf16_hi(vw), o1);
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pw = fast_exp2(__builtin_fmaf(sc[kb2][r], c, -m_new));
+        sc[kb2][r] = pw;
+        rs += pw;
       }
+    l_run = l_run * alpha + rs;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+    // O^T += V^T P^T over the tile's 32 keys: keys {4lq..4lq+3, 16+4lq..16+4lq+3};
+    // in lane group lq, lane j reads 4 d of key row 4lq + j/4; the hardware hands
+    // lane i the 4 keys at d = 16 dt + i
+    bf16x8 pbv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pbv[e] = (__bf16)sc[0][e];
+      pbv[4 + e] = (__bf16)sc[1][e];
     }
-    __syncthreads();  // every wave is done with the chunk before the next is staged
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const __bf16* base = Vw + vofs + 16 * dt;
+      const i16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
+      const i16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * VSD));
+      const i16x8 vw8 = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
+      o[dt] = mfma16(__builtin_bit_cast(bf16x8, vw8), pbv, o[dt]);
+    }
+    wave_lds_sync();  // all lanes done reading the tile before the next overwrite
   }
 
-  // ---- out = o / l (the sink's term is in l), lse = m + ln l
-  if (live) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    const int64_t oo = ((int64_t)b * a.Hq + g * G + hh) * kHeadDim;
-    *reinterpret_cast<uint32_t*>(a.out + oo + 2 * jj) = pack_bf16x2(o0 * inv, o1 * inv);
-    if (a.lse && jj == 0)
-      a.lse[(int64_t)b * a.Hq + g * G + hh] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+  // ---- merge the 4 waves: per head max, sum and output; then the sink, out = o / l, lse
+  __syncthreads();  // every wave is out of its key loop: the tile memory becomes the merge buffers
+  float* red_m = reinterpret_cast<float*>(lds);  // [4][16]
+  float* red_l = red_m + 64;                    // [4][16]
+  float* red_o = red_l + 64;                    // [4][16][68]
+  {
+    float lt = l_run + __shfl_xor(l_run, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (lq == 0) {
+      red_m[wave * 16 + lc] = m_run;
+      red_l[wave * 16 + lc] = lt;
+    }
+    // lane holds O^T[d = 16 dt + 4 lq + r][head lc]
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red_o[(wave * 16 + lc) * 68 + 16 * dt + 4 * lq + r] = o[dt][r];
+  }
+  __syncthreads();
+  const int hh = t >> 4;        // head of this KV head
+  const int d0 = (t & 15) * 4;  // 4 output columns
+  if (hh < G) {
+    float M = red_m[hh];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, red_m[w * 16 + hh]);
+    float wsc[4];
+    float lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wsc[w] = fast_exp2(red_m[w * 16 + hh] - M);
+      lsum += red_l[w * 16 + hh] * wsc[w];
+    }
+    float acc[4];
+#pragma unroll
+    for (int cq = 0; cq < 4; ++cq) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) sum += red_o[(w * 16 + hh) * 68 + d0 + cq] * wsc[w];
+      acc[cq] = sum;
+    }
+    const int hq = g * G + hh;
+    const float s2 = a.sinks ? a.sinks[hq] * kLog2e : -INFINITY;
+    const float Mf = fmaxf(M, s2);
+    const float scl = fast_exp2(M - Mf);
+    const float Z = fast_exp2(s2 - Mf) + lsum * scl;
+    const float inv = Z > 0.f ? scl / Z : (Z == 0.f ? 0.f : Z);
+    u32x2 w2;
+    w2[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    w2[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<u32x2*>(a.out + ((int64_t)b * a.Hq + hq) * kHeadDim + d0) = w2;
+    if (a.lse && d0 == 0) a.lse[(int64_t)b * a.Hq + hq] = (Z == 0.f) ? -INFINITY : (Mf + __log2f(Z)) * kLn2;
   }
 }
 

@@ -117,7 +117,7 @@ struct RopeAppendArgs {
 
 // One decode step in one launch: rotary encoding of the new token's query and
 // key, append of the rotated key and the value to the cache, attention.
-constexpr int kStepMaxG = 8;      // query heads per KV head the fused step supports
+constexpr int kStepMaxG = 16;     // query heads per KV head the fused step supports (the MFMA columns)
 constexpr int kStepMaxKeys = 2048;  // keys a query of the fused step may read (one workgroup streams them)
 enum StepCacheKind : int { STEP_CACHE_CONTIGUOUS = 0, STEP_CACHE_PAGED = 1, STEP_CACHE_RING = 2 };
 struct DecodeStepArgs {

@@ -383,7 +383,7 @@ int gqa_rope_append(const void* q, const void* k, const void* v, void* q_out,
  *   sinks, out [B, Hq, D], lse [B, Hq] (optional), window, sink_tokens,
  *     scale: as gqa_attn_decode.  With a ring cache the ring is the window
  *     (window 0 or cache_len) and sink_tokens must be 0.
- * bf16 only (fp32: GQA_ERR_UNSUPPORTED), at most 8 query heads per KV head,
+ * bf16 only (fp32: GQA_ERR_UNSUPPORTED), at most 16 query heads per KV head,
  * and at most 2048 keys per query (window + sink_tokens on windowed layers,
  * the cache capacity on dense ones): one workgroup streams a (sequence, KV
  * head)'s keys, which suits windowed layers and short caches; longer key

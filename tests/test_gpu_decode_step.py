@@ -12,7 +12,7 @@ calls it replaces and against the fp64 oracle:
 * end to end, the output matches the oracle composition from the unrotated
   inputs (rope_append_ref, then decode_ref / decode_ring_ref), to the bf16 bar.
 Contiguous, paged and ring caches; dense and windowed layers, sink tokens,
-custom frequency tables, both pairings, 8 and 4 query heads per KV head,
+custom frequency tables, both pairings, 16, 8 and 4 query heads per KV head,
 sequences of one token, shorter than the window, and far longer.
 """
 import numpy as np
@@ -113,6 +113,14 @@ def test_step_contiguous_custom_table_halves_g4():
     say("decode step contiguous, custom table, halves pairing, mscale 1.1, 16/4 heads")
     run_case(R.CACHE_CONTIGUOUS, B, Hq, Hkv, (B, Lmax, Hkv, 64), seqlens, 128, 0, inv=inv, pairing=1, mscale=1.1,
              cfg=82)
+
+
+def test_step_sixteen_heads_per_kv_head():
+    # 32 query heads over 2 KV heads: the 16 columns of the step's matrix products all in use
+    B, Hq, Hkv, Lmax = 4, 32, 2, 700
+    seqlens = np.array([1, 33, 640, 700], dtype=np.int32)
+    say("decode step contiguous, 32/2 heads, window 256, pairing halves")
+    run_case(R.CACHE_CONTIGUOUS, B, Hq, Hkv, (B, Lmax, Hkv, 64), seqlens, 256, 0, pairing=1, cfg=88)
 
 
 @pytest.mark.parametrize("window", [128, 0])
