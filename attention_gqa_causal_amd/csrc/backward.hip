@@ -628,6 +628,11 @@ __global__ __launch_bounds__(BT, 2) void bwd_dq_kernel(BwdArgs a) {
           sc = mfma32(ka[kk], qb[i][kk], kk == 0 ? zero16() : sc);
           dp = mfma32(va[kk], gb[i][kk], kk == 0 ? zero16() : dp);
         }
+        // Dense layers: the vector work of an N-tile runs at a higher issue
+        // priority than the matrix work, so of the two waves of a SIMD the one
+        // with exponentials to do goes before one that only feeds MFMAs
+        // (measured 3-4 % on the dense layer; windowed layers unchanged).
+        if (W == 0) __builtin_amdgcn_s_setprio(1);
         const int dh = pos0[i] + lr - j0 - 4 * lg;
         const int dlw = W > 0 ? dh - W : -0x40000000;
         mask_half<STK>(sc, h, j0, pos0[i], phi[i], W, st, dh, dlw, ds);
@@ -645,6 +650,7 @@ __global__ __launch_bounds__(BT, 2) void bwd_dq_kernel(BwdArgs a) {
           }
           db[uu] = __builtin_bit_cast(bf16x8, w);
         }
+        if (W == 0) __builtin_amdgcn_s_setprio(0);
         // K^T operands are read per N-tile: holding them across both would
         // cost 16 registers the allocator does not have
 #pragma unroll
