@@ -83,6 +83,27 @@ enum KvMode : int {
                    // the ring [B, W, Hkv, D] of lmax = W slots (row b * W + j % W)
 };
 
+// Division of a non-negative int below 2^31 by a divisor d >= 1 fixed for a
+// launch, without a division sequence on the device: the host picks a shift
+// sh with 2^sh >= d and a multiplier m = floor(2^32 (2^sh - d) / d) + 1, and
+// n / d = (umulhi(n, m) + n) >> sh (the round-up method of Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994).
+struct FastDiv {
+  uint32_t d, m, sh;
+};
+
+__host__ __device__ inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t sh = 0;
+  while ((1ull << sh) < d) ++sh;
+  const uint64_t m = ((1ull << 32) * ((1ull << sh) - d)) / d + 1;
+  return FastDiv{d, (uint32_t)m, sh};
+}
+
+__host__ __device__ inline int fast_div(int n, const FastDiv& f) {
+  const uint32_t t = (uint32_t)(((uint64_t)(uint32_t)n * f.m) >> 32);
+  return (int)((t + (uint32_t)n) >> f.sh);
+}
+
 struct SeqArgs {
   // query side
   const int32_t* cu_seqlens_q;  // varlen only (NULL for batched)

@@ -30,6 +30,8 @@ struct PrefillArgs {
   int rope;          // queries arrive unrotated: 0 no, 1 pairs (2i, 2i+1), 2 pairs (i, i + D/2)
   const float* inv_freq;  // rope: [D/2] or NULL (the default table)
   float rope_mscale;
+  // divisors of the workgroup-to-job mapping, filled by the launcher
+  FastDiv div_wg_per_seq, div_hkv, div_g, div_units;
 };
 
 // Decode-style attention: one query token per sequence, KV split over

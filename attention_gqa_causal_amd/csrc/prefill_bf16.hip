@@ -242,21 +242,25 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
   // (sequence, KV head) go to the same XCD (dispatch is round-robin over the 8
   // XCDs) and are dispatched back to back, heaviest tile group first, so they
   // stream the same K/V tiles at about the same time out of that XCD's L2.
+  // (divisions by the launch's divisors use the launcher's multipliers: a
+  // division sequence per job is a good part of a short job's setup)
   const int U = a.B * a.Hkv;
   int unit, rank;
   {
     if ((U & 7) == 0) {
       const int sidx = x >> 3;
-      rank = sidx % a.wg_per_seq;
-      unit = (x & 7) + 8 * (sidx / a.wg_per_seq);
+      const int sq = fast_div(sidx, a.div_wg_per_seq);
+      rank = sidx - sq * a.wg_per_seq;
+      unit = (x & 7) + 8 * sq;
     } else {
-      rank = x / U;
-      unit = x % U;
+      rank = fast_div(x, a.div_units);
+      unit = x - rank * U;
     }
   }
   const int tg = a.wg_per_seq - 1 - rank;
-  const int g = unit % a.Hkv;
-  const int b = order ? order[unit / a.Hkv] : unit / a.Hkv;  // ragged batches: longest sequences first
+  const int uq = fast_div(unit, a.div_hkv);
+  const int g = unit - uq * a.Hkv;
+  const int b = order ? order[uq] : uq;  // ragged batches: longest sequences first
   const SeqView sv = seq_view<MODE>(a.seq, b, VARLEN);
   const int G = a.G;
   const int n_ntiles = ((sv.q_len + 31) >> 5) * G;
@@ -273,7 +277,7 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
   for (int i = 0; i < 2; ++i) {
     const int n = tg * NT_WG + wave * 2 + i;
     nt_valid[i] = n < n_ntiles;
-    const int pb = n / G;
+    const int pb = fast_div(n, a.div_g);
     nt_t0[i] = pb * 32;
     nt_hq[i] = g * G + (n - pb * G);
     pos0[i] = pos_off + nt_t0[i];
@@ -282,8 +286,8 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
 
   // ---- key range of the whole workgroup
   const int n_last = min(tg * NT_WG + NT_WG - 1, n_ntiles - 1);
-  const int t_min = ((tg * NT_WG) / G) * 32;
-  const int t_max = min((n_last / G) * 32 + 31, sv.q_len - 1);
+  const int t_min = fast_div(tg * NT_WG, a.div_g) * 32;
+  const int t_max = min(fast_div(n_last, a.div_g) * 32 + 31, sv.q_len - 1);
   const int p_min = pos_off + t_min;
   const int p_max = pos_off + t_max;
   const int lo = W > 0 ? max(0, p_min - W + 1) : 0;
@@ -298,30 +302,22 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
 
   // ---- Q^T operands (B of S^T = K Q^T): lane holds row lr, d = 16*k + 8*lg .. +7
   // (addresses: the N-tile's first row as a scalar base, a 32-bit lane offset)
+  // Unconditional loads: a row past the end reads the sequence's last row (its
+  // head is valid; its results are never stored).  Without branches around
+  // the loads the compiler keeps each operand where its load puts it, so
+  // nothing waits for them before their first use (the rotation, or the first
+  // scores).  The N-tile's first row is a scalar base, the lane's row a 32-bit
+  // offset.
   bf16x8 qb[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int t = nt_t0[i] + lr;
-    const bool ok = nt_valid[i] && t < sv.q_len;
-    const char* qt = reinterpret_cast<const char*>(a.q + ((sv.q_row0 + nt_t0[i]) * a.Hq + nt_hq[i]) * (int64_t)kHeadDim);
-    const uint32_t qo = (uint32_t)(lr * a.Hq * kHeadDim + 8 * lg) * 2u;
-    if constexpr (ROPE != 0) {
-      // Unconditional loads: a row past the end reads the sequence's last row
-      // (its head is valid; its results are never stored).  Without the
-      // branches the compiler keeps each operand where its load puts it, so
-      // nothing waits for the loads before the rotation needs them.
-      const int ts = ok ? t : sv.q_len - 1;
-      const __bf16* qr = a.q + ((sv.q_row0 + ts) * a.Hq + nt_hq[i]) * (int64_t)kHeadDim + 8 * lg;
+    const int t0 = min(nt_t0[i], sv.q_len - 1);
+    const int r = min(nt_t0[i] + lr, sv.q_len - 1) - t0;  // 0 .. 31
+    const char* qt = reinterpret_cast<const char*>(a.q + ((sv.q_row0 + t0) * a.Hq + nt_hq[i]) * (int64_t)kHeadDim);
+    const uint32_t qo = (uint32_t)(r * a.Hq * kHeadDim + 8 * lg) * 2u;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) qb[i][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qr + 16 * k));
-      continue;
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok) v = *reinterpret_cast<const u32x4*>(qt + qo + 32 * k);
-      qb[i][k] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int k = 0; k < 4; ++k)
+      qb[i][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qt + qo + 32 * k));
   }
   float m_run[2], l_run[2];
   f32x16 o[2][2];
@@ -346,6 +342,10 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
   const __bf16* kbase2 = MODE == KV_RING ? a.k2 + g * kHeadDim : nullptr;
   const __bf16* vbase2 = MODE == KV_RING ? a.v2 + g * kHeadDim : nullptr;
   const int dma_chunk = ((lane & 7) ^ kswz(lane >> 3)) * 8;  // logical chunk this lane's LDS slot holds
+  // LDS byte addresses of the buffers, formed once (a cast per load would
+  // test the address for null each time)
+  const uint32_t ks_lds = lds_addr((lds_void*)&Ks[0][0]);
+  const uint32_t vs_lds = lds_addr((lds_void*)&Vs[0][0]);
   auto fetch_blk = [&](int t, int (&blk)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -364,16 +364,19 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
       const int64_t tb = ((int64_t)sv.b * a.seq.lmax + j0) * kv_stride;
       const char* kt = reinterpret_cast<const char*>(kbase + tb);
       const char* vt = reinterpret_cast<const char*>(vbase + tb);
+      uint32_t off[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int r = min(16 * wave + 8 * i + (lane >> 3), hi - j0);
-        const uint32_t off = (__umul24(r, (uint32_t)kv_stride) + dma_chunk) * 2u;  // r < 64: 24-bit product
-        const int lofs = (16 * wave + 8 * i) * RS;  // wave-uniform slice of 8 rows
-        dma16(kt, off, (lds_void*)(&Ks[buf][lofs]));
-        dma16(vt, off, (lds_void*)(&Vs[buf][lofs]));
+        off[i] = (__umul24(r, (uint32_t)kv_stride) + dma_chunk) * 2u;  // r < 64: 24-bit product
       }
+      const uint32_t lofs = (uint32_t)(buf * BK * RS + 16 * wave * RS) * 2u;  // wave-uniform slice of 16 rows
+      constexpr uint32_t kHalf = 8 * RS * 2;                                  // its second 8 rows
+      dma16_kv(kt, vt, off[0], off[1], ks_lds + lofs, ks_lds + lofs + kHalf, vs_lds + lofs, vs_lds + lofs + kHalf);
       return;
     }
+    const void* ka[2];
+    const void* va[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int j = min(tile_j0(t) + 16 * wave + 8 * i + (lane >> 3), hi);
@@ -395,10 +398,12 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
         row = kv_row<MODE>(a.seq, sv, j);
       }
       const int64_t off = row * kv_stride + dma_chunk;
-      const int lofs = (16 * wave + 8 * i) * RS;  // wave-uniform slice of 8 rows
-      dma16((const void*)(kb + off), (lds_void*)(&Ks[buf][lofs]));
-      dma16((const void*)(vb + off), (lds_void*)(&Vs[buf][lofs]));
+      ka[i] = kb + off;
+      va[i] = vb + off;
     }
+    const uint32_t lofs = (uint32_t)(buf * BK * RS + 16 * wave * RS) * 2u;  // wave-uniform slice of 16 rows
+    constexpr uint32_t kHalf = 8 * RS * 2;                                  // its second 8 rows
+    dma16_kv(ka[0], ka[1], va[0], va[1], ks_lds + lofs, ks_lds + lofs + kHalf, vs_lds + lofs, vs_lds + lofs + kHalf);
   };
 
 
@@ -592,16 +597,29 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
     }
   }
   wave_lds_sync();  // the wave reads back only its own rows
+  // rows 8j .. 8j+7 of the wave's 64: N-tile j / 4, row (lane / 8) + 8 (j % 4)
+  // of it, 16-byte chunk lane % 8
+  u32x4 ov[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int i = j >> 2;                        // N-tile of rows 8j .. 8j+7
-    const int r = (lane >> 3) + 8 * (j & 3);     // row within the N-tile
-    const int cc = lane & 7;                     // 16-byte chunk of the row
-    const int t = nt_t0[i] + r;
-    if (!nt_valid[i] || t >= sv.q_len) continue;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + (32 * i + r) * RS + kchunk(cc, r));
+    const int r = (lane >> 3) + 8 * (j & 3);
+    ov[j] = *reinterpret_cast<const u32x4*>(stg + (32 * (j >> 2) + r) * RS + kchunk(lane & 7, r));
+  }
+  auto store = [&](int j) {
+    const int i = j >> 2;
+    const int r = (lane >> 3) + 8 * (j & 3);
     char* ot = reinterpret_cast<char*>(a.out + ((sv.q_row0 + nt_t0[i]) * a.Hq + nt_hq[i]) * (int64_t)kHeadDim);
-    *reinterpret_cast<u32x4*>(ot + (uint32_t)(r * a.Hq * kHeadDim + 8 * cc) * 2u) = v;
+    *reinterpret_cast<u32x4*>(ot + (uint32_t)(r * a.Hq * kHeadDim + 8 * (lane & 7)) * 2u) = ov[j];
+  };
+  // Both N-tiles whole (every tile but a sequence's last): no per-row tests.
+  const bool whole = nt_valid[0] && nt_valid[1] && max(nt_t0[0], nt_t0[1]) + 31 < sv.q_len;
+  if (whole) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) store(j);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (nt_valid[j >> 2] && nt_t0[j >> 2] + (lane >> 3) + 8 * (j & 3) < sv.q_len) store(j);
   }
 }
 
@@ -647,9 +665,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
 
 int prefill_ntiles_per_wg() { return NT_WG; }
 
-hipError_t launch_prefill_bf16(const PrefillArgs& a, int kv_mode, bool varlen_q, hipStream_t s) {
-  const int grid = a.B * a.Hkv * a.wg_per_seq;
+hipError_t launch_prefill_bf16(const PrefillArgs& args, int kv_mode, bool varlen_q, hipStream_t s) {
+  const int grid = args.B * args.Hkv * args.wg_per_seq;
   if (grid <= 0) return hipSuccess;
+  PrefillArgs a = args;
+  a.div_wg_per_seq = make_fastdiv(a.wg_per_seq);
+  a.div_hkv = make_fastdiv(a.Hkv);
+  a.div_g = make_fastdiv(a.G);
+  a.div_units = make_fastdiv(a.B * a.Hkv);
   const bool stk = a.window > 0 && a.sink_tokens > 0;
   if (a.rope) {  // queries rotated in the kernel: whole-sequence prefill only
     if (kv_mode != KV_BATCHED || varlen_q) return hipErrorInvalidValue;

@@ -171,6 +171,45 @@ __device__ __forceinline__ void dma16(const void* gaddr, lds_void* lds_dst) {
       : "memory");
 }
 
+// The K and V halves of a wave's share of a tile: four 16-byte loads (K rows
+// at voff0 and voff1 past kbase, V rows at the same offsets past vbase) under
+// one save and restore of M0, same contract as dma16.  lds_k0 .. lds_v1 are
+// LDS byte addresses.
+__device__ __forceinline__ void dma16_kv(const char* kbase, const char* vbase, uint32_t voff0, uint32_t voff1,
+                                         uint32_t lds_k0, uint32_t lds_k1, uint32_t lds_v0, uint32_t lds_v1) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_nop 4\n\t"
+      "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %3\n\t"
+      "s_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %4\n\t"
+      "s_mov_b32 m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %8\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %4\n\t"
+      "s_mov_b32 m0, %0\n\ts_nop 0"
+      : "=&s"(saved)
+      : "v"(voff0), "v"(voff1), "s"(uniform_ptr(kbase)), "s"(uniform_ptr(vbase)),
+        "s"(__builtin_amdgcn_readfirstlane(lds_k0)), "s"(__builtin_amdgcn_readfirstlane(lds_k1)),
+        "s"(__builtin_amdgcn_readfirstlane(lds_v0)), "s"(__builtin_amdgcn_readfirstlane(lds_v1))
+      : "memory");
+}
+
+// The same with 64-bit per-lane addresses (K rows at k0, k1, V rows at v0, v1).
+__device__ __forceinline__ void dma16_kv(const void* k0, const void* k1, const void* v0, const void* v1,
+                                         uint32_t lds_k0, uint32_t lds_k1, uint32_t lds_v0, uint32_t lds_v1) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_nop 4\n\t"
+      "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, off\n\t"
+      "s_mov_b32 m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %8\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, off\n\t"
+      "s_mov_b32 m0, %0\n\ts_nop 0"
+      : "=&s"(saved)
+      : "v"(k0), "v"(k1), "v"(v0), "v"(v1),
+        "s"(__builtin_amdgcn_readfirstlane(lds_k0)), "s"(__builtin_amdgcn_readfirstlane(lds_k1)),
+        "s"(__builtin_amdgcn_readfirstlane(lds_v0)), "s"(__builtin_amdgcn_readfirstlane(lds_v1))
+      : "memory");
+}
+
 // Pin the instruction order: nothing is scheduled across this point.
 __device__ __forceinline__ void fence_schedule() { __builtin_amdgcn_sched_barrier(0); }
 
