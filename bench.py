@@ -33,8 +33,8 @@ stream the kernels run on; every stage's own time, TFLOP/s, GB/s and roofline
 fraction is reported under "parts".  "roofline" describes the dominant kernel
 (dense prefill, MFMA-bound); "roofline_decode" the HBM-bound dense decode.
 Each part also carries two other timings of the same stage, never used for
-`value`: cold (each call after a 512 MiB write that evicts the last-level
-cache; median) and back to back (the stage alone, called `steps` times in a
+`value`: cold (each call after a 512 MiB read pass that evicts the last-level
+cache and leaves it clean; median) and back to back (the stage alone, called `steps` times in a
 row, median; a dense MFMA kernel then runs at the lower clock its own power
 draw settles at, where inside the step it starts from the clock the HBM-bound
 stages left).  A part's `roofline_frac` is quoted on the cold median for
@@ -263,8 +263,8 @@ def summarize_trace(trace_dir, out_md=None):
              "    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o run -- "
              "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline",
              "    python3 bench.py --summarize-trace gpurun_out/prof_trace", "",
-             "Every stage runs 35 times: 3 warm-up, 10 in the step loop, 10 cold (each after a 512 MiB fill, the "
-             "`FillFunctor<int>` rows), 2 + 10 back to back. rocprofv3 `--stats` summary (all stages of one kernel "
+             "Every stage runs 35 times: 3 warm-up, 10 in the step loop, 10 cold (each after a 512 MiB read pass, the "
+             "`reduce_kernel` rows), 2 + 10 back to back. rocprofv3 `--stats` summary (all stages of one kernel "
              "pooled):", "",
              "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
     with open(stats[0]) as f:
@@ -796,13 +796,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # cold cache: before each call a 512 MiB write evicts the 256 MiB last-level cache (and the L2s),
-    # so the call's inputs come from HBM; reported beside the warm numbers, never as `value`
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    # cold cache: before each call a 512 MiB read pass evicts the 256 MiB last-level cache (and the L2s),
+    # so the call's inputs come from HBM; reported beside the warm numbers, never as `value`.  A read pass
+    # leaves clean lines behind: after a write pass the timed call would also pay the write-back of 256 MiB
+    # of someone else's dirty lines (measured: +3.4 us on the window-128 prefill)
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    flush_sink = torch.zeros((), dtype=torch.int64, device=dev)
     cold = {n: [] for n in names}
     for i in range(args.steps):
         for n in names:
-            flush.fill_(i)
+            torch.sum(flush, dtype=torch.int64, out=flush_sink)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             stages[n]["fn"]()
