@@ -172,21 +172,23 @@ __global__ __launch_bounds__(BT, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // Q / dO rows out of that XCD's L2.
   const int U = a.B * a.Hkv;
   const int per_unit = nkb * a.n_slabs;  // (slab, key block) jobs of one (sequence, KV head)
+  // (divisions by the launch's divisors use the launcher's multipliers)
   int unit, r;
   {
     const int x = blockIdx.x;
     if ((U & 7) == 0) {
       const int sidx = x >> 3;
-      r = sidx % per_unit;
-      unit = (x & 7) + 8 * (sidx / per_unit);
+      const int sq = fast_div(sidx, a.div_per_unit);
+      r = sidx - sq * per_unit;
+      unit = (x & 7) + 8 * sq;
     } else {
-      r = x / U;
-      unit = x % U;
+      r = fast_div(x, a.div_units);
+      unit = x - r * U;
     }
   }
-  const int slab = r / nkb;
+  const int slab = fast_div(r, a.div_nkb);
   const int kb = r - slab * nkb;
-  const int b = unit / a.Hkv;
+  const int b = fast_div(unit, a.div_hkv);
   const int g = unit - b * a.Hkv;
   const int st = STK && W > 0 ? a.sink_tokens : 0;
   const int j0 = kb * KB;
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(BT, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // queries that can see a key of the block: p >= j0 up to p_hi; this
   // workgroup takes those of its slab
   const int p_hi = block_p_hi(j0, S, W, st);
-  const int s_lo = j0 / a.slab_len, s_hi = p_hi / a.slab_len;
+  const int s_lo = fast_div(j0, a.div_slab_len), s_hi = fast_div(p_hi, a.div_slab_len);
   if (slab < s_lo || slab > s_hi) return;  // uniform: the slab holds no query of the block
   const bool partial = s_hi > s_lo;
   const int t_lo = max(j0, slab * a.slab_len) / QT;
@@ -234,27 +236,29 @@ __global__ __launch_bounds__(BT, 2) void bwd_dkdv_kernel(BwdArgs a) {
     qoff[ii] = (uint32_t)((((R & 31) * a.Hq + (R >> 5)) * kHeadDim + dma_chunk) * 2);
   }
   const uint32_t loff = (uint32_t)((lg * S + lr) * 4);
+  const uint32_t smem_lds = lds_addr((lds_void*)smem_b);  // formed once: a cast per load tests for null
   auto dma_unit = [&](int t, int i, int buf) {
     const int q0 = (t_lo + t) * QT;
     const bool fast = q0 + QT <= S && 2 * i + 1 < G;  // uniform
     const int64_t ubase = ((int64_t)b * S + q0) * q_stride + (int64_t)(g * G + 2 * i) * kHeadDim;
     const char* qb = reinterpret_cast<const char*>(q + ubase);
     const char* gb = reinterpret_cast<const char*>(dout + ubase);
-    __bf16* qs = smem_b + (2 * buf) * TILE;
-    __bf16* gs = smem_b + (2 * buf + 1) * TILE;
+    uint32_t off[2];
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
-      uint32_t off = qoff[ii];
+      off[ii] = qoff[ii];
       if (!fast) {
         const int R = 16 * wave + 8 * ii + (lane >> 3);
         const int pr = min(q0 + (R & 31), S - 1) - q0;
         const int e = min(2 * i + (R >> 5), G - 1) - 2 * i;
-        off = (uint32_t)(((pr * a.Hq + e) * kHeadDim + dma_chunk) * 2);
+        off[ii] = (uint32_t)(((pr * a.Hq + e) * kHeadDim + dma_chunk) * 2);
       }
-      const int lofs = (16 * wave + 8 * ii) * RS;  // wave-uniform slice of 8 rows
-      dma16(qb, off, (lds_void*)(qs + lofs));
-      dma16(gb, off, (lds_void*)(gs + lofs));
     }
+    // wave-uniform slice of 16 rows of the Q and dO tiles of buffer buf (byte addresses)
+    const uint32_t lq = smem_lds + (uint32_t)((2 * buf) * TILE + 16 * wave * RS) * 2u;
+    const uint32_t lgo = lq + (uint32_t)TILE * 2u;
+    constexpr uint32_t kHalf = 8 * RS * 2;
+    dma16_kv(qb, gb, off[0], off[1], lq, lq + kHalf, lgo, lgo + kHalf);
     if (wave == 0) {
       const int64_t lbase = ((int64_t)b * a.Hq + g * G + 2 * i) * S + q0;
       uint32_t off = loff;
@@ -503,20 +507,22 @@ __global__ __launch_bounds__(BT, 2) void bwd_dq_kernel(BwdArgs a) {
   const int n_ntiles = ((S + 31) >> 5) * G;
   const int wg_per_seq = (n_ntiles + NT_WG - 1) / NT_WG;
   const int U = a.B * a.Hkv;
+  // (divisions by the launch's divisors use the launcher's multipliers)
   int unit, rank;
   {
     const int x = blockIdx.x;
     if ((U & 7) == 0) {
       const int sidx = x >> 3;
-      rank = sidx % wg_per_seq;
-      unit = (x & 7) + 8 * (sidx / wg_per_seq);
+      const int sq = fast_div(sidx, a.div_wg_per_seq);
+      rank = sidx - sq * wg_per_seq;
+      unit = (x & 7) + 8 * sq;
     } else {
-      rank = x / U;
-      unit = x % U;
+      rank = fast_div(x, a.div_units);
+      unit = x - rank * U;
     }
   }
   const int tg = wg_per_seq - 1 - rank;  // the latest positions (most keys) first
-  const int b = unit / a.Hkv;
+  const int b = fast_div(unit, a.div_hkv);
   const int g = unit - b * a.Hkv;
 
   int nt_t0[2], nt_hq[2], pos0[2], phi[2];
@@ -525,15 +531,15 @@ __global__ __launch_bounds__(BT, 2) void bwd_dq_kernel(BwdArgs a) {
   for (int i = 0; i < 2; ++i) {
     const int n = tg * NT_WG + wave * 2 + i;
     nt_valid[i] = n < n_ntiles;
-    const int pb = n / G;
+    const int pb = fast_div(n, a.div_g);
     nt_t0[i] = pb * 32;
     nt_hq[i] = g * G + (n - pb * G);
     pos0[i] = nt_t0[i];
     phi[i] = min(nt_t0[i] + 31, S - 1);
   }
   const int n_last = min(tg * NT_WG + NT_WG - 1, n_ntiles - 1);
-  const int t_min = ((tg * NT_WG) / G) * 32;
-  const int t_max = min((n_last / G) * 32 + 31, S - 1);
+  const int t_min = fast_div(tg * NT_WG, a.div_g) * 32;
+  const int t_max = min(fast_div(n_last, a.div_g) * 32 + 31, S - 1);
   const int lo = W > 0 ? max(0, t_min - W + 1) : 0;
   const int hi = t_max;  // inclusive
   const int j_begin = lo & ~(BK - 1);
@@ -545,24 +551,20 @@ __global__ __launch_bounds__(BT, 2) void bwd_dq_kernel(BwdArgs a) {
   // Q and dO rows as B operands (column = query, k = d), lse and D per lane
   bf16x8 qb[2][4], gb[2][4];
   float l2[2], dl[2];
+  // (unconditional loads: a row past the end reads the last row, whose head
+  // is valid; its results are never stored)
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int t = nt_t0[i] + lr;
-    const bool ok = nt_valid[i] && t < S;
+    const int t = min(nt_t0[i] + lr, S - 1);
     const int64_t off = (((int64_t)b * S + t) * a.Hq + nt_hq[i]) * kHeadDim + 8 * lg;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-      if (ok) {
-        x = *reinterpret_cast<const u32x4*>(q + off + 16 * kk);
-        y = *reinterpret_cast<const u32x4*>(dout + off + 16 * kk);
-      }
-      qb[i][kk] = __builtin_bit_cast(bf16x8, x);
-      gb[i][kk] = __builtin_bit_cast(bf16x8, y);
+      qb[i][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + off + 16 * kk));
+      gb[i][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dout + off + 16 * kk));
     }
     const int64_t li = ((int64_t)b * a.Hq + nt_hq[i]) * S + t;
-    l2[i] = ok ? a.lse2[li] : 0.f;
-    dl[i] = ok ? a.dlt[li] : 0.f;
+    l2[i] = a.lse2[li];
+    dl[i] = a.dlt[li];
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);  // as in the dK/dV kernel: no compiler wait on these inside the tile loop
   f32x16 acc[2][2];
@@ -578,18 +580,21 @@ __global__ __launch_bounds__(BT, 2) void bwd_dq_kernel(BwdArgs a) {
   // wave w fills rows 16w .. 16w+15 of a tile; rows past the key range repeat
   // row hi (masked, in bounds)
   // (a scalar base per tile and a 32-bit offset per lane)
+  const uint32_t ks_lds = lds_addr((lds_void*)&Ks[0][0]);  // formed once: a cast per load tests for null
+  const uint32_t vs_lds = lds_addr((lds_void*)&Vs[0][0]);
   auto dma_tile = [&](int t, int buf) {
     const int j0 = tile_j0(t);
     const char* kt = reinterpret_cast<const char*>(kbase + (int64_t)j0 * kv_stride);
     const char* vt = reinterpret_cast<const char*>(vbase + (int64_t)j0 * kv_stride);
+    uint32_t off[2];
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
       const int r = min(16 * wave + 8 * ii + (lane >> 3), hi - j0);
-      const uint32_t off = (__umul24(r, (uint32_t)kv_stride) + dma_chunk) * 2u;  // r < 64: 24-bit product
-      const int lofs = (16 * wave + 8 * ii) * RS;
-      dma16(kt, off, (lds_void*)(&Ks[buf][lofs]));
-      dma16(vt, off, (lds_void*)(&Vs[buf][lofs]));
+      off[ii] = (__umul24(r, (uint32_t)kv_stride) + dma_chunk) * 2u;  // r < 64: 24-bit product
     }
+    const uint32_t lofs = (uint32_t)(buf * BK * RS + 16 * wave * RS) * 2u;  // wave-uniform slice of 16 rows
+    constexpr uint32_t kHalf = 8 * RS * 2;
+    dma16_kv(kt, vt, off[0], off[1], ks_lds + lofs, ks_lds + lofs + kHalf, vs_lds + lofs, vs_lds + lofs + kHalf);
   };
   int vofs[2];
   tr_offsets(lane, vofs);
@@ -696,15 +701,28 @@ __global__ __launch_bounds__(BT, 2) void bwd_dq_kernel(BwdArgs a) {
   }
   wave_lds_sync();  // the wave reads back only its own rows
   __bf16* dq = reinterpret_cast<__bf16*>(a.dq);
+  // rows 8j .. 8j+7 of the wave's 64: N-tile j / 4, row (lane / 8) + 8 (j % 4)
+  // of it, 16-byte chunk lane % 8; a wave whose two N-tiles are whole stores
+  // without per-row tests
+  u32x4 ov[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int i = j >> 2;                     // N-tile of rows 8j .. 8j+7
-    const int r = (lane >> 3) + 8 * (j & 3);  // row within the N-tile
-    const int cc = lane & 7;                  // 16-byte chunk of the row
-    const int t = nt_t0[i] + r;
-    if (!nt_valid[i] || t >= S) continue;
-    const u32x4 w = *reinterpret_cast<const u32x4*>(stg + (32 * i + r) * RS + kchunk(cc, r));
-    *reinterpret_cast<u32x4*>(dq + (((int64_t)b * S + t) * a.Hq + nt_hq[i]) * kHeadDim + 8 * cc) = w;
+    const int r = (lane >> 3) + 8 * (j & 3);
+    ov[j] = *reinterpret_cast<const u32x4*>(stg + (32 * (j >> 2) + r) * RS + kchunk(lane & 7, r));
+  }
+  auto store = [&](int j) {
+    const int i = j >> 2;
+    const int t = nt_t0[i] + (lane >> 3) + 8 * (j & 3);
+    *reinterpret_cast<u32x4*>(dq + (((int64_t)b * S + t) * a.Hq + nt_hq[i]) * kHeadDim + 8 * (lane & 7)) = ov[j];
+  };
+  const bool whole = nt_valid[0] && nt_valid[1] && max(nt_t0[0], nt_t0[1]) + 31 < S;
+  if (whole) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) store(j);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (nt_valid[j >> 2] && nt_t0[j >> 2] + (lane >> 3) + 8 * (j & 3) < S) store(j);
   }
 }
 
@@ -802,7 +820,8 @@ void backward_plan(int B, int S, int Hkv, int window, int sink_tokens, int* n_sl
   *n_slabs = (S + len - 1) / len > 1 ? (S + len - 1) / len : 1;
 }
 
-hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_backward(const BwdArgs& args, hipStream_t s) {
+  const BwdArgs& a = args;
   const int64_t rows = (int64_t)a.B * a.S;
   if (rows > 0) {
     const int64_t blocks = (rows + BT / 64 - 1) / (BT / 64);
@@ -819,20 +838,28 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(bwd_dq_fp32_kernel, dim3((unsigned)nq), dim3(BT), 0, s, a);
     return hipGetLastError();
   }
-  const bool stk = a.window > 0 && a.sink_tokens > 0;
-  const int nkb = (a.S + KB - 1) / KB;
-  const unsigned g1 = (unsigned)((int64_t)a.B * a.Hkv * nkb * a.n_slabs);
-  const unsigned g1r = (unsigned)((int64_t)a.B * a.Hkv * nkb);
-  const int n_ntiles = ((a.S + 31) / 32) * a.G;
-  const unsigned g2 = (unsigned)((int64_t)a.B * a.Hkv * ((n_ntiles + NT_WG - 1) / NT_WG));
+  const bool stk = args.window > 0 && args.sink_tokens > 0;
+  const int nkb = (args.S + KB - 1) / KB;
+  const unsigned g1 = (unsigned)((int64_t)args.B * args.Hkv * nkb * args.n_slabs);
+  const unsigned g1r = (unsigned)((int64_t)args.B * args.Hkv * nkb);
+  const int n_ntiles = ((args.S + 31) / 32) * args.G;
+  const unsigned g2 = (unsigned)((int64_t)args.B * args.Hkv * ((n_ntiles + NT_WG - 1) / NT_WG));
+  BwdArgs ad = args;  // with the divisors of the job mappings
+  ad.div_units = make_fastdiv(ad.B * ad.Hkv);
+  ad.div_hkv = make_fastdiv(ad.Hkv);
+  ad.div_g = make_fastdiv(ad.G);
+  ad.div_nkb = make_fastdiv(nkb);
+  ad.div_per_unit = make_fastdiv(nkb * ad.n_slabs);
+  ad.div_slab_len = make_fastdiv(ad.slab_len);
+  ad.div_wg_per_seq = make_fastdiv((n_ntiles + NT_WG - 1) / NT_WG);
   if (stk) {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3(g1), dim3(BT), 0, s, a);
-    if (a.n_slabs > 1) hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<true>, dim3(g1r), dim3(BT), 0, s, a);
-    hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3(g2), dim3(BT), 0, s, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3(g1), dim3(BT), 0, s, ad);
+    if (ad.n_slabs > 1) hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<true>, dim3(g1r), dim3(BT), 0, s, ad);
+    hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3(g2), dim3(BT), 0, s, ad);
   } else {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3(g1), dim3(BT), 0, s, a);
-    if (a.n_slabs > 1) hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<false>, dim3(g1r), dim3(BT), 0, s, a);
-    hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3(g2), dim3(BT), 0, s, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3(g1), dim3(BT), 0, s, ad);
+    if (ad.n_slabs > 1) hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<false>, dim3(g1r), dim3(BT), 0, s, ad);
+    hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3(g2), dim3(BT), 0, s, ad);
   }
   return hipGetLastError();
 }

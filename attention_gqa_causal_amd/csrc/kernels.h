@@ -171,6 +171,8 @@ struct BwdArgs {
   float scale;         // softmax scale
   float scale_log2;    // scale * log2(e)
   int fp32;
+  // divisors of the workgroup-to-job mappings, filled by the launcher
+  FastDiv div_units, div_hkv, div_g, div_nkb, div_per_unit, div_slab_len, div_wg_per_seq;
 };
 
 int prefill_ntiles_per_wg();  // N-tiles (32 rows of one head) per prefill workgroup
