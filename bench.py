@@ -800,12 +800,13 @@ def main():
     # so the call's inputs come from HBM; reported beside the warm numbers, never as `value`.  A read pass
     # leaves clean lines behind: after a write pass the timed call would also pay the write-back of 256 MiB
     # of someone else's dirty lines (measured: +3.4 us on the window-128 prefill)
-    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
-    flush_sink = torch.zeros((), dtype=torch.int64, device=dev)
+    # (fp32 zeros summed in fp32: one read pass, no conversion copy)
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush_sink = torch.zeros((), dtype=torch.float32, device=dev)
     cold = {n: [] for n in names}
     for i in range(args.steps):
         for n in names:
-            torch.sum(flush, dtype=torch.int64, out=flush_sink)
+            torch.sum(flush, dim=0, out=flush_sink)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             stages[n]["fn"]()
