@@ -30,8 +30,14 @@ struct PrefillArgs {
   int rope;          // queries arrive unrotated: 0 no, 1 pairs (2i, 2i+1), 2 pairs (i, i + D/2)
   const float* inv_freq;  // rope: [D/2] or NULL (the default table)
   float rope_mscale;
-  // divisors of the workgroup-to-job mapping, filled by the launcher
-  FastDiv div_wg_per_seq, div_hkv, div_g, div_units;
+  // whole-sequence windowed layers whose pairs of tile groups need at most 3
+  // key tiles (window <= 128, no sink tokens, G = 8 or a multiple of 16): a
+  // workgroup runs two tile groups over the same tiles
+  int two_step;
+  // filled by the launcher: workgroups per (sequence, KV head), and the
+  // divisors of the workgroup-to-job mapping
+  int wg_per_job;
+  FastDiv div_wg_per_job, div_hkv, div_g, div_units;
 };
 
 // Decode-style attention: one query token per sequence, KV split over

@@ -229,9 +229,9 @@ __device__ __forceinline__ void rope_rotate_q(bf16x8 (&q)[4], const float (&cs)[
 // (sequence, KV head).  STK: the layer keeps start-of-sequence sink tokens
 // visible past its window (a separate instantiation, so that other layers
 // carry none of its code).
-template <int MODE, bool VARLEN, bool STK, int ROPE = 0>
+template <int MODE, bool VARLEN, bool STK, int ROPE = 0, bool TWO = false>
 __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, __bf16 (*Ks)[BK * RS],
-                                            __bf16 (*Vs)[BK * RS], const int* order = nullptr) {
+                                            __bf16 (*Vs)[BK * RS], __bf16* Stg, const int* order = nullptr) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (lets per-wave values live in SGPRs)
@@ -244,49 +244,43 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
   // stream the same K/V tiles at about the same time out of that XCD's L2.
   // (divisions by the launch's divisors use the launcher's multipliers: a
   // division sequence per job is a good part of a short job's setup)
+  //
+  // A job is one tile group, or (two_step: windowed whole-sequence layers
+  // whose tile groups 2r and 2r+1 need at most NBUF key tiles together) those
+  // two in turn over the same tiles in LDS: the second step loads no tile and
+  // repeats none of the job's setup.
   const int U = a.B * a.Hkv;
   int unit, rank;
   {
     if ((U & 7) == 0) {
       const int sidx = x >> 3;
-      const int sq = fast_div(sidx, a.div_wg_per_seq);
-      rank = sidx - sq * a.wg_per_seq;
+      const int sq = fast_div(sidx, a.div_wg_per_job);
+      rank = sidx - sq * a.wg_per_job;
       unit = (x & 7) + 8 * sq;
     } else {
       rank = fast_div(x, a.div_units);
       unit = x - rank * U;
     }
   }
-  const int tg = a.wg_per_seq - 1 - rank;
+  const int jr = a.wg_per_job - 1 - rank;
+  constexpr bool two = TWO;
+  const int tg_hi = two ? min(2 * jr + 1, a.wg_per_seq - 1) : jr;  // steps run tg_hi down to tg_lo
+  const int tg_lo = two ? 2 * jr : jr;
   const int uq = fast_div(unit, a.div_hkv);
   const int g = unit - uq * a.Hkv;
   const int b = order ? order[uq] : uq;  // ragged batches: longest sequences first
   const SeqView sv = seq_view<MODE>(a.seq, b, VARLEN);
   const int G = a.G;
   const int n_ntiles = ((sv.q_len + 31) >> 5) * G;
-  if (tg < 0 || tg * NT_WG >= n_ntiles) return;  // uniform over the workgroup
+  if (tg_lo < 0 || tg_lo * NT_WG >= n_ntiles) return;  // uniform over the workgroup
   if (a.skip_single && sv.q_len == 1) return;
   const int pos_off = sv.kv_len - sv.q_len;
   const int W = a.window;
   const float c = a.scale_log2;
 
-  // ---- this wave's two N-tiles
-  int nt_t0[2], nt_hq[2], pos0[2], phi[2];
-  bool nt_valid[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int n = tg * NT_WG + wave * 2 + i;
-    nt_valid[i] = n < n_ntiles;
-    const int pb = fast_div(n, a.div_g);
-    nt_t0[i] = pb * 32;
-    nt_hq[i] = g * G + (n - pb * G);
-    pos0[i] = pos_off + nt_t0[i];
-    phi[i] = pos_off + min(nt_t0[i] + 31, sv.q_len - 1);
-  }
-
-  // ---- key range of the whole workgroup
-  const int n_last = min(tg * NT_WG + NT_WG - 1, n_ntiles - 1);
-  const int t_min = fast_div(tg * NT_WG, a.div_g) * 32;
+  // ---- key range of the whole job
+  const int n_last = min(tg_hi * NT_WG + NT_WG - 1, n_ntiles - 1);
+  const int t_min = fast_div(tg_lo * NT_WG, a.div_g) * 32;
   const int t_max = min(fast_div(n_last, a.div_g) * 32 + 31, sv.q_len - 1);
   const int p_min = pos_off + t_min;
   const int p_max = pos_off + t_max;
@@ -299,38 +293,6 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
   const int n_st = STK ? (min(st, j_begin) + BK - 1) / BK : 0;
   const int n_tiles = n_st + (hi >= j_begin ? (hi - j_begin) / BK + 1 : 0);
   auto tile_j0 = [&](int t) { return t < n_st ? BK * t : j_begin + BK * (t - n_st); };
-
-  // ---- Q^T operands (B of S^T = K Q^T): lane holds row lr, d = 16*k + 8*lg .. +7
-  // (addresses: the N-tile's first row as a scalar base, a 32-bit lane offset)
-  // Unconditional loads: a row past the end reads the sequence's last row (its
-  // head is valid; its results are never stored).  Without branches around
-  // the loads the compiler keeps each operand where its load puts it, so
-  // nothing waits for them before their first use (the rotation, or the first
-  // scores).  The N-tile's first row is a scalar base, the lane's row a 32-bit
-  // offset.
-  bf16x8 qb[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int t0 = min(nt_t0[i], sv.q_len - 1);
-    const int r = min(nt_t0[i] + lr, sv.q_len - 1) - t0;  // 0 .. 31
-    const char* qt = reinterpret_cast<const char*>(a.q + ((sv.q_row0 + t0) * a.Hq + nt_hq[i]) * (int64_t)kHeadDim);
-    const uint32_t qo = (uint32_t)(r * a.Hq * kHeadDim + 8 * lg) * 2u;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      qb[i][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qt + qo + 32 * k));
-  }
-  float m_run[2], l_run[2];
-  f32x16 o[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const float s2 = a.sinks ? a.sinks[nt_hq[i]] * kLog2e : -INFINITY;
-    const bool none = (s2 == -INFINITY);
-    m_run[i] = none ? kNegBig : s2;
-    // the sink's own term e^{s-m} = 1 at m = s; only one lane of the pair carries it
-    l_run[i] = (none || lg) ? 0.f : 1.f;
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt) o[i][dt] = zero16();
-  }
 
   // ---- global -> LDS staging with 16-byte direct loads: wave w fills rows
   // 16w .. 16w+15 of a tile, 8 rows per instruction.  With a paged cache the
@@ -411,6 +373,66 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
   int vofs[2];
   tr_offsets(lane, vofs);
 
+  // ---- Q^T operands (B of S^T = K Q^T) of tile group tg's N-tiles: lane holds
+  // row lr, d = 16*k + 8*lg .. +7.  Unconditional loads: a row past the end
+  // reads the sequence's last row (its head is valid; its results are never
+  // stored).  Without branches around the loads the compiler keeps each
+  // operand where its load puts it, so nothing waits for them before their
+  // first use (the rotation, or the first scores).  The N-tile's first row is
+  // a scalar base, the lane's row a 32-bit offset.
+  bf16x8 qb[2][4];
+  auto load_q = [&](int tg_q) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int n = tg_q * NT_WG + wave * 2 + i;
+      const int pb = fast_div(n, a.div_g);
+      const int t0 = min(pb * 32, sv.q_len - 1);
+      const int r = min(pb * 32 + lr, sv.q_len - 1) - t0;  // 0 .. 31
+      const int hq = g * G + (n - pb * G);
+      const char* qt = reinterpret_cast<const char*>(a.q + ((sv.q_row0 + t0) * a.Hq + hq) * (int64_t)kHeadDim);
+      const uint32_t qo = (uint32_t)(r * a.Hq * kHeadDim + 8 * lg) * 2u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        qb[i][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qt + qo + 32 * k));
+    }
+  };
+  load_q(tg_hi);
+
+  const int n_steps = tg_hi - tg_lo + 1;
+  // (unrolled: each step's code knows whether it loads tiles)
+#pragma unroll
+  for (int step = 0; step < (TWO ? 2 : 1); ++step) {
+  if (step >= n_steps) break;  // uniform
+  const int tg = tg_hi - step;
+
+  // ---- this wave's two N-tiles
+  int nt_t0[2], nt_hq[2], pos0[2], phi[2];
+  bool nt_valid[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int n = tg * NT_WG + wave * 2 + i;
+    nt_valid[i] = n < n_ntiles;
+    const int pb = fast_div(n, a.div_g);
+    nt_t0[i] = pb * 32;
+    nt_hq[i] = g * G + (n - pb * G);
+    pos0[i] = pos_off + nt_t0[i];
+    phi[i] = pos_off + min(nt_t0[i] + 31, sv.q_len - 1);
+  }
+
+  float m_run[2], l_run[2];
+  f32x16 o[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float s2 = a.sinks ? a.sinks[nt_hq[i]] * kLog2e : -INFINITY;
+    const bool none = (s2 == -INFINITY);
+    m_run[i] = none ? kNegBig : s2;
+    // the sink's own term e^{s-m} = 1 at m = s; only one lane of the pair carries it
+    l_run[i] = (none || lg) ? 0.f : 1.f;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) o[i][dt] = zero16();
+  }
+
+
   // Tile t runs in three phases, each pairing vector work with independent
   // matrix work so that both units stay busy within the wave:
   //   (a) weights of key half 0          | scores of key half 1
@@ -424,7 +446,7 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
   f32x16 sA[2], sB[2];  // scores of key halves 0 and 1, per N-tile
   int blk_next[2];      // block ids of the next tile to load
   if (n_tiles > 0) {
-    {
+    if (step == 0) {
       int blk0[2];
       fetch_blk(0, blk0);
       dma_tile(0, blk0, 0);
@@ -442,8 +464,10 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
       if (nt_t0[1] != nt_t0[0]) rope_angles<ROPE - 1>(a, f, pos0[1] + lr, cs, sn);
       rope_rotate_q<ROPE - 1>(qb[1], cs, sn);
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
+    if (step == 0) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+    }
     qk_half(sA[0], sA[1], Ks[0], qb, 0, lr, lg);
     int cur = 0;
     auto body = [&](auto mask_tag, int t) {
@@ -535,11 +559,13 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
       }
       l_run[0] += r0;
       l_run[1] += r1;
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's loads of tile t+1 have landed
-      __syncthreads();
+      if (step == 0) {  // a later step finds every tile in LDS
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's loads of tile t+1 have landed
+        __syncthreads();
+      }
       if (W == 0) __builtin_amdgcn_s_setprio(0);
       // (c)
-      if (t + 2 < n_tiles) dma_tile(t + 2, blk_next, nxt == NBUF - 1 ? 0 : nxt + 1);
+      if (step == 0 && t + 2 < n_tiles) dma_tile(t + 2, blk_next, nxt == NBUF - 1 ? 0 : nxt + 1);
       fetch_blk(t + 3, blk_next);
       pv_half(o, Vs[cur], pB0, pB1, 1, vofs);
       if (has_next) qk_half(sA[0], sA[1], Ks[nxt], qb, 0, lr, lg);
@@ -558,10 +584,18 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
     const int pe = max(pb, n_st + min(t_hi + 1, n_wt));
     std::true_type MSK;
     std::false_type PLN;
-    for (int t = 0; t < pb; ++t) body(MSK, t);
-    for (int t = pb; t < pe; ++t) body(PLN, t);
-    for (int t = pe; t < n_tiles; ++t) body(MSK, t);
+    if (TWO) {
+      // at most NBUF tiles, mostly edges: one (masked) body keeps the code of
+      // both steps within the instruction cache
+      for (int t = 0; t < n_tiles; ++t) body(MSK, t);
+    } else {
+      for (int t = 0; t < pb; ++t) body(MSK, t);
+      for (int t = pb; t < pe; ++t) body(PLN, t);
+      for (int t = pe; t < n_tiles; ++t) body(MSK, t);
+    }
   }
+  // the next step's queries load while this step's output goes out
+  if (TWO && step + 1 < n_steps) load_q(tg_hi - step - 1);
 
   // ---- epilogue: normalise, round to bf16, log-sum-exp.  A lane's registers
   // hold 4-element pieces of 32 different rows, so the output tile goes
@@ -572,61 +606,83 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
   // (it would spill it).
   int lr_e = lr;
   asm volatile("" : "+v"(lr_e));
-  __syncthreads();  // every wave is done with the K/V tiles
-  __bf16* stg = wave < NBUF ? Ks[wave] : Vs[0];  // this wave's 64 rows: [N-tile][row][64]
+  // The wave's rows go through LDS: all 64 ([N-tile][row][64]) in a free K/V
+  // buffer once every wave is done with the tiles, or (two steps: the tiles
+  // stay) one N-tile at a time through the wave's own 32-row slice.
+  constexpr int NP = TWO ? 1 : 2;  // N-tiles per staging pass
+  __bf16* stg;
+  if (TWO) {
+    stg = Stg + wave * 32 * RS;
+  } else {
+    __syncthreads();
+    stg = wave < NBUF ? Ks[wave] : Vs[0];
+  }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[i]), __float_as_uint(l_run[i]), false, false);
-    const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const float inv = lt > 0.f ? 1.f / lt : (lt == 0.f ? 0.f : lt);
-    const int row = 32 * i + lr_e;
+  for (int ps = 0; ps < 2 / NP; ++ps) {
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
+    for (int ii = 0; ii < NP; ++ii) {
+      const int i = ps * NP + ii;
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[i]), __float_as_uint(l_run[i]), false, false);
+      const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      const float inv = lt > 0.f ? 1.f / lt : (lt == 0.f ? 0.f : lt);
+      const int row = 32 * ii + lr_e;
 #pragma unroll
-      for (int cq = 0; cq < 4; ++cq) {
-        u32x2 v;
-        v[0] = pack_bf16x2(o[i][dt][4 * cq + 0] * inv, o[i][dt][4 * cq + 1] * inv);
-        v[1] = pack_bf16x2(o[i][dt][4 * cq + 2] * inv, o[i][dt][4 * cq + 3] * inv);
-        *reinterpret_cast<u32x2*>(stg + row * RS + kchunk(4 * dt + cq, row) + 4 * lg) = v;  // d = 32dt + 8cq + 4lg
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int cq = 0; cq < 4; ++cq) {
+          u32x2 v;
+          v[0] = pack_bf16x2(o[i][dt][4 * cq + 0] * inv, o[i][dt][4 * cq + 1] * inv);
+          v[1] = pack_bf16x2(o[i][dt][4 * cq + 2] * inv, o[i][dt][4 * cq + 3] * inv);
+          *reinterpret_cast<u32x2*>(stg + row * RS + kchunk(4 * dt + cq, row) + 4 * lg) = v;  // d = 32dt + 8cq + 4lg
+        }
+      const int t = nt_t0[i] + lr_e;
+      if (nt_valid[i] && t < sv.q_len && a.lse && lg == 0) {
+        const float v = (lt == 0.f) ? -INFINITY : (m_run[i] + __log2f(lt)) * kLn2;
+        const int64_t idx = (int64_t)b * a.lse_sb + (int64_t)nt_hq[i] * a.lse_sh + t + (a.lse_row0 ? sv.q_row0 : 0);
+        a.lse[idx] = v;
       }
-    const int t = nt_t0[i] + lr_e;
-    if (nt_valid[i] && t < sv.q_len && a.lse && lg == 0) {
-      const float v = (lt == 0.f) ? -INFINITY : (m_run[i] + __log2f(lt)) * kLn2;
-      const int64_t idx = (int64_t)b * a.lse_sb + (int64_t)nt_hq[i] * a.lse_sh + t + (a.lse_row0 ? sv.q_row0 : 0);
-      a.lse[idx] = v;
+    }
+    wave_lds_sync();  // the wave reads back only its own rows
+    // rows 8j .. 8j+7 of the staged ones: N-tile j / 4 of the pass, row
+    // (lane / 8) + 8 (j % 4) of it, 16-byte chunk lane % 8
+    u32x4 ov[4 * NP];
+#pragma unroll
+    for (int j = 0; j < 4 * NP; ++j) {
+      const int r = (lane >> 3) + 8 * (j & 3);
+      ov[j] = *reinterpret_cast<const u32x4*>(stg + (32 * (j >> 2) + r) * RS + kchunk(lane & 7, r));
+    }
+    if (TWO) wave_lds_sync();  // read back before the next pass writes the slice
+    auto store = [&](int j) {
+      const int i = ps * NP + (j >> 2);
+      const int r = (lane >> 3) + 8 * (j & 3);
+      char* ot = reinterpret_cast<char*>(a.out + ((sv.q_row0 + nt_t0[i]) * a.Hq + nt_hq[i]) * (int64_t)kHeadDim);
+      *reinterpret_cast<u32x4*>(ot + (uint32_t)(r * a.Hq * kHeadDim + 8 * (lane & 7)) * 2u) = ov[j];
+    };
+    // the pass's N-tiles whole (every tile but a sequence's last): no per-row tests
+    bool whole = true;
+#pragma unroll
+    for (int ii = 0; ii < NP; ++ii) whole = whole && nt_valid[ps * NP + ii] && nt_t0[ps * NP + ii] + 31 < sv.q_len;
+    if (whole) {
+#pragma unroll
+      for (int j = 0; j < 4 * NP; ++j) store(j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4 * NP; ++j) {
+        const int i = ps * NP + (j >> 2);
+        if (nt_valid[i] && nt_t0[i] + (lane >> 3) + 8 * (j & 3) < sv.q_len) store(j);
+      }
     }
   }
-  wave_lds_sync();  // the wave reads back only its own rows
-  // rows 8j .. 8j+7 of the wave's 64: N-tile j / 4, row (lane / 8) + 8 (j % 4)
-  // of it, 16-byte chunk lane % 8
-  u32x4 ov[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = (lane >> 3) + 8 * (j & 3);
-    ov[j] = *reinterpret_cast<const u32x4*>(stg + (32 * (j >> 2) + r) * RS + kchunk(lane & 7, r));
-  }
-  auto store = [&](int j) {
-    const int i = j >> 2;
-    const int r = (lane >> 3) + 8 * (j & 3);
-    char* ot = reinterpret_cast<char*>(a.out + ((sv.q_row0 + nt_t0[i]) * a.Hq + nt_hq[i]) * (int64_t)kHeadDim);
-    *reinterpret_cast<u32x4*>(ot + (uint32_t)(r * a.Hq * kHeadDim + 8 * (lane & 7)) * 2u) = ov[j];
-  };
-  // Both N-tiles whole (every tile but a sequence's last): no per-row tests.
-  const bool whole = nt_valid[0] && nt_valid[1] && max(nt_t0[0], nt_t0[1]) + 31 < sv.q_len;
-  if (whole) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) store(j);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (nt_valid[j >> 2] && nt_t0[j >> 2] + (lane >> 3) + 8 * (j & 3) < sv.q_len) store(j);
-  }
+  }  // step
 }
 
-template <int MODE, bool VARLEN, bool STK, int ROPE = 0>
+template <int MODE, bool VARLEN, bool STK, int ROPE = 0, bool TWO = false>
 __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 Ks[NBUF][BK * RS];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[NBUF][BK * RS];
+  // output staging of two-step jobs: 4 waves x 32 rows (so that two
+  // workgroups' LDS fits a CU with room to spare)
+  __shared__ __attribute__((aligned(16))) __bf16 Stg[TWO ? 4 * 32 * RS : 8];
   const int* order = nullptr;
   if constexpr (VARLEN) {
     // Ragged batches: the sequences' tile groups carry work in proportion to
@@ -658,7 +714,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
       order = seq_order;
     }
   }
-  prefill_job<MODE, VARLEN, STK, ROPE>(a, blockIdx.x, Ks, Vs, order);  // one call site: inlined once
+  prefill_job<MODE, VARLEN, STK, ROPE, TWO>(a, blockIdx.x, Ks, Vs, Stg, order);  // one call site: inlined once
 }
 
 }  // namespace
@@ -666,10 +722,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
 int prefill_ntiles_per_wg() { return NT_WG; }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& args, int kv_mode, bool varlen_q, hipStream_t s) {
-  const int grid = args.B * args.Hkv * args.wg_per_seq;
+  const bool two = kv_mode == KV_BATCHED && !varlen_q && args.two_step && !(args.window > 0 && args.sink_tokens > 0);
+  const int wg_per_job = two ? (args.wg_per_seq + 1) / 2 : args.wg_per_seq;
+  const int grid = args.B * args.Hkv * wg_per_job;
   if (grid <= 0) return hipSuccess;
   PrefillArgs a = args;
-  a.div_wg_per_seq = make_fastdiv(a.wg_per_seq);
+  a.two_step = two;
+  a.wg_per_job = wg_per_job;
+  a.div_wg_per_job = make_fastdiv(wg_per_job);
   a.div_hkv = make_fastdiv(a.Hkv);
   a.div_g = make_fastdiv(a.G);
   a.div_units = make_fastdiv(a.B * a.Hkv);
@@ -679,6 +739,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& args, int kv_mode, bool varlen
 #define GQA_ROPE_LAUNCH(R)                                                                                          \
   do {                                                                                                              \
     if (stk) hipLaunchKernelGGL((prefill_bf16_kernel<KV_BATCHED, false, true, R>), dim3(grid), dim3(NTHREADS), 0, s, a); \
+    else if (two) hipLaunchKernelGGL((prefill_bf16_kernel<KV_BATCHED, false, false, R, true>), dim3(grid), dim3(NTHREADS), 0, s, a); \
     else hipLaunchKernelGGL((prefill_bf16_kernel<KV_BATCHED, false, false, R>), dim3(grid), dim3(NTHREADS), 0, s, a);    \
   } while (0)
     if (a.rope == 1) GQA_ROPE_LAUNCH(1);
@@ -691,7 +752,9 @@ hipError_t launch_prefill_bf16(const PrefillArgs& args, int kv_mode, bool varlen
     if (stk) hipLaunchKernelGGL((prefill_bf16_kernel<M, V, true>), dim3(grid), dim3(NTHREADS), 0, s, a); \
     else hipLaunchKernelGGL((prefill_bf16_kernel<M, V, false>), dim3(grid), dim3(NTHREADS), 0, s, a);    \
   } while (0)
-  if (!varlen_q && kv_mode == KV_BATCHED)
+  if (!varlen_q && kv_mode == KV_BATCHED && two)
+    hipLaunchKernelGGL((prefill_bf16_kernel<KV_BATCHED, false, false, 0, true>), dim3(grid), dim3(NTHREADS), 0, s, a);
+  else if (!varlen_q && kv_mode == KV_BATCHED)
     GQA_LAUNCH(KV_BATCHED, false);
   else if (varlen_q && kv_mode == KV_PAGED)
     GQA_LAUNCH(KV_PAGED, true);

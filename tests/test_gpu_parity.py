@@ -45,6 +45,8 @@ PREFILL_CASES = [
     (1, 77, 32, 2, 0, "normal"),
     (1, 300, 8, 1, 64, "normal"),
     (3, 65, 64, 8, 0, "normal"),
+    (1, 333, 64, 4, 128, "normal"),  # G = 16, windowed: two tile groups per workgroup
+    (1, 190, 32, 1, 100, "none"),    # G = 32, windowed, no sink
 ]
 
 
@@ -59,6 +61,22 @@ def test_prefill_bf16_small(device, B, S, Hq, Hkv, W, sk):
     o_ref, l_ref = oracle.prefill_ref(p.q.f64, p.k.f64, p.v.f64, p.sinks, W, p.scale)
     assert_bf16_close(to_f64(out), o_ref, "out")
     assert_lse_close(to_f64(lse), l_ref, "lse")
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,W", [(1, 257, 64, 8, 128), (2, 200, 64, 8, 16), (1, 333, 64, 4, 128),
+                                        (1, 4096, 64, 8, 128)])
+def test_prefill_two_step_equals_one_step(device, monkeypatch, B, S, Hq, Hkv, W):
+    # windowed whole-sequence layers run two tile groups per workgroup over the
+    # same key tiles; the result is the one-group-per-workgroup kernel's, bit for bit
+    p = gi.prefill_problem(2100 + S + W, B, S, Hq, Hkv, 64, "bf16", std=SQRT_HALF)
+    args = (dev_tensor(p.q, device), dev_tensor(p.k, device), dev_tensor(p.v, device), dev_f32(p.sinks, device))
+    say(f"prefill two tile groups per workgroup vs one: B={B} S={S} Hq={Hq} Hkv={Hkv} W={W}")
+    res = {}
+    for flag in ("0", "1"):
+        monkeypatch.setenv("GQA_PREFILL_TWO_STEP", flag)
+        res[flag] = gq.attn_prefill(*args, window=W, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(res["0"][0], res["1"][0]) and torch.equal(res["0"][1], res["1"][1])
 
 
 def test_prefill_bf16_window_covering_sequence_equals_dense(device):

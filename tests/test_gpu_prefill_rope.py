@@ -75,7 +75,7 @@ def test_window_sink_tokens():
 
 
 @pytest.mark.parametrize("Hq,Hkv,S,W,pairing", [(12, 4, 333, 0, 1), (8, 8, 200, 64, 0), (16, 4, 517, 0, 0),
-                                                (24, 8, 130, 0, 0)])
+                                                (24, 8, 130, 0, 0), (64, 8, 300, 128, 0), (64, 4, 200, 100, 1)])
 def test_group_sizes(Hq, Hkv, S, W, pairing):
     run_case(103, 2, S, Hq, Hkv, window=W, pairing=pairing)
 
