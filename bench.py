@@ -188,7 +188,7 @@ def summarize_counters(fetch_dir, write_dir):
     w_scale = (w_copy * 1024.0) / COPY_BYTES
     res = {}
     # the dense B1 S4096 prefill: one job per workgroup, batched keys, no sink tokens, queries already rotated
-    for kind, key, work in (("prefill", "prefill_bf16_kernel<0, false, false, 0>", prefill_work(1, 4096, 64, 8, 64, 0)),
+    for kind, key, work in (("prefill", "prefill_bf16_kernel<0, false, false, 0, false>", prefill_work(1, 4096, 64, 8, 64, 0)),
                             ("decode", "decode_rows_kernel", decode_work([8192] * 64, 64, 8, 64, 0))):
         fk, wk = pick(fetch, key), pick(write, key)
         rd = fk * 1024.0 / f_scale
