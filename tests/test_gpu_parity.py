@@ -79,6 +79,29 @@ def test_prefill_two_step_equals_one_step(device, monkeypatch, B, S, Hq, Hkv, W)
     assert torch.equal(res["0"][0], res["1"][0]) and torch.equal(res["0"][1], res["1"][1])
 
 
+def test_prefill_two_step_random_shapes(device, monkeypatch):
+    # two tile groups per workgroup wherever the launcher allows it (forced past the
+    # one-round rule): random lengths, windows up to 128 and G = 8, 16, 32 keep every
+    # job within the three key tiles held in LDS, so the result is the one-group
+    # kernel's, bit for bit
+    rng = np.random.default_rng(2200)
+    for case in range(12):
+        G = int(rng.choice([8, 16, 32]))
+        Hkv = int(rng.choice([1, 2]))
+        B = int(rng.integers(1, 3))
+        S = int(rng.integers(1, 700))
+        W = int(rng.integers(1, 129))
+        p = gi.prefill_problem(2200 + case, B, S, G * Hkv, Hkv, 64, "bf16", std=SQRT_HALF)
+        args = (dev_tensor(p.q, device), dev_tensor(p.k, device), dev_tensor(p.v, device), dev_f32(p.sinks, device))
+        say(f"two-step random case {case}: B={B} S={S} G={G} Hkv={Hkv} W={W}")
+        res = {}
+        for flag in ("0", "2"):
+            monkeypatch.setenv("GQA_PREFILL_TWO_STEP", flag)
+            res[flag] = gq.attn_prefill(*args, window=W, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(res["0"][0], res["2"][0]) and torch.equal(res["0"][1], res["2"][1]), (B, S, G, Hkv, W)
+
+
 def test_prefill_bf16_window_covering_sequence_equals_dense(device):
     p = gi.prefill_problem(2001, 1, 200, 64, 8, 64, "bf16", std=SQRT_HALF)
     args = (dev_tensor(p.q, device), dev_tensor(p.k, device), dev_tensor(p.v, device), dev_f32(p.sinks, device))
