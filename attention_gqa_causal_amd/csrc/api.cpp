@@ -243,10 +243,13 @@ int prefill_call(const void* q, const void* k, const void* v, const float* sinks
   // when that turns two rounds of workgroups (two resident per CU) into one;
   // with more rounds the finer jobs balance better (measured: S4096 -7 %,
   // S32768 +5 % with two steps).
-  // (GQA_PREFILL_TWO_STEP: 0 never, 1 as above, 2 whenever the tiles fit)
+  // (GQA_PREFILL_TWO_STEP: 0 never, 1 as above, 2 on every windowed layer
+  // without sink tokens: where the tiles do not fit, the second step streams
+  // them again)
   const int two_env = env_int("GQA_PREFILL_TWO_STEP", 1);
-  a.two_step = window > 0 && window <= 128 && sink_tokens == 0 && (G == 8 || G % 16 == 0) &&
-               (two_env == 2 || (two_env == 1 && (long long)B * Hkv * a.wg_per_seq <= 4LL * num_cus()));
+  a.two_step = window > 0 && sink_tokens == 0 &&
+               (two_env == 2 || (two_env == 1 && window <= 128 && (G == 8 || G % 16 == 0) &&
+                                 (long long)B * Hkv * a.wg_per_seq <= 4LL * num_cus()));
   hipError_t e = launch_prefill_bf16(a, KV_BATCHED, false, st);
   return e == hipSuccess ? ok() : hip_fail(e, "prefill bf16 launch");
 }

@@ -445,8 +445,13 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
   // every wave finished reading before the barrier of tile t.
   f32x16 sA[2], sB[2];  // scores of key halves 0 and 1, per N-tile
   int blk_next[2];      // block ids of the next tile to load
+  // A later step finds every tile in LDS when the job's tiles fit the buffers
+  // (the launcher asks for two steps only then); otherwise it streams them
+  // again, once every wave is done with the previous step's.
+  const bool load = step == 0 || n_tiles > NBUF;
   if (n_tiles > 0) {
-    if (step == 0) {
+    if (load) {
+      if (step > 0) __syncthreads();
       int blk0[2];
       fetch_blk(0, blk0);
       dma_tile(0, blk0, 0);
@@ -464,7 +469,7 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
       if (nt_t0[1] != nt_t0[0]) rope_angles<ROPE - 1>(a, f, pos0[1] + lr, cs, sn);
       rope_rotate_q<ROPE - 1>(qb[1], cs, sn);
     }
-    if (step == 0) {
+    if (load) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
     }
@@ -559,13 +564,13 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
       }
       l_run[0] += r0;
       l_run[1] += r1;
-      if (step == 0) {  // a later step finds every tile in LDS
+      if (load) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's loads of tile t+1 have landed
         __syncthreads();
       }
       if (W == 0) __builtin_amdgcn_s_setprio(0);
       // (c)
-      if (step == 0 && t + 2 < n_tiles) dma_tile(t + 2, blk_next, nxt == NBUF - 1 ? 0 : nxt + 1);
+      if (load && t + 2 < n_tiles) dma_tile(t + 2, blk_next, nxt == NBUF - 1 ? 0 : nxt + 1);
       fetch_blk(t + 3, blk_next);
       pv_half(o, Vs[cur], pB0, pB1, 1, vofs);
       if (has_next) qk_half(sA[0], sA[1], Ks[nxt], qb, 0, lr, lg);
