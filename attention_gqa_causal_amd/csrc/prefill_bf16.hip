@@ -11,7 +11,9 @@
 // "N-tiles"; an N-tile is 32 query positions of one query head of g's group.
 // For the 64/8 head layout that is all 8 heads of the group at 32 positions, so
 // every K/V tile staged in LDS is used by the whole group.  Each of the 4 waves
-// owns two N-tiles (64 query rows); two workgroups share a CU.
+// owns two N-tiles (64 query rows); two workgroups share a CU.  On windowed
+// layers, where a tile group is a short job of a few tiles, a workgroup may run
+// two adjacent tile groups in turn over the same tiles (see prefill_job).
 //
 // The scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 // A = rows of the K tile (keys) from LDS, B = Q^T held in registers.  In the
@@ -245,10 +247,11 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
   // (divisions by the launch's divisors use the launcher's multipliers: a
   // division sequence per job is a good part of a short job's setup)
   //
-  // A job is one tile group, or (two_step: windowed whole-sequence layers
-  // whose tile groups 2r and 2r+1 need at most NBUF key tiles together) those
-  // two in turn over the same tiles in LDS: the second step loads no tile and
-  // repeats none of the job's setup.
+  // A job is one tile group or (TWO: windowed whole-sequence layers) the two
+  // tile groups 2r+1 and 2r in turn.  When the job's key tiles fit the NBUF
+  // buffers (the launcher asks for two steps only then, unless forced) the
+  // second step reuses them: it loads no tile and repeats none of the job's
+  // setup.
   const int U = a.B * a.Hkv;
   int unit, rank;
   {
@@ -263,9 +266,8 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
     }
   }
   const int jr = a.wg_per_job - 1 - rank;
-  constexpr bool two = TWO;
-  const int tg_hi = two ? min(2 * jr + 1, a.wg_per_seq - 1) : jr;  // steps run tg_hi down to tg_lo
-  const int tg_lo = two ? 2 * jr : jr;
+  const int tg_hi = TWO ? min(2 * jr + 1, a.wg_per_seq - 1) : jr;  // steps run tg_hi down to tg_lo
+  const int tg_lo = TWO ? 2 * jr : jr;
   const int uq = fast_div(unit, a.div_hkv);
   const int g = unit - uq * a.Hkv;
   const int b = order ? order[uq] : uq;  // ragged batches: longest sequences first
