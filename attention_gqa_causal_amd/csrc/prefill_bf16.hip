@@ -401,7 +401,8 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
   load_q(tg_hi);
 
   const int n_steps = tg_hi - tg_lo + 1;
-  // (unrolled: each step's code knows whether it loads tiles)
+  // (unrolled, so that each step's code is specialised for it; the two-step
+  // kernel has one tile loop per step to stay within the instruction cache)
 #pragma unroll
   for (int step = 0; step < (TWO ? 2 : 1); ++step) {
   if (step >= n_steps) break;  // uniform
