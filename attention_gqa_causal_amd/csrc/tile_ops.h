@@ -121,17 +121,17 @@ __device__ __forceinline__ void mask_half(f32x16& s, int h, int j0, int plo, int
   }
 }
 
-// 16-byte global-to-LDS load (lane i lands at byte 16 i past lds_dst, which
-// must be wave-uniform), issued from inline asm.  The compiler, seeing an LDS
-// write in flight, would make every later LDS read wait for it, even reads of
-// another buffer; the tile loops instead wait for these loads themselves
-// (s_waitcnt vmcnt, then a barrier) before any wave reads the buffer they fill.
-// M0 takes the LDS address (one wait state before the load) and gets its old
-// value back afterwards (one wait state after), since the compiler does not
-// track M0 across asm; the
-// leading s_nop covers a base address just written to SGPRs by a vector
-// instruction (five wait states).  Base and LDS address go through
-// readfirstlane, so they are scalar operands whatever the compiler proved.
+// Direct global-to-LDS loads (lane i's 16 or 4 bytes land at byte 16 i or 4 i
+// past the LDS address, which must be wave-uniform), issued from inline asm.
+// The compiler, seeing an LDS write in flight, would make every later LDS read
+// wait for it, even reads of another buffer; the tile loops instead wait for
+// these loads themselves (s_waitcnt vmcnt, then a barrier) before any wave
+// reads the buffer they fill.  M0 takes each LDS address (one wait state
+// before the load) and gets its old value back afterwards (one wait state
+// after), since the compiler does not track M0 across asm; the leading s_nop
+// covers a base address just written to SGPRs by a vector instruction (five
+// wait states).  Bases and LDS addresses go through readfirstlane, so they are
+// scalar operands whatever the compiler proved.
 __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
@@ -141,16 +141,7 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 __device__ __forceinline__ uint32_t lds_addr(lds_void* p) {
   return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
 }
-__device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, lds_void* lds_dst) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_nop 4\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0\n\ts_nop 0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(uniform_ptr(gbase)), "s"(lds_addr(lds_dst))
-      : "memory");
-}
-// 4-byte form (lane i lands at byte 4 i past lds_dst), same contract.
+// 4-byte loads from gbase + voff.
 __device__ __forceinline__ void dma4(const char* gbase, uint32_t voff, lds_void* lds_dst) {
   uint32_t saved;
   asm volatile(
@@ -160,21 +151,10 @@ __device__ __forceinline__ void dma4(const char* gbase, uint32_t voff, lds_void*
       : "v"(voff), "s"(uniform_ptr(gbase)), "s"(lds_addr(lds_dst))
       : "memory");
 }
-// 16-byte form with a 64-bit per-lane address (no scalar base).
-__device__ __forceinline__ void dma16(const void* gaddr, lds_void* lds_dst) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0\n\ts_nop 0"
-      : "=&s"(saved)
-      : "v"(gaddr), "s"(lds_addr(lds_dst))
-      : "memory");
-}
 
 // The K and V halves of a wave's share of a tile: four 16-byte loads (K rows
 // at voff0 and voff1 past kbase, V rows at the same offsets past vbase) under
-// one save and restore of M0, same contract as dma16.  lds_k0 .. lds_v1 are
-// LDS byte addresses.
+// one save and restore of M0.  lds_k0 .. lds_v1 are LDS byte addresses.
 __device__ __forceinline__ void dma16_kv(const char* kbase, const char* vbase, uint32_t voff0, uint32_t voff1,
                                          uint32_t lds_k0, uint32_t lds_k1, uint32_t lds_v0, uint32_t lds_v1) {
   uint32_t saved;
