@@ -79,3 +79,47 @@ def test_decode_step_and_noalloc_decode_in_a_graph():
                                               vc0.f64, R.CACHE_CONTIGUOUS, cache_len=Lc)
     o_ref, _ = oracle.decode_ref(q_ref, kc_ref, vc_ref, seqlens_np, sinks_np, 128, 1.0 / 8.0)
     assert_bf16_close(to_f64(o_step), o_ref, "graph-replayed decode step vs oracle")
+
+
+def test_mixed_varlen_call_in_a_graph():
+    # A ragged batch of prefill chunks and decode rows (two launches, the decode
+    # split kernel with its combine) captured as one graph.
+    kv, ql = [300, 1, 700, 129, 2000, 1, 64, 5], [64, 1, 100, 1, 33, 1, 64, 5]
+    p = gi.varlen_problem(130, kv, ql, 64, 8, 64, block_size=16, dtype="bf16")
+    q = dev_tensor(p.q, "cuda")
+    cache = (dev_tensor(p.k, "cuda"), dev_tensor(p.v, "cuda"))
+    bt, cu, sk = dev_i32(p.block_table, "cuda"), dev_i32(p.cu_seqlens_q, "cuda"), dev_i32(p.seqlens_k, "cuda")
+    sinks = dev_f32(p.sinks, "cuda")
+    B = len(kv)
+    ws = torch.empty((gq.varlen_workspace_size(B, p.max_q_len, p.max_kv_len, 64, 8),), dtype=torch.uint8,
+                     device="cuda")
+
+    def call(out):
+        return gq.attn_varlen_paged(q, cache, bt, cu, sk, sinks, window=0, max_q_len=p.max_q_len,
+                                    max_kv_len=p.max_kv_len, workspace=ws, out=out)
+
+    say("graph: mixed varlen eager")
+    o_eager = call(torch.empty_like(q))
+    torch.cuda.synchronize()
+    o = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(o)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say("graph: mixed varlen capture")
+    with torch.cuda.graph(g):
+        call(o)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        o.fill_(0)
+        torch.cuda.synchronize()
+        say(f"graph: mixed varlen replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_eager.view(torch.int16)), f"replay {rep}"
+    o_ref, _ = oracle.varlen_ref(p.q.f64, p.k.f64, p.v.f64, p.cu_seqlens_q, p.seqlens_k, p.sinks, 0, p.scale,
+                                 block_table=p.block_table, block_size=p.block_size)
+    assert_bf16_close(to_f64(o), o_ref, "graph-replayed mixed varlen vs oracle")
