@@ -82,8 +82,8 @@ def test_decode_step_and_noalloc_decode_in_a_graph():
 
 
 def test_mixed_varlen_call_in_a_graph():
-    # A ragged batch of prefill chunks and decode rows (two launches, the decode
-    # split kernel with its combine) captured as one graph.
+    # A ragged batch of prefill chunks and decode rows (a prefill launch and a
+    # decode launch) captured as one graph.
     kv, ql = [300, 1, 700, 129, 2000, 1, 64, 5], [64, 1, 100, 1, 33, 1, 64, 5]
     p = gi.varlen_problem(130, kv, ql, 64, 8, 64, block_size=16, dtype="bf16")
     q = dev_tensor(p.q, "cuda")
