@@ -547,15 +547,36 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
     row0 = r0;
   }
   const int64_t base = ((int64_t)b * a.Hq + hq) * a.n_splits;
+  const int ns = a.n_splits;
   const float s2 = a.sinks ? a.sinks[hq] * kLog2e : -INFINITY;
   float M = s2;
-  for (int s = lane; s < a.n_splits; s += 64) M = fmaxf(M, a.ws_ml[(base + s) * 2]);
-  M = wave_max(M);
   float Z = 0.f;
-  for (int s = lane; s < a.n_splits; s += 64) Z += a.ws_ml[(base + s) * 2 + 1] * fast_exp2(a.ws_ml[(base + s) * 2] - M);
-  Z = wave_sum(Z) + fast_exp2(s2 - M);
   float acc = 0.f;
-  for (int s = 0; s < a.n_splits; ++s) acc += a.ws_acc[(base + s) * kHeadDim + lane] * fast_exp2(a.ws_ml[(base + s) * 2] - M);
+  if (ns <= 8) {
+    // one trip to memory: every split's (m, l) and partial row are loaded
+    // before any of them is used; lane s holds split s's (m, l), and the
+    // weights reach every lane by readlane
+    float m_s = -INFINITY, l_s = 0.f;
+    if (lane < ns) {
+      m_s = a.ws_ml[(base + lane) * 2];
+      l_s = a.ws_ml[(base + lane) * 2 + 1];
+    }
+    float x[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) x[s] = s < ns ? a.ws_acc[(base + s) * kHeadDim + lane] : 0.f;
+    M = wave_max(fmaxf(M, m_s));
+    const float w_s = lane < ns ? fast_exp2(m_s - M) : 0.f;
+    Z = wave_sum(l_s * w_s) + fast_exp2(s2 - M);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s < ns) acc += x[s] * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_s), s));
+  } else {
+    for (int s = lane; s < ns; s += 64) M = fmaxf(M, a.ws_ml[(base + s) * 2]);
+    M = wave_max(M);
+    for (int s = lane; s < ns; s += 64) Z += a.ws_ml[(base + s) * 2 + 1] * fast_exp2(a.ws_ml[(base + s) * 2] - M);
+    Z = wave_sum(Z) + fast_exp2(s2 - M);
+    for (int s = 0; s < ns; ++s) acc += a.ws_acc[(base + s) * kHeadDim + lane] * fast_exp2(a.ws_ml[(base + s) * 2] - M);
+  }
   const float inv = Z > 0.f ? 1.f / Z : (Z == 0.f ? 0.f : Z);
   a.out[(q_row * a.Hq + hq) * kHeadDim + lane] = (__bf16)(acc * inv);
   if (a.lse && lane == 0) {
