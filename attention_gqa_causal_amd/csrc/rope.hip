@@ -66,62 +66,80 @@ __device__ __forceinline__ void store_n(T* dst, const T (&src)[N]) {
   }
 }
 
-// Rotate this lane's 4 pairs of NH heads (heads h0, h0 + 8, ...): all loads
-// are issued before any math, so one wave keeps NH loads in flight.  src and
-// dst may alias (every element is read before the same lane writes it).
+// This lane's 4 pairs of up to NH heads (heads h0, h0 + 8, ...), held in
+// registers between the loads and the rotation, so that a wave can issue the
+// loads of a whole row (queries, keys, values) before any of its math.
 template <typename T, int PAIRING, int NH>
-__device__ __forceinline__ void rotate_heads(T* dst, const T* src, int h0, int nh, int c, const float (&cs)[4],
-                                             const float (&sn)[4]) {
-  if (PAIRING == 0) {
-    // pairs (2i, 2i+1), i = 4c .. 4c+3: elements 8c .. 8c+7
-    T x[NH][8];
-#pragma unroll
-    for (int u = 0; u < NH; ++u)
-      if (u < nh) load_n<T, 8>(x[u], src + (h0 + 8 * u) * kHeadDim + 8 * c);
+struct HeadPairs {
+  static constexpr int NX = PAIRING == 0 ? 8 : 4;  // (2i, 2i+1): 8 contiguous elements; (i, i+32): 4 and 4
+  T x[NH][NX];
+  T y[NH][PAIRING == 0 ? 1 : 4];
+
+  __device__ __forceinline__ void load(const T* src, int h0, int nh, int c) {
 #pragma unroll
     for (int u = 0; u < NH; ++u) {
       if (u >= nh) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a = Elt<T>::get(x[u], 2 * j), b = Elt<T>::get(x[u], 2 * j + 1);
-        float ra, rb;
-        rope_rotate(a, b, cs[j], sn[j], ra, rb);
-        Elt<T>::put(x[u], 2 * j, ra);
-        Elt<T>::put(x[u], 2 * j + 1, rb);
-      }
-      store_n<T, 8>(dst + (h0 + 8 * u) * kHeadDim + 8 * c, x[u]);
-    }
-  } else {
-    // pairs (i, i + 32), i = 4c .. 4c+3: elements 4c .. 4c+3 and 32+4c .. 32+4c+3
-    T x[NH][4], y[NH][4];
-#pragma unroll
-    for (int u = 0; u < NH; ++u)
-      if (u < nh) {
+      if constexpr (PAIRING == 0) {
+        load_n<T, 8>(x[u], src + (h0 + 8 * u) * kHeadDim + 8 * c);
+      } else {
         load_n<T, 4>(x[u], src + (h0 + 8 * u) * kHeadDim + 4 * c);
         load_n<T, 4>(y[u], src + (h0 + 8 * u) * kHeadDim + 32 + 4 * c);
       }
+    }
+  }
+
+  // Rotate and store.  dst may be the source (every element was read before).
+  __device__ __forceinline__ void rotate_store(T* dst, int h0, int nh, int c, const float (&cs)[4],
+                                               const float (&sn)[4]) {
 #pragma unroll
     for (int u = 0; u < NH; ++u) {
       if (u >= nh) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float a = Elt<T>::get(x[u], j), b = Elt<T>::get(y[u], j);
         float ra, rb;
-        rope_rotate(a, b, cs[j], sn[j], ra, rb);
-        Elt<T>::put(x[u], j, ra);
-        Elt<T>::put(y[u], j, rb);
+        if constexpr (PAIRING == 0) {
+          rope_rotate(Elt<T>::get(x[u], 2 * j), Elt<T>::get(x[u], 2 * j + 1), cs[j], sn[j], ra, rb);
+          Elt<T>::put(x[u], 2 * j, ra);
+          Elt<T>::put(x[u], 2 * j + 1, rb);
+        } else {
+          rope_rotate(Elt<T>::get(x[u], j), Elt<T>::get(y[u], j), cs[j], sn[j], ra, rb);
+          Elt<T>::put(x[u], j, ra);
+          Elt<T>::put(y[u], j, rb);
+        }
       }
-      store_n<T, 4>(dst + (h0 + 8 * u) * kHeadDim + 4 * c, x[u]);
-      store_n<T, 4>(dst + (h0 + 8 * u) * kHeadDim + 32 + 4 * c, y[u]);
+      if constexpr (PAIRING == 0) {
+        store_n<T, 8>(dst + (h0 + 8 * u) * kHeadDim + 8 * c, x[u]);
+      } else {
+        store_n<T, 4>(dst + (h0 + 8 * u) * kHeadDim + 4 * c, x[u]);
+        store_n<T, 4>(dst + (h0 + 8 * u) * kHeadDim + 32 + 4 * c, y[u]);
+      }
     }
   }
-}
+};
 
 template <typename T, int PAIRING>
 __global__ __launch_bounds__(RP_THREADS) void rope_append_kernel(RopeAppendArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (RP_THREADS / 64) + (threadIdx.x >> 6);
   if (row >= a.T) return;
+  const int c = lane & 7;   // lane within its head group: pairs 4c .. 4c+3
+  const int hg = lane >> 3; // head group: heads hg, hg + 8, ...
+
+  // The sources are indexed by the row alone: the loads of its first 64
+  // query heads, its first 64 key heads and its first value words go out
+  // before the row's position is looked up and its angles formed, so the wave
+  // waits for memory once (more heads than 64 follow in later batches).
+  const int64_t kv_row = (int64_t)a.Hkv * kHeadDim;
+  const T* q = a.q ? reinterpret_cast<const T*>(a.q) + row * a.Hq * kHeadDim : nullptr;
+  const T* k = reinterpret_cast<const T*>(a.k) + row * kv_row;
+  typedef uint32_t w4 __attribute__((ext_vector_type(4)));
+  const w4* vs = reinterpret_cast<const w4*>(reinterpret_cast<const T*>(a.v) + row * kv_row);
+  const int words = (int)(kv_row * sizeof(T) / 16);
+  HeadPairs<T, PAIRING, 8> qp, kp;
+  if (q && hg < a.Hq) qp.load(q, hg, (a.Hq - hg + 7) / 8 < 8 ? (a.Hq - hg + 7) / 8 : 8, c);
+  if (hg < a.Hkv) kp.load(k, hg, (a.Hkv - hg + 7) / 8 < 8 ? (a.Hkv - hg + 7) / 8 : 8, c);
+  w4 v0 = {0u, 0u, 0u, 0u};
+  if (lane < words) v0 = vs[lane];
 
   // sequence and position of this row (the newest q_len positions of its sequence)
   int b, t, q_len;
@@ -144,20 +162,21 @@ __global__ __launch_bounds__(RP_THREADS) void rope_append_kernel(RopeAppendArgs 
   }
   const int L = a.seqlens[b];
   const int p = L - q_len + t;
-  const int c = lane & 7;   // lane within its head group: pairs 4c .. 4c+3
-  const int hg = lane >> 3; // head group: heads hg, hg + 8, ...
 
   float cs[4], sn[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     rope_cos_sin(p, a.inv_freq ? a.inv_freq[4 * c + j] : rope_default_freq(4 * c + j), a.mscale, cs[j], sn[j]);
 
-  // heads hg, hg + 8, ... in batches of 8 per lane (64 heads: one batch)
-  if (a.q) {  // NULL: keys only (the attention rotates its queries itself)
-    const T* q = reinterpret_cast<const T*>(a.q) + row * a.Hq * kHeadDim;
+  // queries (NULL: keys only, the attention rotates its queries itself)
+  if (q) {
     T* qo = reinterpret_cast<T*>(a.q_out) + row * a.Hq * kHeadDim;
-    for (int h0 = hg; h0 < a.Hq; h0 += 64)
-      rotate_heads<T, PAIRING, 8>(qo, q, h0, (a.Hq - h0 + 7) / 8, c, cs, sn);
+    if (hg < a.Hq) qp.rotate_store(qo, hg, (a.Hq - hg + 7) / 8 < 8 ? (a.Hq - hg + 7) / 8 : 8, c, cs, sn);
+    for (int h0 = hg + 64; h0 < a.Hq; h0 += 64) {
+      HeadPairs<T, PAIRING, 8> more;
+      more.load(q, h0, (a.Hq - h0 + 7) / 8, c);
+      more.rotate_store(qo, h0, (a.Hq - h0 + 7) / 8, c, cs, sn);
+    }
   }
 
   // destination row of this position in the cache (or none)
@@ -178,17 +197,17 @@ __global__ __launch_bounds__(RP_THREADS) void rope_append_kernel(RopeAppendArgs 
     }
   }
   if (dst < 0) return;
-  const int64_t kv_row = (int64_t)a.Hkv * kHeadDim;
-  const T* k = reinterpret_cast<const T*>(a.k) + row * kv_row;
   T* kc = reinterpret_cast<T*>(a.k_cache) + dst * kv_row;
-  for (int h0 = hg; h0 < a.Hkv; h0 += 64)
-    rotate_heads<T, PAIRING, 8>(kc, k, h0, (a.Hkv - h0 + 7) / 8, c, cs, sn);
+  if (hg < a.Hkv) kp.rotate_store(kc, hg, (a.Hkv - hg + 7) / 8 < 8 ? (a.Hkv - hg + 7) / 8 : 8, c, cs, sn);
+  for (int h0 = hg + 64; h0 < a.Hkv; h0 += 64) {
+    HeadPairs<T, PAIRING, 8> more;
+    more.load(k, h0, (a.Hkv - h0 + 7) / 8, c);
+    more.rotate_store(kc, h0, (a.Hkv - h0 + 7) / 8, c, cs, sn);
+  }
   // values: copied as 16-byte words
-  typedef uint32_t w4 __attribute__((ext_vector_type(4)));
-  const w4* vs = reinterpret_cast<const w4*>(reinterpret_cast<const T*>(a.v) + row * kv_row);
   w4* vd = reinterpret_cast<w4*>(reinterpret_cast<T*>(a.v_cache) + dst * kv_row);
-  const int words = (int)(kv_row * sizeof(T) / 16);
-  for (int i = lane; i < words; i += 64) vd[i] = vs[i];
+  if (lane < words) vd[lane] = v0;
+  for (int i = lane + 64; i < words; i += 64) vd[i] = vs[i];
 }
 
 }  // namespace
