@@ -478,8 +478,9 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
     }
     qk_half(sA[0], sA[1], Ks[0], qb, 0, lr, lg);
     int cur = 0;
-    auto body = [&](auto mask_tag, int t) {
+    auto body = [&](auto mask_tag, auto h1_tag, int t) {
       constexpr bool MASK = decltype(mask_tag)::value;
+      constexpr bool H1 = decltype(h1_tag)::value;  // false: key half 1 is masked for every row (skipped)
       const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
       const int j0 = tile_j0(t);
       const bool has_next = t + 1 < n_tiles;
@@ -504,14 +505,18 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
       float r0, r1;  // set by the first exponential chunk of each N-tile
       {
         bf16x8 ka[4];
+        if (H1) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          ka[k] = *reinterpret_cast<const bf16x8*>(Ks[cur] + (32 + lr) * RS + kchunk(2 * k + lg, lr));
+          for (int k = 0; k < 4; ++k)
+            ka[k] = *reinterpret_cast<const bf16x8*>(Ks[cur] + (32 + lr) * RS + kchunk(2 * k + lg, lr));
+        }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           fence_schedule();
-          sB[0] = mfma32(ka[k], qb[0][k], k == 0 ? zero16() : sB[0]);
-          sB[1] = mfma32(ka[k], qb[1][k], k == 0 ? zero16() : sB[1]);
+          if (H1) {
+            sB[0] = mfma32(ka[k], qb[0][k], k == 0 ? zero16() : sB[0]);
+            sB[1] = mfma32(ka[k], qb[1][k], k == 0 ? zero16() : sB[1]);
+          }
           fence_schedule();
           if (k == 0) r0 = exp_chunk(sA[0], pA0[k], k, m_run[0], c);
           else if (k == 1) r0 += exp_chunk(sA[0], pA0[k], k, m_run[0], c);
@@ -534,7 +539,7 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
       if (W == 0) __builtin_amdgcn_s_setprio(2);
       // (b): P V over key half 0 in four steps, each followed by a quarter of
       // the half-1 exponentials
-      if (MASK) {
+      if (MASK && H1) {
         mask_half<STK>(sB[0], 1, j0, pos0[0], phi[0], W, st, dh0, dl0, ds);
         mask_half<STK>(sB[1], 1, j0, pos0[1], phi[1], W, st, dh1, dl1, ds);
       }
@@ -549,6 +554,7 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
           o[0][dt] = mfma32(va[i], pA0[uu], o[0][dt]);
           o[1][dt] = mfma32(va[i], pA1[uu], o[1][dt]);
           fence_schedule();
+          if (!H1) continue;
           if (i == 0) r0 = exp_chunk(sB[0], pB0[i], i, m_run[0], c);
           else if (i == 1) r0 += exp_chunk(sB[0], pB0[i], i, m_run[0], c);
           else if (i == 2) r1 = exp_chunk(sB[1], pB1[i - 2], i - 2, m_run[1], c);
@@ -556,7 +562,7 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
         }
         fence_schedule();
       }
-      {
+      if (H1) {
         const bool f0 = __builtin_amdgcn_ballot_w64(r0 > kRefit) != 0;
         const bool f1 = __builtin_amdgcn_ballot_w64(r1 > kRefit) != 0;
         float al0 = 1.f, al1 = 1.f;
@@ -564,9 +570,9 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
         if (f1) r1 = refit_half<STK>(sB[1], pB1, m_run[1], l_run[1], al1, Ks[cur], qb[1], 1, lr, lg, c, j0, pos0[1], phi[1], W, st, dh1, dl1, ds);
         if (f0) { o[0][0] *= al0; o[0][1] *= al0; }
         if (f1) { o[1][0] *= al1; o[1][1] *= al1; }
+        l_run[0] += r0;
+        l_run[1] += r1;
       }
-      l_run[0] += r0;
-      l_run[1] += r1;
       if (load) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's loads of tile t+1 have landed
         __syncthreads();
@@ -575,7 +581,7 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
       // (c)
       if (load && t + 2 < n_tiles) dma_tile(t + 2, blk_next, nxt == NBUF - 1 ? 0 : nxt + 1);
       fetch_blk(t + 3, blk_next);
-      pv_half(o, Vs[cur], pB0, pB1, 1, vofs);
+      if (H1) pv_half(o, Vs[cur], pB0, pB1, 1, vofs);
       if (has_next) qk_half(sA[0], sA[1], Ks[nxt], qb, 0, lr, lg);
       cur = nxt;
     };
@@ -590,16 +596,21 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
     const int n_wt = n_tiles - n_st;  // window tiles; the sink tiles all take the masked body
     const int pb = n_st + min(t_lo, n_wt);
     const int pe = max(pb, n_st + min(t_hi + 1, n_wt));
-    std::true_type MSK;
-    std::false_type PLN;
+    std::true_type MSK, FULL;
+    std::false_type PLN, HALF0;
     if (TWO) {
       // at most NBUF tiles, mostly edges: one (masked) body keeps the code of
       // both steps within the instruction cache
-      for (int t = 0; t < n_tiles; ++t) body(MSK, t);
+      for (int t = 0; t < n_tiles; ++t) body(MSK, FULL, t);
     } else {
-      for (int t = 0; t < pb; ++t) body(MSK, t);
-      for (int t = pb; t < pe; ++t) body(PLN, t);
-      for (int t = pe; t < n_tiles; ++t) body(MSK, t);
+      int t = 0;
+      // One sink tile holding at most 32 sink tokens: its key half 1 lies
+      // below the window and past the sink tokens, so every row masks it, and
+      // the tile runs key half 0 only (the skipped half adds exact zeros).
+      if (STK && n_st == 1 && st <= BK / 2) body(MSK, HALF0, t++);
+      for (; t < pb; ++t) body(MSK, FULL, t);
+      for (int t = pb; t < pe; ++t) body(PLN, FULL, t);
+      for (int t = pe; t < n_tiles; ++t) body(MSK, FULL, t);
     }
   }
   // the next step's queries load while this step's output goes out

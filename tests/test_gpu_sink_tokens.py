@@ -26,6 +26,8 @@ pytestmark = pytest.mark.gpu
     (1, 200, 128, 500),
     (1, 1000, 128, 64),
     (1, 33, 8, 40),
+    (1, 600, 128, 32),   # the most sink tokens whose tile runs key half 0 only
+    (1, 600, 100, 33),   # one more: the sink tile runs both halves
 ])
 def test_prefill_sink_tokens(device, B, S, W, n):
     say(f"prefill sink tokens B{B} S{S} W={W} n={n}")
