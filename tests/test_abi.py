@@ -356,12 +356,12 @@ def test_backward_rejects(L, kw, code):
 def test_backward_workspace_size(L):
     # two fp32 per (sequence, head, position) and one per (head, sequence, 1024
     # positions), each array rounded up to 256 bytes; with few
-    # 64-key blocks (under 4096 per call) bf16 adds fp32 dK/dV partials for up
-    # to 4 query slabs of every block
+    # 64-key blocks (under 1024 per call) bf16 adds fp32 dK/dV partials for up
+    # to 4 query slabs of every block (enough slabs for about 1024 jobs)
     part = 2 * 64 * 64 * 4
     ws = L.gqa_attn_prefill_backward_workspace_size
     assert ws(1, 16, 64, 8, 64, 1) == 2 * 16 * 64 * 4 + 256
-    assert ws(1, 4096, 64, 8, 64, 0) == 2 * 4096 * 64 * 4 + 4 * 64 * 4 + 8 * 64 * 4 * part
+    assert ws(1, 4096, 64, 8, 64, 0) == 2 * 4096 * 64 * 4 + 4 * 64 * 4 + 8 * 64 * 2 * part  # 512 blocks: 2 slabs
     assert ws(8, 4096, 64, 8, 64, 0) == 2 * 8 * 4096 * 64 * 4 + 8 * 4 * 64 * 4  # 4096 key blocks: no slabs
     assert ws(1, 100, 64, 8, 64, 0) == 2 * 100 * 64 * 4 + 256 + 8 * 2 * 4 * part
     assert ws(1, 3, 1, 1, 64, 1) == 3 * 256
