@@ -38,6 +38,7 @@ struct PrefillArgs {
   // divisors of the workgroup-to-job mapping
   int wg_per_job;
   FastDiv div_wg_per_job, div_hkv, div_g, div_units;
+  FastDiv div_ring;  // KV_RING: the ring's slot count seq.lmax
 };
 
 // Decode-style attention: one query token per sequence, KV split over

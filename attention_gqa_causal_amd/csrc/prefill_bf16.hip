@@ -352,7 +352,11 @@ __device__ __forceinline__ void prefill_job(const PrefillArgs& a, const int x, _
         GQA_FLAG(bb != blk[i], kDbgBlockTable);
         row = ((int64_t)bb << a.seq.log2_block) + (j & ((1 << a.seq.log2_block) - 1));
       } else if (MODE == KV_RING) {
-        row = ring_chunk_row(a.seq, sv, j);
+        // ring_chunk_row with the slot taken by the launch's multiplier
+        // instead of a division sequence per row
+        const int jc = sv.kv_len - sv.q_len;
+        row = j >= jc ? -1 - (sv.q_row0 + (j - jc))
+                      : (int64_t)sv.b * a.seq.lmax + (j - fast_div(j, a.div_ring) * a.seq.lmax);
         if (row < 0) {  // the chunk's own row
           row = -1 - row;
           kb = kbase2;
@@ -755,6 +759,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& args, int kv_mode, bool varlen
   a.div_hkv = make_fastdiv(a.Hkv);
   a.div_g = make_fastdiv(a.G);
   a.div_units = make_fastdiv(a.B * a.Hkv);
+  a.div_ring = make_fastdiv(a.seq.lmax > 0 ? a.seq.lmax : 1);
   const bool stk = a.window > 0 && a.sink_tokens > 0;
   if (a.rope) {  // queries rotated in the kernel: whole-sequence prefill only
     if (kv_mode != KV_BATCHED || varlen_q) return hipErrorInvalidValue;
